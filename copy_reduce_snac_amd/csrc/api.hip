@@ -1,0 +1,553 @@
+// api.hip -- the C ABI declared in include/snac.h: argument validation,
+// layout planning on the host, context and workspace management, launches.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "../../include/snac.h"
+#include "atoms.hpp"
+#include "internal.hpp"
+#include "layout.hpp"
+
+using namespace snac;
+
+struct snac_ctx {
+  int nranks;
+  int device;
+  size_t staging_bytes;  // per rank
+  uint32_t slots;
+  uint32_t tile_bytes;
+  char* workspace;  // device: staging then signal area
+  char* staging;
+  uint64_t* ready;
+  uint64_t* freed;
+  uint64_t* ctrl;
+  uint64_t signal_words;
+  uint32_t* abort_host;  // host-mapped word (hipHostMalloc)
+  uint32_t* abort_dev;   // its device-visible address
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+snac_status fail(snac_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+snac_status ok() {
+  g_err.clear();
+  return SNAC_OK;
+}
+
+snac_status hip_fail(hipError_t e, const char* what) {
+  return fail(SNAC_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+snac_tuning g_tuning = {0, 0, 0, 0, 0, 0, {0, 0}};
+
+constexpr uint32_t kDefaultPipeTile = 64u * 1024u;
+constexpr size_t kDefaultStaging = 8u * 1024u * 1024u;
+constexpr int kDefaultSpinLog2 = 22;
+
+LaunchCfg launch_cfg() { return LaunchCfg{g_tuning.wgs_per_cu, g_tuning.cache_policy}; }
+
+int esize_of(snac_dtype t) {
+  switch (t) {
+    case SNAC_BYTE: return 1;
+    case SNAC_U32: return 4;
+    case SNAC_F32: return 4;
+    case SNAC_BF16: return 2;
+    default: return 0;
+  }
+}
+
+bool is_float(snac_dtype t) { return t == SNAC_F32 || t == SNAC_BF16; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Shared argument checks and planning for every collective.
+struct Plan {
+  CollDesc d;
+  bool aligned;
+  uint64_t tiles;
+};
+
+// Host copy of the layout: total tiles and the aligned flag.
+void finish_plan(Plan& p) {
+  const int nj = num_jobs(p.d);
+  bool aligned = true;
+  for (int j = 0; j < nj && aligned; ++j) {
+    const Job jb = make_job(p.d, j);
+    if (jb.bytes == 0) continue;
+    if (jb.bytes & 15u) aligned = false;
+    const int s0 = jb.src_rank < 0 ? 0 : jb.src_rank, s1 = jb.src_rank < 0 ? p.d.nsrc : jb.src_rank + 1;
+    for (int s = s0; s < s1; ++s)
+      if (((uintptr_t)p.d.src[s] + jb.src_off) & 15u) aligned = false;
+    const int t0 = jb.dst_rank < 0 ? 0 : jb.dst_rank, t1 = jb.dst_rank < 0 ? p.d.ndst : jb.dst_rank + 1;
+    for (int t = t0; t < t1; ++t)
+      if (((uintptr_t)p.d.dst[t] + jb.dst_off) & 15u) aligned = false;
+  }
+  p.aligned = aligned;
+  const uint64_t tile = coll_tile_bytes(p.d, aligned);
+  uint64_t tiles = 0;
+  for (int j = 0; j < nj; ++j) {
+    const Job jb = make_job(p.d, j);
+    const uint32_t head = aligned ? 0u : job_head_bytes(p.d, jb);
+    tiles += job_tiles(jb, head, tile);
+  }
+  p.tiles = tiles;
+}
+
+// Multicast jobs need one destination residue modulo 16.
+int needs_split(void* const* dst, int ndst) {
+  for (int i = 1; i < ndst; ++i)
+    if ((((uintptr_t)dst[i]) & 15u) != (((uintptr_t)dst[0]) & 15u)) return 1;
+  return 0;
+}
+
+snac_status check_ptrs(const void* const* src, int nsrc, void* const* dst, int ndst, int esize) {
+  if (!src || !dst) return fail(SNAC_E_ARG, "src and dst pointer arrays must not be NULL");
+  for (int i = 0; i < nsrc; ++i) {
+    if (!src[i]) return fail(SNAC_E_ARG, "src[%d] is NULL", i);
+    if ((uintptr_t)src[i] % (uintptr_t)esize) return fail(SNAC_E_ARG, "src[%d] not aligned to %d bytes", i, esize);
+  }
+  for (int i = 0; i < ndst; ++i) {
+    if (!dst[i]) return fail(SNAC_E_ARG, "dst[%d] is NULL", i);
+    if ((uintptr_t)dst[i] % (uintptr_t)esize) return fail(SNAC_E_ARG, "dst[%d] not aligned to %d bytes", i, esize);
+  }
+  return SNAC_OK;
+}
+
+// in_bytes[i]/out_bytes[i]: extents of each src/dst buffer.  `inplace_ok`
+// says whether dst d may start exactly at src s (position-aligned reuse).
+template <typename InplaceFn>
+snac_status check_overlap(const void* const* src, const uint64_t* in_bytes, int nsrc, void* const* dst,
+                          const uint64_t* out_bytes, int ndst, InplaceFn inplace_ok) {
+  for (int a = 0; a < ndst; ++a) {
+    const Range ra{(uintptr_t)dst[a], (uintptr_t)dst[a] + out_bytes[a]};
+    if (ra.lo == ra.hi) continue;
+    for (int b = a + 1; b < ndst; ++b) {
+      const Range rb{(uintptr_t)dst[b], (uintptr_t)dst[b] + out_bytes[b]};
+      if (rb.lo != rb.hi && overlaps(ra, rb)) return fail(SNAC_E_ARG, "dst[%d] and dst[%d] overlap", a, b);
+    }
+    for (int s = 0; s < nsrc; ++s) {
+      const Range rs{(uintptr_t)src[s], (uintptr_t)src[s] + in_bytes[s]};
+      if (rs.lo == rs.hi || !overlaps(ra, rs)) continue;
+      if (!inplace_ok(a, s)) return fail(SNAC_E_ARG, "dst[%d] overlaps src[%d] (not a supported in-place form)", a, s);
+    }
+  }
+  return SNAC_OK;
+}
+
+snac_status check_ctx(const snac_ctx* ctx) {
+  if (!ctx) return fail(SNAC_E_ARG, "ctx is NULL");
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(SNAC_E_HIP, "hipGetDevice failed");
+  if (dev != ctx->device) return fail(SNAC_E_STATE, "context belongs to device %d, current device is %d", ctx->device, dev);
+  return SNAC_OK;
+}
+
+snac_status run(Plan& p, hipStream_t stream) {
+  finish_plan(p);
+  if (p.tiles == 0) return ok();
+  hipError_t e = launch_collective(p.d, p.aligned, p.tiles, launch_cfg(), stream);
+  if (e != hipSuccess) return hip_fail(e, "collective launch");
+  return ok();
+}
+
+Plan base_plan(int32_t coll, int nsrc, int ndst, int esize) {
+  Plan p;
+  std::memset(&p, 0, sizeof p);
+  p.d.coll = coll;
+  p.d.nsrc = nsrc;
+  p.d.ndst = ndst;
+  p.d.esize = esize;
+  return p;
+}
+
+// fixed-size collectives share their checks
+snac_status fixed_collective(int32_t coll, snac_ctx* ctx, const void* const* src, void* const* dst, size_t bytes,
+                             snac_dtype dtype, snac_stream stream) {
+  snac_status st = check_ctx(ctx);
+  if (st != SNAC_OK) return st;
+  const int n = ctx->nranks;
+  const int e = esize_of(dtype);
+  if (!e) return fail(SNAC_E_ARG, "unknown dtype %d", (int)dtype);
+  const bool reduce = coll == kAllReduce || coll == kReduceScatter;
+  if (reduce && !is_float(dtype)) return fail(SNAC_E_ARG, "reductions need SNAC_F32 or SNAC_BF16");
+  if (bytes % (size_t)e) return fail(SNAC_E_ARG, "bytes (%zu) is not a multiple of the element size %d", bytes, e);
+  if ((coll == kReduceScatter || coll == kAllToAll) && bytes % ((size_t)n * e))
+    return fail(SNAC_E_ARG, "bytes (%zu) is not a multiple of N * element size (%d)", bytes, n * e);
+  if (bytes == 0) return ok();
+  if ((st = check_ptrs(src, n, dst, n, e)) != SNAC_OK) return st;
+  uint64_t in_b[kMaxRanks], out_b[kMaxRanks];
+  for (int i = 0; i < n; ++i) {
+    in_b[i] = bytes;
+    out_b[i] = coll == kAllGather ? bytes * n : (coll == kReduceScatter ? bytes / n : bytes);
+  }
+  const size_t chunk = bytes / (size_t)n;
+  st = check_overlap(src, in_b, n, dst, out_b, n, [&](int d, int s) {
+    if (d != s) return false;
+    if (coll == kAllReduce) return (uintptr_t)dst[d] == (uintptr_t)src[s];
+    if (coll == kReduceScatter) return (uintptr_t)dst[d] == (uintptr_t)src[s] + (uintptr_t)d * chunk;
+    if (coll == kAllGather) return (uintptr_t)src[s] == (uintptr_t)dst[d] + (uintptr_t)d * bytes;
+    return false;
+  });
+  if (st != SNAC_OK) return st;
+  Plan p = base_plan(coll, n, n, e);
+  p.d.bytes = bytes;
+  for (int i = 0; i < n; ++i) {
+    p.d.src[i] = src[i];
+    p.d.dst[i] = dst[i];
+  }
+  if (coll == kAllReduce || coll == kAllGather) p.d.split_multicast = needs_split(dst, n);
+  return run(p, (hipStream_t)stream);
+}
+
+snac_status v_collective(int32_t coll, snac_ctx* ctx, const void* const* src, void* const* dst, const size_t* counts,
+                         snac_dtype dtype, snac_stream stream) {
+  snac_status st = check_ctx(ctx);
+  if (st != SNAC_OK) return st;
+  const int n = ctx->nranks;
+  const int e = esize_of(dtype);
+  if (!e) return fail(SNAC_E_ARG, "unknown dtype %d", (int)dtype);
+  if (coll == kReduceScatterV && !is_float(dtype)) return fail(SNAC_E_ARG, "reductions need SNAC_F32 or SNAC_BF16");
+  if (!counts) return fail(SNAC_E_ARG, "counts is NULL");
+  const int nc = coll == kAllToAllV ? n * n : n;
+  uint64_t total = 0;
+  for (int i = 0; i < nc; ++i) {
+    if (counts[i] > ((uint64_t)1 << 40)) return fail(SNAC_E_ARG, "counts[%d] is implausibly large", i);
+    total += counts[i];
+  }
+  if (total == 0) return ok();
+  if ((st = check_ptrs(src, n, dst, n, e)) != SNAC_OK) return st;
+  uint64_t in_b[kMaxRanks], out_b[kMaxRanks];
+  for (int i = 0; i < n; ++i) {
+    if (coll == kAllGatherV) {
+      in_b[i] = counts[i] * e;
+      out_b[i] = total * e;
+    } else if (coll == kReduceScatterV) {
+      in_b[i] = total * e;
+      out_b[i] = counts[i] * e;
+    } else {
+      uint64_t row = 0, col = 0;
+      for (int j = 0; j < n; ++j) {
+        row += counts[i * n + j];
+        col += counts[j * n + i];
+      }
+      in_b[i] = row * e;
+      out_b[i] = col * e;
+    }
+  }
+  st = check_overlap(src, in_b, n, dst, out_b, n, [](int, int) { return false; });
+  if (st != SNAC_OK) return st;
+  Plan p = base_plan(coll, n, n, e);
+  for (int i = 0; i < n; ++i) {
+    p.d.src[i] = src[i];
+    p.d.dst[i] = dst[i];
+  }
+  for (int i = 0; i < nc; ++i) p.d.counts[i] = counts[i];
+  if (coll == kAllGatherV) p.d.split_multicast = needs_split(dst, n);
+  return run(p, (hipStream_t)stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int snac_abi_version(void) { return SNAC_ABI_VERSION; }
+
+const char* snac_status_str(snac_status s) {
+  switch (s) {
+    case SNAC_OK: return "SNAC_OK";
+    case SNAC_E_ARG: return "SNAC_E_ARG: invalid argument";
+    case SNAC_E_UNSUPPORTED: return "SNAC_E_UNSUPPORTED: not implemented";
+    case SNAC_E_NOMEM: return "SNAC_E_NOMEM: device allocation failed";
+    case SNAC_E_HIP: return "SNAC_E_HIP: HIP runtime error";
+    case SNAC_E_TIMEOUT: return "SNAC_E_TIMEOUT: device-side wait timed out";
+    case SNAC_E_STATE: return "SNAC_E_STATE: context unusable";
+    case SNAC_E_ABORTED: return "SNAC_E_ABORTED: device-side waits aborted";
+    default: return "SNAC_E_?: unknown status";
+  }
+}
+
+const char* snac_last_error(void) { return g_err.c_str(); }
+
+int snac_ctx_nranks(const snac_ctx* ctx) { return ctx ? ctx->nranks : 0; }
+
+snac_status snac_get_tuning(snac_tuning* out) {
+  if (!out) return fail(SNAC_E_ARG, "out is NULL");
+  *out = g_tuning;
+  return ok();
+}
+
+snac_status snac_set_tuning(const snac_tuning* in) {
+  if (!in) return fail(SNAC_E_ARG, "in is NULL");
+  if (in->wgs_per_cu < 0 || in->wgs_per_cu > 32) return fail(SNAC_E_ARG, "wgs_per_cu out of range [0, 32]");
+  if (in->cache_policy < 0 || in->cache_policy > 3) return fail(SNAC_E_ARG, "cache_policy out of range [0, 3]");
+  if (in->pipeline_tile_bytes < 0 || in->pipeline_tile_bytes % 4096)
+    return fail(SNAC_E_ARG, "pipeline_tile_bytes must be a non-negative multiple of 4096");
+  if (in->pipeline_lookahead < 0) return fail(SNAC_E_ARG, "pipeline_lookahead must be >= 0");
+  if (in->spin_limit_log2 < 0 || in->spin_limit_log2 > 40) return fail(SNAC_E_ARG, "spin_limit_log2 out of range");
+  if (in->debug_drop_notify < 0 || in->debug_drop_notify > SNAC_MAX_RANKS)
+    return fail(SNAC_E_ARG, "debug_drop_notify out of range");
+  g_tuning = *in;
+  return ok();
+}
+
+snac_status snac_init(int nranks, size_t staging_bytes_per_rank, snac_stream stream, snac_ctx** out) {
+  if (!out) return fail(SNAC_E_ARG, "out is NULL");
+  *out = nullptr;
+  if (nranks < 1 || nranks > SNAC_MAX_RANKS) return fail(SNAC_E_ARG, "nranks %d outside 1..%d", nranks, SNAC_MAX_RANKS);
+  const uint32_t tile = g_tuning.pipeline_tile_bytes ? (uint32_t)g_tuning.pipeline_tile_bytes : kDefaultPipeTile;
+  const size_t staging = staging_bytes_per_rank ? staging_bytes_per_rank : kDefaultStaging;
+  if (staging % tile) return fail(SNAC_E_ARG, "staging_bytes_per_rank must be a multiple of the pipeline tile (%u)", tile);
+  const uint64_t slots = staging / tile;
+  if (slots < 2 || slots > (1u << 20)) return fail(SNAC_E_ARG, "staging ring needs 2 .. 2^20 slots (got %llu)", (unsigned long long)slots);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  snac_ctx* c = new (std::nothrow) snac_ctx();
+  if (!c) return fail(SNAC_E_NOMEM, "host allocation failed");
+  c->nranks = nranks;
+  c->device = dev;
+  c->staging_bytes = staging;
+  c->slots = (uint32_t)slots;
+  c->tile_bytes = tile;
+  const uint64_t ready_words = (uint64_t)nranks * slots * kFlagStride;
+  const uint64_t free_words = slots * kFlagStride;
+  c->signal_words = ready_words + free_words + kCtrlWords;
+  const size_t staging_total = (size_t)nranks * staging;
+  const size_t bytes = staging_total + c->signal_words * sizeof(uint64_t);
+  e = hipMalloc(reinterpret_cast<void**>(&c->workspace), bytes);
+  if (e != hipSuccess) {
+    delete c;
+    return fail(SNAC_E_NOMEM, "hipMalloc(%zu) failed: %s", bytes, hipGetErrorString(e));
+  }
+  c->staging = c->workspace;
+  c->ready = reinterpret_cast<uint64_t*>(c->workspace + staging_total);
+  c->freed = c->ready + ready_words;
+  c->ctrl = c->freed + free_words;
+  e = hipHostMalloc(reinterpret_cast<void**>(&c->abort_host), sizeof(uint32_t), hipHostMallocMapped | hipHostMallocCoherent);
+  if (e != hipSuccess) {
+    (void)hipFree(c->workspace);
+    delete c;
+    return fail(SNAC_E_NOMEM, "hipHostMalloc failed: %s", hipGetErrorString(e));
+  }
+  *c->abort_host = 0;
+  e = hipHostGetDevicePointer(reinterpret_cast<void**>(&c->abort_dev), c->abort_host, 0);
+  if (e == hipSuccess) e = fill_u64(c->ready, c->signal_words, 0, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    (void)hipHostFree(c->abort_host);
+    (void)hipFree(c->workspace);
+    delete c;
+    return hip_fail(e, "workspace set-up");
+  }
+  *out = c;
+  return ok();
+}
+
+snac_status snac_check(snac_ctx* ctx, snac_stream stream) {
+  if (!ctx) return fail(SNAC_E_ARG, "ctx is NULL");
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  uint64_t status = 0;
+  e = hipMemcpy(&status, ctx->ctrl + kCtrlStatus, sizeof status, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "reading the status word");
+  const bool aborted = __atomic_load_n(ctx->abort_host, __ATOMIC_SEQ_CST) != 0;
+  if (status == 0 && !aborted) return ok();
+  // re-arm: clear the abort word, every flag and the control words
+  __atomic_store_n(ctx->abort_host, 0u, __ATOMIC_SEQ_CST);
+  e = fill_u64(ctx->ready, ctx->signal_words, 0, (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "re-arming the signal area");
+  if (status == SNAC_E_TIMEOUT) return fail(SNAC_E_TIMEOUT, "a device-side SNAC wait exceeded its spin limit");
+  return fail(SNAC_E_ABORTED, "device-side SNAC waits were aborted");
+}
+
+snac_status snac_abort(snac_ctx* ctx) {
+  if (!ctx) return fail(SNAC_E_ARG, "ctx is NULL");
+  __atomic_store_n(ctx->abort_host, 1u, __ATOMIC_SEQ_CST);
+  return ok();
+}
+
+snac_status snac_finalize(snac_ctx* ctx, snac_stream stream) {
+  if (!ctx) return ok();
+  snac_status st = snac_check(ctx, stream);
+  std::string err = g_err;
+  (void)hipStreamSynchronize((hipStream_t)stream);
+  (void)hipHostFree(ctx->abort_host);
+  hipError_t e = hipFree(ctx->workspace);
+  delete ctx;
+  if (st != SNAC_OK) return fail(st, "%s", err.c_str());
+  if (e != hipSuccess) return hip_fail(e, "hipFree");
+  return ok();
+}
+
+snac_status snac_copy(void* dst, const void* src, size_t bytes, snac_stream stream) {
+  if (bytes == 0) return ok();
+  if (!dst || !src) return fail(SNAC_E_ARG, "NULL pointer");
+  const Range a{(uintptr_t)dst, (uintptr_t)dst + bytes}, b{(uintptr_t)src, (uintptr_t)src + bytes};
+  if (overlaps(a, b)) return fail(SNAC_E_ARG, "src and dst overlap");
+  Plan p = base_plan(kAtomCopy, 1, 1, 1);
+  p.d.bytes = bytes;
+  p.d.src[0] = src;
+  p.d.dst[0] = dst;
+  return run(p, (hipStream_t)stream);
+}
+
+snac_status snac_reduce_n(void* const* dst, int ndst, const void* const* src, int nsrc, size_t count,
+                          snac_dtype dtype, snac_stream stream) {
+  if (nsrc < 1 || nsrc > SNAC_MAX_RANKS) return fail(SNAC_E_ARG, "nsrc %d outside 1..%d", nsrc, SNAC_MAX_RANKS);
+  if (ndst < 1 || ndst > SNAC_MAX_RANKS) return fail(SNAC_E_ARG, "ndst %d outside 1..%d", ndst, SNAC_MAX_RANKS);
+  if (!is_float(dtype)) return fail(SNAC_E_ARG, "reduce needs SNAC_F32 or SNAC_BF16");
+  if (count == 0) return ok();
+  const int e = esize_of(dtype);
+  snac_status st = check_ptrs(src, nsrc, dst, ndst, e);
+  if (st != SNAC_OK) return st;
+  const uint64_t bytes = (uint64_t)count * e;
+  uint64_t in_b[kMaxRanks], out_b[kMaxRanks];
+  for (int i = 0; i < kMaxRanks; ++i) in_b[i] = out_b[i] = bytes;
+  st = check_overlap(src, in_b, nsrc, dst, out_b, ndst,
+                     [&](int d, int s) { return (uintptr_t)dst[d] == (uintptr_t)src[s]; });
+  if (st != SNAC_OK) return st;
+  Plan p = base_plan(kAtomReduce, nsrc, ndst, e);
+  p.d.bytes = bytes;
+  for (int i = 0; i < nsrc; ++i) p.d.src[i] = src[i];
+  for (int i = 0; i < ndst; ++i) p.d.dst[i] = dst[i];
+  p.d.split_multicast = needs_split(dst, ndst);
+  return run(p, (hipStream_t)stream);
+}
+
+snac_status snac_all_reduce(snac_ctx* ctx, const void* const* src, void* const* dst, size_t bytes, snac_dtype dtype,
+                            snac_stream stream) {
+  return fixed_collective(kAllReduce, ctx, src, dst, bytes, dtype, stream);
+}
+
+snac_status snac_reduce_scatter(snac_ctx* ctx, const void* const* src, void* const* dst, size_t bytes,
+                                snac_dtype dtype, snac_stream stream) {
+  return fixed_collective(kReduceScatter, ctx, src, dst, bytes, dtype, stream);
+}
+
+snac_status snac_all_gather(snac_ctx* ctx, const void* const* src, void* const* dst, size_t bytes, snac_dtype dtype,
+                            snac_stream stream) {
+  return fixed_collective(kAllGather, ctx, src, dst, bytes, dtype, stream);
+}
+
+snac_status snac_all_to_all(snac_ctx* ctx, const void* const* src, void* const* dst, size_t bytes, snac_dtype dtype,
+                            snac_stream stream) {
+  return fixed_collective(kAllToAll, ctx, src, dst, bytes, dtype, stream);
+}
+
+snac_status snac_all_gather_v(snac_ctx* ctx, const void* const* src, void* const* dst, const size_t* counts,
+                              snac_dtype dtype, snac_stream stream) {
+  return v_collective(kAllGatherV, ctx, src, dst, counts, dtype, stream);
+}
+
+snac_status snac_reduce_scatter_v(snac_ctx* ctx, const void* const* src, void* const* dst, const size_t* counts,
+                                  snac_dtype dtype, snac_stream stream) {
+  return v_collective(kReduceScatterV, ctx, src, dst, counts, dtype, stream);
+}
+
+snac_status snac_all_to_all_v(snac_ctx* ctx, const void* const* src, void* const* dst, const size_t* counts,
+                              snac_dtype dtype, snac_stream stream) {
+  return v_collective(kAllToAllV, ctx, src, dst, counts, dtype, stream);
+}
+
+snac_status snac_pipeline_scale_reduce(snac_ctx* ctx, const void* const* x, void* out, size_t count,
+                                       snac_dtype dtype, snac_stream stream) {
+  snac_status st = check_ctx(ctx);
+  if (st != SNAC_OK) return st;
+  if (!is_float(dtype)) return fail(SNAC_E_ARG, "the pipeline needs SNAC_F32 or SNAC_BF16");
+  if (count == 0) return ok();
+  const int n = ctx->nranks;
+  const int e = esize_of(dtype);
+  if (!x || !out) return fail(SNAC_E_ARG, "NULL pointer");
+  for (int i = 0; i < n; ++i) {
+    if (!x[i]) return fail(SNAC_E_ARG, "x[%d] is NULL", i);
+    if ((uintptr_t)x[i] & 15u) return fail(SNAC_E_ARG, "x[%d] must be 16-byte aligned", i);
+  }
+  if ((uintptr_t)out & 15u) return fail(SNAC_E_ARG, "out must be 16-byte aligned");
+  const Range ro{(uintptr_t)out, (uintptr_t)out + count * (uint64_t)e};
+  for (int i = 0; i < n; ++i)
+    if (overlaps(ro, Range{(uintptr_t)x[i], (uintptr_t)x[i] + count * (uint64_t)e}))
+      return fail(SNAC_E_ARG, "out overlaps x[%d]", i);
+  if (ctx->tile_bytes % (uint32_t)e) return fail(SNAC_E_STATE, "pipeline tile not a multiple of the element size");
+  PipeArgs a;
+  std::memset(&a, 0, sizeof a);
+  for (int i = 0; i < n; ++i) a.x[i] = x[i];
+  a.out = out;
+  a.count = count;
+  a.nranks = n;
+  a.esize = e;
+  a.staging = ctx->staging;
+  a.ready = ctx->ready;
+  a.freed = ctx->freed;
+  a.ctrl = ctx->ctrl;
+  a.abort_word = ctx->abort_dev;
+  a.slots = ctx->slots;
+  a.tile_bytes = ctx->tile_bytes;
+  a.lookahead = (uint32_t)g_tuning.pipeline_lookahead;
+  a.spin_limit_log2 = (uint32_t)(g_tuning.spin_limit_log2 ? g_tuning.spin_limit_log2 : kDefaultSpinLog2);
+  a.drop_notify = g_tuning.debug_drop_notify;
+  hipError_t err = launch_pipeline(a, dtype == SNAC_BF16, launch_cfg(), (hipStream_t)stream, nullptr);
+  if (err != hipSuccess) return hip_fail(err, "pipeline launch");
+  return ok();
+}
+
+snac_status snac_plan(snac_coll coll, int nranks, snac_dtype dtype, size_t bytes, const size_t* counts,
+                      snac_job* jobs, int max_jobs, int* njobs) {
+  if (!njobs) return fail(SNAC_E_ARG, "njobs is NULL");
+  *njobs = 0;
+  if (nranks < 1 || nranks > SNAC_MAX_RANKS) return fail(SNAC_E_ARG, "nranks %d outside 1..%d", nranks, SNAC_MAX_RANKS);
+  const int e = esize_of(dtype);
+  if (!e) return fail(SNAC_E_ARG, "unknown dtype %d", (int)dtype);
+  if ((int)coll < 0 || (int)coll > 6) return fail(SNAC_E_ARG, "unknown collective %d", (int)coll);
+  const bool v = coll == SNAC_COLL_ALL_GATHER_V || coll == SNAC_COLL_REDUCE_SCATTER_V || coll == SNAC_COLL_ALL_TO_ALL_V;
+  const bool red = coll == SNAC_COLL_ALL_REDUCE || coll == SNAC_COLL_REDUCE_SCATTER || coll == SNAC_COLL_REDUCE_SCATTER_V;
+  if (red && !is_float(dtype)) return fail(SNAC_E_ARG, "reductions need SNAC_F32 or SNAC_BF16");
+  Plan p = base_plan((int32_t)coll, nranks, nranks, e);
+  if (v) {
+    if (!counts) return fail(SNAC_E_ARG, "counts is NULL");
+    const int nc = coll == SNAC_COLL_ALL_TO_ALL_V ? nranks * nranks : nranks;
+    for (int i = 0; i < nc; ++i) p.d.counts[i] = counts[i];
+  } else {
+    if (bytes % (size_t)e) return fail(SNAC_E_ARG, "bytes not a multiple of the element size");
+    if ((coll == SNAC_COLL_REDUCE_SCATTER || coll == SNAC_COLL_ALL_TO_ALL) && bytes % ((size_t)nranks * e))
+      return fail(SNAC_E_ARG, "bytes not a multiple of N * element size");
+    p.d.bytes = bytes;
+  }
+  const int nj = num_jobs(p.d);
+  int w = 0;
+  for (int j = 0; j < nj; ++j) {
+    const Job jb = make_job(p.d, j);
+    if (jb.bytes == 0) continue;
+    if (w >= max_jobs || !jobs) return fail(SNAC_E_ARG, "more than max_jobs (%d) jobs", max_jobs);
+    jobs[w].src_off = jb.src_off;
+    jobs[w].dst_off = jb.dst_off;
+    jobs[w].bytes = jb.bytes;
+    jobs[w].src_rank = jb.src_rank;
+    jobs[w].dst_rank = jb.dst_rank;
+    ++w;
+  }
+  *njobs = w;
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,133 @@
+// atoms.hpp -- gfx950 datapath primitives: the copy and N-to-1 reduce Atoms
+// work on 16-byte units (one global_load/store_dwordx4 per lane), accumulate
+// in binary32 in source order, and round bf16 outputs to nearest-even with
+// the hardware converter (v_cvt_pk_bf16_f32).
+//
+// The two primitives are the ones Purlin 0.6.4 ("# Purlin") puts under every
+// collective: copy, and an N-to-1 reduce that combines several input buffers
+// into one output.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace snac {
+
+constexpr int kThreads = 256;  // 4 wave64 per workgroup
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// same vector with 4-byte alignment: still one global_load_dwordx4 (the
+// hardware needs only dword alignment for multi-dword accesses)
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Cache policies for collective inputs and outputs.
+enum : int { kCacheDefault = 0, kCacheStream = 1, kCacheStreamStores = 2, kCacheStreamLoads = 3 };
+
+template <int CP>
+__device__ __forceinline__ u32x4 ld16(const char* p) {
+  if constexpr (CP == kCacheStream || CP == kCacheStreamLoads)
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  else
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
+template <int CP>
+__device__ __forceinline__ void st16(char* p, u32x4 v) {
+  if constexpr (CP == kCacheStream || CP == kCacheStreamStores)
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+  else
+    *reinterpret_cast<u32x4*>(p) = v;
+}
+
+// 16 bytes from any address.  m = p & 3 must be uniform across the wave.
+// m == 0: one dword-aligned dwordx4.  Otherwise the 20 bytes starting at the
+// dword below p are loaded (every dword touched holds at least one wanted
+// byte, so nothing outside the source range's dwords is read) and shifted
+// into place with v_alignbyte_b32.
+__device__ __forceinline__ u32x4 ld16_any(const char* p, uint32_t m) {
+  if (m == 0) return *reinterpret_cast<const u32x4_a4*>(p);
+  const char* b = p - m;
+  const u32x4 a = *reinterpret_cast<const u32x4_a4*>(b);
+  const uint32_t e = *reinterpret_cast<const uint32_t*>(b + 16);
+  u32x4 r;
+  r.x = __builtin_amdgcn_alignbyte(a.y, a.x, m);
+  r.y = __builtin_amdgcn_alignbyte(a.z, a.y, m);
+  r.z = __builtin_amdgcn_alignbyte(a.w, a.z, m);
+  r.w = __builtin_amdgcn_alignbyte(e, a.w, m);
+  return r;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two binary32 values -> two bf16 (round to nearest even), lo in bits 0..15.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const f32x2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+__device__ __forceinline__ uint16_t to_bf16(float x) { return (uint16_t)(pack_bf16(x, 0.0f) & 0xffffu); }
+
+struct F32 {
+  static constexpr int kSize = 4;
+};
+struct BF16 {
+  static constexpr int kSize = 2;
+};
+
+// One 16-byte unit of the N-to-1 reduce: out = R(v[0] + v[1] + ... + v[N-1])
+// per element, added in index order starting from v[0].
+template <typename T, int N>
+__device__ __forceinline__ u32x4 reduce_unit(const u32x4 (&v)[N]) {
+  u32x4 out;
+  if constexpr (T::kSize == 4) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      float acc = __uint_as_float(v[0][c]);
+#pragma unroll
+      for (int k = 1; k < N; ++k) acc = acc + __uint_as_float(v[k][c]);
+      out[c] = __float_as_uint(acc);
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      float lo = bf16_lo(v[0][c]);
+      float hi = bf16_hi(v[0][c]);
+#pragma unroll
+      for (int k = 1; k < N; ++k) {
+        lo = lo + bf16_lo(v[k][c]);
+        hi = hi + bf16_hi(v[k][c]);
+      }
+      out[c] = pack_bf16(lo, hi);
+    }
+  }
+  return out;
+}
+
+template <typename T>
+__device__ __forceinline__ float load_elem(const char* p) {
+  if constexpr (T::kSize == 4)
+    return *reinterpret_cast<const float*>(p);
+  else
+    return __uint_as_float((uint32_t)(*reinterpret_cast<const uint16_t*>(p)) << 16);
+}
+
+template <typename T>
+__device__ __forceinline__ void store_elem(char* p, float v) {
+  if constexpr (T::kSize == 4)
+    *reinterpret_cast<float*>(p) = v;
+  else
+    *reinterpret_cast<uint16_t*>(p) = to_bf16(v);
+}
+
+// Force a wave-uniform value into a scalar register.
+__device__ __forceinline__ uint32_t uniform(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ uint64_t uniform64(uint64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+}  // namespace snac

@@ -1,0 +1,65 @@
+// internal.hpp -- host-side interface between the C ABI and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "layout.hpp"
+
+namespace snac {
+
+struct LaunchCfg {
+  int wgs_per_cu;    // 0: as many as fit
+  int cache_policy;  // kCache*
+};
+
+// Tile size (bytes of each source per workgroup iteration) of the kernel
+// that serves this descriptor; the host needs it to size the grid.
+uint32_t coll_tile_bytes(const CollDesc& d, bool aligned);
+
+// Launch the copy or reduce kernel for a collective descriptor.  `tiles` is
+// the total tile count of the layout (computed on the host with the same
+// layout functions the kernel uses).
+hipError_t launch_collective(const CollDesc& d, bool aligned, uint64_t tiles, const LaunchCfg& cfg,
+                             hipStream_t stream);
+
+// Device-side SNAC pipeline (y = 0.5 x + r staged, then N-to-1 reduce).
+struct PipeArgs {
+  const void* x[kMaxRanks];
+  void* out;
+  uint64_t count;      // elements
+  int32_t nranks;
+  int32_t esize;
+  char* staging;       // [nranks][slots][tile_bytes]
+  uint64_t* ready;     // [nranks][slots], 16 words (128 B) apart
+  uint64_t* freed;     // [slots], 16 words apart
+  uint64_t* ctrl;      // control words, 16 apart: ticket, done, epoch, status
+  const uint32_t* abort_word;  // host-mapped
+  uint32_t slots;
+  uint32_t tile_bytes;
+  uint32_t lookahead;
+  uint32_t grid;
+  uint32_t spin_limit_log2;
+  int32_t drop_notify;  // r+1: rank r never notifies (test hook)
+  // Derived on the host so that every loop and branch condition in the
+  // kernel is a scalar (kernel-argument) value: a condition the compiler
+  // cannot prove uniform lets it restructure a loop that holds barriers.
+  uint32_t tiles;       // ceil(count / tile elements)
+  uint32_t items;       // (tiles + lookahead) * (nranks + 1)
+  uint32_t rounds;      // ceil(tiles / slots)
+  uint32_t tile_elems;  // tile_bytes / esize
+};
+
+enum : uint32_t { kCtrlTicket = 0, kCtrlDone = 16, kCtrlEpoch = 32, kCtrlStatus = 48, kCtrlWords = 64 };
+constexpr uint32_t kFlagStride = 16;  // uint64 words between flags (128 B)
+
+hipError_t launch_pipeline(const PipeArgs& a, int dtype_bf16, const LaunchCfg& cfg, hipStream_t stream,
+                           uint32_t* grid_out);
+
+// Fill `n` uint64 words with `v` (a kernel, so it may sit inside a captured
+// graph, unlike a memset node).
+hipError_t fill_u64(uint64_t* p, uint64_t n, uint64_t v, hipStream_t stream);
+
+int device_cu_count();
+
+}  // namespace snac

@@ -1,0 +1,190 @@
+// layout.hpp -- the layout engine: a collective -> a list of copy or reduce
+// jobs over byte ranges.
+//
+// "Layouts describe the collective: how inputs and outputs are distributed,
+// and whether to copy or reduce" (Purlin 0.6.4 project description, "Key
+// Idea").  The same functions run on the host (snac_plan, argument checks)
+// and in every workgroup of a collective kernel, which rebuilds the job table
+// in LDS from the compact descriptor passed as a kernel argument -- so no
+// per-call host-to-device copy is needed.
+//
+// Per-collective layouts (N ranks, B per-rank input bytes, e element size,
+// D(c) exclusive prefix sum of counts, every offset in bytes):
+//   AllReduce       1 reduce job: all sources [0,B) -> all destinations [0,B)
+//   ReduceScatter   job r: all sources [r*B/N, (r+1)*B/N) -> dst r [0, B/N)
+//   AllGather       job k: src k [0,B) -> all destinations [k*B, (k+1)*B)
+//   AllToAll        job (s,d): src s [d*B/N, ..) -> dst d [s*B/N, ..)
+//   AllGatherV      job k: src k [0, c_k e) -> all destinations at D(c)_k e
+//   ReduceScatterV  job r: all sources [D(c)_r e, ..) -> dst r [0, c_r e)
+//   AllToAllV       job (s,d): src s at sum_{j<d} C[s][j] e -> dst d at
+//                   sum_{j<s} C[j][d] e, C[s][d] e bytes
+// "All destinations" jobs are multicasts: one read, N writes.  When the
+// destination buffers do not share an address residue modulo 16 the host
+// sets split_multicast and each multicast becomes N single-destination jobs
+// so that every job can store with aligned 16-byte vectors.
+#pragma once
+
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define SNAC_HD __host__ __device__ inline
+#else
+#define SNAC_HD inline
+#endif
+
+namespace snac {
+
+constexpr int kMaxRanks = 16;
+constexpr int kMaxJobs = kMaxRanks * kMaxRanks;
+
+// Collective kinds: the public snac_coll values, plus the two raw Atoms.
+enum Coll : int32_t {
+  kAllReduce = 0,
+  kReduceScatter = 1,
+  kAllGather = 2,
+  kAllToAll = 3,
+  kAllGatherV = 4,
+  kReduceScatterV = 5,
+  kAllToAllV = 6,
+  kAtomCopy = 100,    // src[0] -> dst[0], `bytes`
+  kAtomReduce = 101,  // src[0..nsrc) -> dst[0..ndst), `bytes` per buffer
+};
+
+SNAC_HD bool coll_is_reduce(int32_t c) {
+  return c == kAllReduce || c == kReduceScatter || c == kReduceScatterV || c == kAtomReduce;
+}
+
+// Compact description of one collective call; passed by value to kernels.
+struct CollDesc {
+  int32_t coll;
+  int32_t nsrc;             // source buffers (= N for collectives)
+  int32_t ndst;             // destination buffers (= N for collectives)
+  int32_t esize;            // element size in bytes
+  int32_t split_multicast;  // see above
+  int32_t pad_;
+  uint64_t bytes;           // per-rank input bytes (fixed-size collectives, Atoms)
+  const void* src[kMaxRanks];
+  void* dst[kMaxRanks];
+  uint64_t counts[kMaxJobs];  // V collectives: element counts
+};
+
+struct Job {
+  uint64_t src_off;
+  uint64_t dst_off;
+  uint64_t bytes;
+  int32_t src_rank;  // -1: every source (reduce)
+  int32_t dst_rank;  // -1: every destination (multicast)
+};
+
+SNAC_HD int num_jobs(const CollDesc& d) {
+  const int n = d.nsrc;
+  switch (d.coll) {
+    case kAllReduce:
+    case kAtomReduce: return d.split_multicast ? d.ndst : 1;
+    case kReduceScatter:
+    case kReduceScatterV: return n;
+    case kAllGather:
+    case kAllGatherV: return d.split_multicast ? n * n : n;
+    case kAllToAll:
+    case kAllToAllV: return n * n;
+    case kAtomCopy: return 1;
+    default: return 0;
+  }
+}
+
+// Job j of a collective.  A job may have zero bytes (V counts of zero).
+SNAC_HD Job make_job(const CollDesc& d, int j) {
+  const int n = d.nsrc;
+  const uint64_t e = (uint64_t)d.esize;
+  Job r{0, 0, 0, -1, -1};
+  switch (d.coll) {
+    case kAllReduce:
+    case kAtomReduce:
+      r.bytes = d.bytes;
+      r.dst_rank = d.split_multicast ? j : -1;
+      break;
+    case kReduceScatter: {
+      const uint64_t chunk = d.bytes / (uint64_t)n;
+      r.src_off = (uint64_t)j * chunk;
+      r.bytes = chunk;
+      r.dst_rank = j;
+      break;
+    }
+    case kAllGather: {
+      const int k = d.split_multicast ? j / n : j;
+      r.src_rank = k;
+      r.dst_off = (uint64_t)k * d.bytes;
+      r.bytes = d.bytes;
+      r.dst_rank = d.split_multicast ? j % n : -1;
+      break;
+    }
+    case kAllToAll: {
+      const int s = j / n, dd = j % n;
+      const uint64_t chunk = d.bytes / (uint64_t)n;
+      r.src_rank = s;
+      r.dst_rank = dd;
+      r.src_off = (uint64_t)dd * chunk;
+      r.dst_off = (uint64_t)s * chunk;
+      r.bytes = chunk;
+      break;
+    }
+    case kAllGatherV: {
+      const int k = d.split_multicast ? j / n : j;
+      uint64_t disp = 0;
+      for (int i = 0; i < k; ++i) disp += d.counts[i];
+      r.src_rank = k;
+      r.dst_off = disp * e;
+      r.bytes = d.counts[k] * e;
+      r.dst_rank = d.split_multicast ? j % n : -1;
+      break;
+    }
+    case kReduceScatterV: {
+      uint64_t disp = 0;
+      for (int i = 0; i < j; ++i) disp += d.counts[i];
+      r.src_off = disp * e;
+      r.bytes = d.counts[j] * e;
+      r.dst_rank = j;
+      break;
+    }
+    case kAllToAllV: {
+      const int s = j / n, dd = j % n;
+      uint64_t sd = 0, rd = 0;
+      for (int i = 0; i < dd; ++i) sd += d.counts[s * n + i];
+      for (int i = 0; i < s; ++i) rd += d.counts[i * n + dd];
+      r.src_rank = s;
+      r.dst_rank = dd;
+      r.src_off = sd * e;
+      r.dst_off = rd * e;
+      r.bytes = d.counts[s * n + dd] * e;
+      break;
+    }
+    case kAtomCopy:
+      r.src_rank = 0;
+      r.dst_rank = 0;
+      r.bytes = d.bytes;
+      break;
+    default: break;
+  }
+  return r;
+}
+
+// Bytes of a job before its destination reaches a 16-byte boundary (0 when
+// the job is 16-byte aligned); always a multiple of the element size.
+SNAC_HD uint32_t job_head_bytes(const CollDesc& d, const Job& j) {
+  const int dr = j.dst_rank < 0 ? 0 : j.dst_rank;
+  const uint64_t a = (uint64_t)(uintptr_t)d.dst[dr] + j.dst_off;
+  uint64_t h = (16u - (uint32_t)(a & 15u)) & 15u;
+  if (h > j.bytes) h = j.bytes;
+  return (uint32_t)h;
+}
+
+// Tiles of a job: tile_bytes-sized pieces of its 16-byte body; the head and
+// tail bytes ride on tile 0.  A job with bytes but no body still gets one.
+SNAC_HD uint64_t job_tiles(const Job& j, uint32_t head, uint64_t tile_bytes) {
+  if (j.bytes == 0) return 0;
+  const uint64_t body = (j.bytes - head) & ~(uint64_t)15;
+  const uint64_t t = (body + tile_bytes - 1) / tile_bytes;
+  return t ? t : 1;
+}
+
+}  // namespace snac

@@ -1,0 +1,316 @@
+/*
+ * snac.h -- C ABI of the copy / N-to-1 reduce collective datapath for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The library runs single-kernel collectives over N "logical ranks" whose
+ * source, destination, staging and signal buffers all live in one GPU's HBM.
+ * Underneath every collective are two data-movement primitives (Atoms):
+ * copy, and N-to-1 reduce, which combines several input buffers into one
+ * output (Purlin 0.6.4 project description, "# Purlin").  A per-collective
+ * layout says which Atom runs on which byte ranges ("Key Idea": layouts
+ * describe the collective, SNAC coordinates execution, Atoms move the data).
+ *
+ * Conventions for every entry point:
+ *   - Pointers named src/dst/x/out are device pointers the caller owns; the
+ *     library never allocates per call.  Pointer arrays (src[], dst[],
+ *     counts[]) are host arrays read during the call, before it returns.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null
+ *     stream).  Buffers must stay alive until the stream has passed the call.
+ *   - Argument errors are reported synchronously (SNAC_E_ARG) and nothing is
+ *     enqueued.  Errors detected on the device (a consumer that waited too
+ *     long, an abort) latch in the context's status word; snac_check() and
+ *     snac_finalize() report them.
+ *   - A context is used from one host thread and one stream at a time.
+ *   - Reductions accumulate in binary32 in rank order 0..N-1 starting from
+ *     the rank-0 value and round once to the output type (bf16:
+ *     round-to-nearest-even).  Results are therefore bitwise repeatable, the
+ *     deterministic mode of Purlin 0.6.5 ("Reduction determinism"); there is
+ *     no non-deterministic mode.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef SNAC_H
+#define SNAC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SNAC_ABI_VERSION 1
+#define SNAC_MAX_RANKS 16
+
+typedef enum snac_status {
+  SNAC_OK = 0,
+  SNAC_E_ARG = 1,         /* invalid argument; nothing was enqueued */
+  SNAC_E_UNSUPPORTED = 2, /* valid request the library does not implement */
+  SNAC_E_NOMEM = 3,       /* device allocation failed (snac_init only) */
+  SNAC_E_HIP = 4,         /* a HIP runtime call failed */
+  SNAC_E_TIMEOUT = 5,     /* a device-side wait exceeded its spin limit */
+  SNAC_E_STATE = 6,       /* context unusable (aborted, or wrong device) */
+  SNAC_E_ABORTED = 7      /* device-side waits were abandoned by snac_abort */
+} snac_status;
+
+typedef enum snac_dtype {
+  SNAC_BYTE = 0, /* 1-byte opaque element: copy-only collectives */
+  SNAC_U32 = 1,  /* 4-byte opaque element: copy-only collectives */
+  SNAC_F32 = 2,  /* IEEE binary32 */
+  SNAC_BF16 = 3  /* bfloat16 (upper half of a binary32) */
+} snac_dtype;
+
+typedef enum snac_coll {
+  SNAC_COLL_ALL_REDUCE = 0,
+  SNAC_COLL_REDUCE_SCATTER = 1,
+  SNAC_COLL_ALL_GATHER = 2,
+  SNAC_COLL_ALL_TO_ALL = 3,
+  SNAC_COLL_ALL_GATHER_V = 4,
+  SNAC_COLL_REDUCE_SCATTER_V = 5,
+  SNAC_COLL_ALL_TO_ALL_V = 6
+} snac_coll;
+
+typedef void* snac_stream; /* hipStream_t */
+typedef struct snac_ctx snac_ctx;
+
+/* ------------------------------------------------------------------ info */
+
+/* ABI version of the loaded library (SNAC_ABI_VERSION at build time). */
+int snac_abi_version(void);
+
+/* Static string naming a status code; never NULL. */
+const char* snac_status_str(snac_status s);
+
+/* Human-readable detail of the last error returned to this host thread
+ * (empty string when none).  The pointer stays valid until the next call
+ * on this thread. */
+const char* snac_last_error(void);
+
+/* ------------------------------------------------------------- context */
+
+/*
+ * snac_init -- create a context for `nranks` logical ranks on the current
+ * HIP device (Purlin 0.6.5 "Host-side": create a context once with symmetric
+ * staging and signal buffers and reuse it for every collective).
+ *
+ *   nranks                  1 .. SNAC_MAX_RANKS
+ *   staging_bytes_per_rank  size of each rank's staging ring, used by the
+ *                           device-side SNAC pipeline.  0 selects the
+ *                           default (8 MiB).  It is split into slots of the
+ *                           pipeline tile size (64 KiB by default); at least
+ *                           2 slots are required.
+ *   stream                  signals are cleared on this stream.
+ *   out                     receives the context; on error *out is NULL.
+ *
+ * The context owns its workspace: staging[nranks][slots][tile] and the
+ * signal area (one 128-byte line per ready flag, per free flag and per
+ * control word).  Errors: SNAC_E_ARG (bad nranks/size/out), SNAC_E_NOMEM,
+ * SNAC_E_HIP.
+ */
+snac_status snac_init(int nranks, size_t staging_bytes_per_rank, snac_stream stream, snac_ctx** out);
+
+/*
+ * snac_finalize -- wait for `stream`, report any latched device error, and
+ * free the workspace (Purlin 0.6.5 "Host-side": finalize frees the internal
+ * buffers after the last collective).  NULL ctx is a no-op returning
+ * SNAC_OK.  The context is freed even when an error is returned.
+ */
+snac_status snac_finalize(snac_ctx* ctx, snac_stream stream);
+
+/*
+ * snac_check -- synchronise `stream`, read the context's device status word
+ * and clear it.  Returns SNAC_OK, SNAC_E_TIMEOUT or SNAC_E_ABORTED.
+ */
+snac_status snac_check(snac_ctx* ctx, snac_stream stream);
+
+/* Number of logical ranks of a context (0 for NULL). */
+int snac_ctx_nranks(const snac_ctx* ctx);
+
+/*
+ * snac_abort -- ask every device-side wait of this context to give up.  Sets
+ * a word in host-mapped memory that waiting workgroups poll; they exit
+ * without finishing their tile and latch SNAC_E_ABORTED.  Safe to call while
+ * a kernel runs.  snac_check() then reports SNAC_E_ABORTED and re-arms the
+ * context (clears the word and the signal state on its stream).
+ */
+snac_status snac_abort(snac_ctx* ctx);
+
+/* ---------------------------------------------------------------- Atoms */
+
+/*
+ * snac_copy -- the copy Atom: dst[0..bytes) = src[0..bytes), byte for byte
+ * (Purlin 0.6.5 "Samples": an Atom copies a slice from src to dst).  Any
+ * alignment and length; bytes == 0 is a no-op.  The ranges must not
+ * overlap (SNAC_E_ARG).  No context is needed.
+ */
+snac_status snac_copy(void* dst, const void* src, size_t bytes, snac_stream stream);
+
+/*
+ * snac_reduce_n -- the N-to-1 reduce Atom (Purlin 0.6.4 "# Purlin": it
+ * combines several input buffers into one output), writing the result to
+ * one or more outputs:
+ *     for d < ndst, i < count:  dst[d][i] = R(src[0][i] + ... + src[nsrc-1][i])
+ * summed in binary32 in index order, R = output rounding (identity for F32,
+ * round-to-nearest-even for BF16).
+ *   dst, ndst   1 <= ndst <= SNAC_MAX_RANKS output pointers
+ *   src, nsrc   1 <= nsrc <= SNAC_MAX_RANKS input pointers
+ *   count       elements per buffer (0 is a no-op)
+ *   dtype       SNAC_F32 or SNAC_BF16
+ * Every pointer must be aligned to the element size.  An output may equal
+ * an input (in place); any other overlap is SNAC_E_ARG.
+ */
+snac_status snac_reduce_n(void* const* dst, int ndst, const void* const* src, int nsrc, size_t count,
+                          snac_dtype dtype, snac_stream stream);
+
+/* ----------------------------------------------------------- collectives
+ *
+ * Every collective takes ctx (which fixes N = snac_ctx_nranks(ctx)), an array
+ * of N source pointers and an array of N destination pointers, one per
+ * logical rank, and runs as one kernel on `stream`.  Byte sizes must be
+ * multiples of the element size and pointers aligned to it.  A size of zero
+ * is a no-op.  Destination ranges may not overlap each other; a destination
+ * may overlap a source only in the in-place forms noted per call.
+ */
+
+/*
+ * snac_all_reduce -- AllReduce(sum): every dst[r] receives the reduction of
+ * all src[0..N-1] (NKI Collective Communication Kernels API,
+ * all_reduce_hbm_kernel and its worked example; Purlin 0.6.5 "Host-side").
+ *   bytes   per-rank input size = per-rank output size ("Understanding
+ *           totalBytes": the input size per rank)
+ *   dtype   SNAC_F32 or SNAC_BF16
+ * In place: dst[r] == src[r] is allowed.
+ */
+snac_status snac_all_reduce(snac_ctx* ctx, const void* const* src, void* const* dst, size_t bytes,
+                            snac_dtype dtype, snac_stream stream);
+
+/*
+ * snac_reduce_scatter -- dst[r] (bytes/N) receives the reduction of chunk r
+ * of every src, dim 0 split into N equal contiguous chunks (NKI
+ * reduce_scatter_hbm_kernel).  `bytes` is the per-rank input size and must
+ * be a multiple of N * element size (else SNAC_E_ARG; uneven splits use
+ * snac_reduce_scatter_v).  dtype: SNAC_F32 or SNAC_BF16.
+ * In place: dst[r] == src[r] + r * bytes/N is allowed.
+ */
+snac_status snac_reduce_scatter(snac_ctx* ctx, const void* const* src, void* const* dst, size_t bytes,
+                                snac_dtype dtype, snac_stream stream);
+
+/*
+ * snac_all_gather -- dst[r] (N * bytes) receives src[0..N-1] concatenated in
+ * rank order (NKI all_gather_hbm_kernel, dim 0).  `bytes` is the per-rank
+ * input size.  Any dtype.  In place: src[r] == dst[r] + r * bytes.
+ */
+snac_status snac_all_gather(snac_ctx* ctx, const void* const* src, void* const* dst, size_t bytes,
+                            snac_dtype dtype, snac_stream stream);
+
+/*
+ * snac_all_to_all -- chunk d of src[s] goes to chunk s of dst[d], chunks being
+ * bytes/N contiguous bytes (NKI all_to_all_hbm_kernel: rank s sends
+ * input[d, :] to rank d).  `bytes` is the per-rank input (= output) size and
+ * must be a multiple of N * element size.  Any dtype.  No in-place form.
+ */
+snac_status snac_all_to_all(snac_ctx* ctx, const void* const* src, void* const* dst, size_t bytes,
+                            snac_dtype dtype, snac_stream stream);
+
+/*
+ * snac_all_gather_v -- variable-length AllGather (Purlin 0.6.4 "# Purlin"
+ * lists variable-length variants).  counts[k] (elements) is rank k's input
+ * length; every dst[r] receives src[k][0..counts[k]) at element offset
+ * sum_{j<k} counts[j], packed.  Zero counts are allowed.  Any dtype.
+ */
+snac_status snac_all_gather_v(snac_ctx* ctx, const void* const* src, void* const* dst, const size_t* counts,
+                              snac_dtype dtype, snac_stream stream);
+
+/*
+ * snac_reduce_scatter_v -- variable-length ReduceScatter.  Every src holds
+ * sum(counts) elements; dst[r] receives counts[r] elements, the reduction of
+ * elements [D_r, D_r + counts[r]) of every src with D_r = sum_{j<r} counts[j].
+ * dtype: SNAC_F32 or SNAC_BF16.
+ */
+snac_status snac_reduce_scatter_v(snac_ctx* ctx, const void* const* src, void* const* dst, const size_t* counts,
+                                  snac_dtype dtype, snac_stream stream);
+
+/*
+ * snac_all_to_all_v -- variable-length AllToAll.  counts is an N x N
+ * row-major matrix, counts[s*N + d] = elements rank s sends to rank d.  Rank
+ * s's chunk for d starts at element sum_{j<d} counts[s*N+j] of src[s]; it
+ * lands in dst[d] at element sum_{j<s} counts[j*N+d].  dst[d] holds
+ * sum_s counts[s*N+d] elements.  Any dtype.
+ */
+snac_status snac_all_to_all_v(snac_ctx* ctx, const void* const* src, void* const* dst, const size_t* counts,
+                              snac_dtype dtype, snac_stream stream);
+
+/* ----------------------------------------------------- SNAC pipeline */
+
+/*
+ * snac_pipeline_scale_reduce -- a collective fused with compute inside one
+ * kernel, coordinated by the Stage / Notify / And Consume protocol (Purlin
+ * 0.6.4 "Key Idea"; Purlin 0.6.5 "Samples": a collective called from inside
+ * a kernel between other work).  Producer workgroups compute
+ * y_r = 0.5 * x[r] + r in binary32, round y_r to `dtype`, stage the tile in
+ * rank r's staging slot and raise that slot's ready flag with a release
+ * store.  Consumer workgroups acquire all N ready flags of a slot, N-to-1
+ * reduce the staged tiles in rank order into `out`, and release the slot.
+ *   x       N device pointers, each `count` elements
+ *   out     one output of `count` elements
+ *   dtype   SNAC_F32 or SNAC_BF16
+ * The context's staging ring bounds the work in flight; any count works.
+ */
+snac_status snac_pipeline_scale_reduce(snac_ctx* ctx, const void* const* x, void* out, size_t count,
+                                       snac_dtype dtype, snac_stream stream);
+
+/* -------------------------------------------------------- layout engine */
+
+/*
+ * One unit of work of a collective: move `bytes` bytes from the source
+ * buffer(s) at byte offset src_off to the destination buffer(s) at dst_off.
+ * src_rank == -1 means "every rank's source buffer" (an N-to-1 reduce job);
+ * dst_rank == -1 means "every rank's destination buffer" (a multicast).
+ */
+typedef struct snac_job {
+  uint64_t src_off;
+  uint64_t dst_off;
+  uint64_t bytes;
+  int32_t src_rank;
+  int32_t dst_rank;
+} snac_job;
+
+/*
+ * snac_plan -- host-only: the layout of a collective as the kernels see it
+ * ("Key Idea": layouts describe how inputs and outputs are distributed and
+ * whether to copy or reduce).  Runs no GPU code.
+ *   coll, nranks, dtype   the collective
+ *   bytes                 per-rank input size (fixed-size collectives)
+ *   counts                element counts (V collectives: N for ALL_GATHER_V
+ *                         and REDUCE_SCATTER_V, N*N for ALL_TO_ALL_V)
+ *   jobs, max_jobs        output array; *njobs receives the job count.
+ * Zero-length jobs are omitted.  Returns SNAC_E_ARG if the request is
+ * invalid or more than max_jobs jobs result.
+ */
+snac_status snac_plan(snac_coll coll, int nranks, snac_dtype dtype, size_t bytes, const size_t* counts,
+                      snac_job* jobs, int max_jobs, int* njobs);
+
+/* --------------------------------------------------------------- tuning */
+
+/*
+ * Process-wide launch parameters (Purlin 0.6.4 "Key Idea" mentions tuning
+ * for peak performance).  Zero fields select the defaults.
+ */
+typedef struct snac_tuning {
+  int32_t wgs_per_cu;      /* workgroups per compute unit in the persistent grid */
+  int32_t cache_policy;    /* 0 default, 1 streaming loads+stores, 2 streaming stores, 3 streaming loads */
+  int32_t pipeline_tile_bytes; /* per-rank bytes per pipeline tile (multiple of 4096) */
+  int32_t pipeline_lookahead;  /* tiles staged ahead of the consumers */
+  int32_t spin_limit_log2;     /* device waits give up after 2^k polls */
+  int32_t debug_drop_notify;   /* test hook: when r+1, rank r's producers never
+                                  raise their ready flags, so consumers time out */
+  int32_t reserved[2];
+} snac_tuning;
+
+snac_status snac_get_tuning(snac_tuning* out);
+snac_status snac_set_tuning(const snac_tuning* in);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SNAC_H */

@@ -1,0 +1,81 @@
+"""Properties of the gfx950 code the compiler emits for the kernels
+(CPU only: hipcc cross-compiles to assembly, nothing runs).
+
+* In the SNAC pipeline kernel every workgroup barrier must sit in the
+  ticket loop itself, never inside a nested loop.  When the compiler
+  cannot prove the loop's control flow uniform it may split the loop so
+  that the lanes of one wave reach a barrier on different iterations,
+  which deadlocks the workgroup.
+* No packed fp32 arithmetic (the build disables that target feature).
+"""
+from __future__ import annotations
+
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "copy_reduce_snac_amd", "csrc")
+
+hipcc = shutil.which("hipcc") or ("/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else None)
+pytestmark = pytest.mark.skipif(hipcc is None, reason="hipcc not available")
+
+PACKED = ["v_pk_" + op + "_f32" for op in ("add", "mul", "fma")]
+
+
+def _asm(src: str, tmp_path) -> str:
+    from copy_reduce_snac_amd.build import DEVICE_FLAGS
+
+    out = tmp_path / (src + ".s")
+    flags = [f for f in DEVICE_FLAGS if f not in ("-fPIC",)]
+    subprocess.run([hipcc, *flags, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", str(out)],
+                   check=True, capture_output=True)
+    return out.read_text()
+
+
+def _kernels(asm: str) -> dict[str, list[str]]:
+    out = {}
+    cur = None
+    for line in asm.splitlines():
+        m = re.match(r"^(_Z\S+):\s", line + " ")
+        if m and not line.startswith("\t"):
+            cur = m.group(1)
+            out[cur] = []
+            continue
+        if cur is not None:
+            out[cur].append(line)
+            if "s_endpgm" in line:
+                cur = None
+    return out
+
+
+def _barrier_depths(lines: list[str]) -> list[int]:
+    depth = 0
+    found = []
+    for l in lines:
+        m = re.match(r"^\.LBB\d+_\d+:(.*)", l)
+        if m:
+            d = re.search(r"Depth=(\d+)", m.group(1))
+            depth = int(d.group(1)) if d else 0
+        if "s_barrier" in l:
+            found.append(depth)
+    return found
+
+
+def test_pipeline_barriers_only_in_the_ticket_loop(tmp_path):
+    ks = {k: v for k, v in _kernels(_asm("pipeline.hip", tmp_path)).items() if "pipeline_kernel" in k}
+    assert len(ks) == 32
+    for name, lines in ks.items():
+        depths = _barrier_depths(lines)
+        assert depths, name
+        assert max(depths) <= 1, f"{name}: barrier inside a nested loop"
+
+
+@pytest.mark.parametrize("src", ["collectives.hip", "pipeline.hip"])
+def test_no_packed_fp32(tmp_path, src):
+    asm = _asm(src, tmp_path)
+    for op in PACKED:
+        assert op not in asm, f"{src}: {op} emitted"
