@@ -121,14 +121,16 @@ int needs_split(void* const* dst, int ndst) {
   return 0;
 }
 
-snac_status check_ptrs(const void* const* src, int nsrc, void* const* dst, int ndst, int esize) {
+// A buffer may be NULL only when its extent (in_bytes/out_bytes) is zero.
+snac_status check_ptrs(const void* const* src, const uint64_t* in_bytes, int nsrc, void* const* dst,
+                       const uint64_t* out_bytes, int ndst, int esize) {
   if (!src || !dst) return fail(SNAC_E_ARG, "src and dst pointer arrays must not be NULL");
   for (int i = 0; i < nsrc; ++i) {
-    if (!src[i]) return fail(SNAC_E_ARG, "src[%d] is NULL", i);
+    if (!src[i] && in_bytes[i]) return fail(SNAC_E_ARG, "src[%d] is NULL", i);
     if ((uintptr_t)src[i] % (uintptr_t)esize) return fail(SNAC_E_ARG, "src[%d] not aligned to %d bytes", i, esize);
   }
   for (int i = 0; i < ndst; ++i) {
-    if (!dst[i]) return fail(SNAC_E_ARG, "dst[%d] is NULL", i);
+    if (!dst[i] && out_bytes[i]) return fail(SNAC_E_ARG, "dst[%d] is NULL", i);
     if ((uintptr_t)dst[i] % (uintptr_t)esize) return fail(SNAC_E_ARG, "dst[%d] not aligned to %d bytes", i, esize);
   }
   return SNAC_OK;
@@ -195,12 +197,12 @@ snac_status fixed_collective(int32_t coll, snac_ctx* ctx, const void* const* src
   if ((coll == kReduceScatter || coll == kAllToAll) && bytes % ((size_t)n * e))
     return fail(SNAC_E_ARG, "bytes (%zu) is not a multiple of N * element size (%d)", bytes, n * e);
   if (bytes == 0) return ok();
-  if ((st = check_ptrs(src, n, dst, n, e)) != SNAC_OK) return st;
   uint64_t in_b[kMaxRanks], out_b[kMaxRanks];
   for (int i = 0; i < n; ++i) {
     in_b[i] = bytes;
     out_b[i] = coll == kAllGather ? bytes * n : (coll == kReduceScatter ? bytes / n : bytes);
   }
+  if ((st = check_ptrs(src, in_b, n, dst, out_b, n, e)) != SNAC_OK) return st;
   const size_t chunk = bytes / (size_t)n;
   st = check_overlap(src, in_b, n, dst, out_b, n, [&](int d, int s) {
     if (d != s) return false;
@@ -236,7 +238,6 @@ snac_status v_collective(int32_t coll, snac_ctx* ctx, const void* const* src, vo
     total += counts[i];
   }
   if (total == 0) return ok();
-  if ((st = check_ptrs(src, n, dst, n, e)) != SNAC_OK) return st;
   uint64_t in_b[kMaxRanks], out_b[kMaxRanks];
   for (int i = 0; i < n; ++i) {
     if (coll == kAllGatherV) {
@@ -255,6 +256,7 @@ snac_status v_collective(int32_t coll, snac_ctx* ctx, const void* const* src, vo
       out_b[i] = col * e;
     }
   }
+  if ((st = check_ptrs(src, in_b, n, dst, out_b, n, e)) != SNAC_OK) return st;
   st = check_overlap(src, in_b, n, dst, out_b, n, [](int, int) { return false; });
   if (st != SNAC_OK) return st;
   Plan p = base_plan(coll, n, n, e);
@@ -419,11 +421,11 @@ snac_status snac_reduce_n(void* const* dst, int ndst, const void* const* src, in
   if (!is_float(dtype)) return fail(SNAC_E_ARG, "reduce needs SNAC_F32 or SNAC_BF16");
   if (count == 0) return ok();
   const int e = esize_of(dtype);
-  snac_status st = check_ptrs(src, nsrc, dst, ndst, e);
-  if (st != SNAC_OK) return st;
   const uint64_t bytes = (uint64_t)count * e;
   uint64_t in_b[kMaxRanks], out_b[kMaxRanks];
   for (int i = 0; i < kMaxRanks; ++i) in_b[i] = out_b[i] = bytes;
+  snac_status st = check_ptrs(src, in_b, nsrc, dst, out_b, ndst, e);
+  if (st != SNAC_OK) return st;
   st = check_overlap(src, in_b, nsrc, dst, out_b, ndst,
                      [&](int d, int s) { return (uintptr_t)dst[d] == (uintptr_t)src[s]; });
   if (st != SNAC_OK) return st;

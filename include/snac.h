@@ -12,7 +12,8 @@
  *
  * Conventions for every entry point:
  *   - Pointers named src/dst/x/out are device pointers the caller owns; the
- *     library never allocates per call.  Pointer arrays (src[], dst[],
+ *     library never allocates per call.  A buffer whose extent is zero (a
+ *     rank with a zero count in a V collective) may be NULL.  Pointer arrays (src[], dst[],
  *     counts[]) are host arrays read during the call, before it returns.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null
  *     stream).  Buffers must stay alive until the stream has passed the call.

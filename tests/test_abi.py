@@ -1,0 +1,190 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the header
+declares, rejects invalid arguments before touching the GPU, and its layout
+engine (snac_plan, the same code the kernels run) describes each collective
+exactly: applying its jobs on the host reproduces the oracle."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import copy_reduce_snac_amd as snac
+import oracle
+from copy_reduce_snac_amd import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "snac.h")
+
+
+def declared_functions() -> list[str]:
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(snac_[a-z_0-9]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = snac.lib()
+    names = declared_functions()
+    assert len(names) >= 20
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in snac.h but not exported"
+    # and the binding wraps each of them under the same name
+    for n in names:
+        assert hasattr(snac, n), f"binding lacks {n}"
+
+
+def test_nm_shows_c_linkage():
+    import subprocess
+
+    out = subprocess.run(["nm", "-D", "--defined-only", snac.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (snac_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def test_versions_and_status_strings():
+    assert snac.snac_abi_version() == 1
+    for s in range(8):
+        assert snac.snac_status_str(s).startswith("SNAC_")
+    assert "unknown" in snac.snac_status_str(99)
+
+
+def _expect(status, fn, *args):
+    with pytest.raises(snac.SnacError) as e:
+        fn(*args)
+    assert e.value.status == status, str(e.value)
+    return str(e.value)
+
+
+def test_argument_errors_without_gpu():
+    E = snac.SNAC_E_ARG
+    _expect(E, snac.snac_init, 0, 0)
+    _expect(E, snac.snac_init, 17, 0)
+    _expect(E, snac.snac_copy, 0, 0x1000, 16)
+    _expect(E, snac.snac_copy, 0x1000, 0x1008, 16)  # overlap
+    _expect(E, snac.snac_reduce_n, [0x1000], [0x2000], 8, "byte")
+    _expect(E, snac.snac_reduce_n, [0x1000], [0x2000] * 17, 8, "f32")
+    _expect(E, snac.snac_reduce_n, [0x1001], [0x2000], 8, "f32")  # misaligned
+    _expect(E, snac.snac_reduce_n, [0x1000], [0x2000, 0x1010], 8, "f32")  # dst overlaps a src
+    _expect(E, snac.snac_all_reduce, None, [0x1000], [0x2000], 16, "f32")
+    _expect(E, snac.snac_check, None)
+    _expect(E, snac.snac_abort, None)
+    assert snac.snac_ctx_nranks(None) == 0
+    # zero-size calls are no-ops, even with NULL pointers
+    snac.snac_copy(0, 0, 0)
+    snac.snac_reduce_n([0], [0], 0, "f32")
+    snac.snac_finalize(None)
+
+
+def test_tuning_roundtrip_and_ranges():
+    t0 = snac.snac_get_tuning()
+    try:
+        snac.snac_set_tuning(wgs_per_cu=3, cache_policy=1)
+        t = snac.snac_get_tuning()
+        assert t["wgs_per_cu"] == 3 and t["cache_policy"] == 1
+        _expect(snac.SNAC_E_ARG, lambda: snac.snac_set_tuning(cache_policy=9))
+        _expect(snac.SNAC_E_ARG, lambda: snac.snac_set_tuning(pipeline_tile_bytes=1000))
+    finally:
+        snac.snac_set_tuning(**t0)
+
+
+# ------------------------------------------------------------------ layouts
+COLLS = {
+    "all_reduce": snac.SNAC_COLL_ALL_REDUCE,
+    "reduce_scatter": snac.SNAC_COLL_REDUCE_SCATTER,
+    "all_gather": snac.SNAC_COLL_ALL_GATHER,
+    "all_to_all": snac.SNAC_COLL_ALL_TO_ALL,
+    "all_gather_v": snac.SNAC_COLL_ALL_GATHER_V,
+    "reduce_scatter_v": snac.SNAC_COLL_REDUCE_SCATTER_V,
+    "all_to_all_v": snac.SNAC_COLL_ALL_TO_ALL_V,
+}
+
+
+def apply_plan(jobs, srcs_bytes, out_sizes, dtype, n, esize):
+    """Interpret a job list on the host: copy jobs move bytes, reduce jobs
+    call the oracle's N-to-1 reduce on the element range.  Also checks that
+    every output byte is written exactly once."""
+    outs = [np.zeros(s, dtype=np.uint8) for s in out_sizes]
+    written = [np.zeros(s, dtype=np.int32) for s in out_sizes]
+    npd = {"f32": np.float32, "bf16": np.uint16}.get(dtype)
+    for src_off, dst_off, nbytes, sr, dr in jobs:
+        assert nbytes > 0 and nbytes % esize == 0 and src_off % esize == 0 and dst_off % esize == 0
+        if sr < 0:
+            parts = [s[src_off:src_off + nbytes].view(npd) for s in srcs_bytes]
+            data = oracle.reduce_n(parts, dtype).view(np.uint8)
+        else:
+            assert src_off + nbytes <= srcs_bytes[sr].size
+            data = srcs_bytes[sr][src_off:src_off + nbytes]
+        targets = range(n) if dr < 0 else [dr]
+        for d in targets:
+            assert dst_off + nbytes <= out_sizes[d]
+            outs[d][dst_off:dst_off + nbytes] = data
+            written[d][dst_off:dst_off + nbytes] += 1
+    for w in written:
+        assert np.all(w == 1), "an output byte was written zero or several times"
+    return outs
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 5, 8, 16])
+@pytest.mark.parametrize("name", sorted(COLLS))
+def test_plan_matches_oracle(name, n):
+    dtype = "bf16" if "reduce" in name else "u32"
+    esize = 2 if dtype == "bf16" else 4
+    g = np.random.default_rng(n)
+    if name in ("all_reduce", "all_gather"):
+        m = 37
+        srcs = [wl.raw_bytes(m * esize, wl.CFG_TEST, r) for r in range(n)]
+        jobs = snac.snac_plan(COLLS[name], n, dtype, m * esize)
+        if name == "all_reduce":
+            want = oracle.all_reduce([s.view(np.uint16) for s in srcs], "bf16")
+            sizes = [m * esize] * n
+        else:
+            want = oracle.all_gather(srcs)
+            sizes = [n * m * esize] * n
+    elif name in ("reduce_scatter", "all_to_all"):
+        m = 6 * n
+        srcs = [wl.raw_bytes(m * esize, wl.CFG_TEST, r) for r in range(n)]
+        jobs = snac.snac_plan(COLLS[name], n, dtype, m * esize)
+        if name == "reduce_scatter":
+            want = oracle.reduce_scatter([s.view(np.uint16) for s in srcs], "bf16")
+            sizes = [m // n * esize] * n
+        else:
+            want = oracle.all_to_all(srcs)
+            sizes = [m * esize] * n
+    elif name == "all_to_all_v":
+        c = g.integers(0, 6, size=(n, n))
+        c[0, 0] = 0
+        srcs = [wl.raw_bytes(int(c[s].sum()) * esize, wl.CFG_TEST, s) for s in range(n)]
+        jobs = snac.snac_plan(COLLS[name], n, dtype, 0, c.reshape(-1).tolist())
+        want = oracle.all_to_all_v([s.view(np.uint32) for s in srcs], c)
+        sizes = [int(c[:, d].sum()) * esize for d in range(n)]
+    else:
+        c = g.integers(0, 6, size=n)
+        c[-1] = 0
+        tot = int(c.sum())
+        jobs = snac.snac_plan(COLLS[name], n, dtype, 0, c.tolist())
+        if name == "all_gather_v":
+            srcs = [wl.raw_bytes(int(c[k]) * esize, wl.CFG_TEST, k) for k in range(n)]
+            want = oracle.all_gather_v([s.view(np.uint32) for s in srcs], list(c))
+            sizes = [tot * esize] * n
+        else:
+            srcs = [wl.raw_bytes(tot * esize, wl.CFG_TEST, k) for k in range(n)]
+            want = oracle.reduce_scatter_v([s.view(np.uint16) for s in srcs], list(c), "bf16")
+            sizes = [int(x) * esize for x in c]
+    outs = apply_plan(jobs, srcs, sizes, dtype, n, esize)
+    for o, w in zip(outs, want):
+        assert np.array_equal(o, np.asarray(w).view(np.uint8))
+
+
+def test_plan_rejects_bad_requests():
+    E = snac.SNAC_E_ARG
+    _expect(E, snac.snac_plan, snac.SNAC_COLL_REDUCE_SCATTER, 3, "f32", 16)  # not N*e divisible
+    _expect(E, snac.snac_plan, snac.SNAC_COLL_ALL_REDUCE, 2, "byte", 16)      # reduce needs floats
+    _expect(E, snac.snac_plan, snac.SNAC_COLL_ALL_REDUCE, 0, "f32", 16)
+    _expect(E, snac.snac_plan, 42, 2, "f32", 16)
+    _expect(E, snac.snac_plan, snac.SNAC_COLL_ALL_TO_ALL_V, 2, "f32", 0, None)
+    # more jobs than room
+    with pytest.raises(snac.SnacError):
+        snac.snac_plan(snac.SNAC_COLL_ALL_TO_ALL, 4, "f32", 64, max_jobs=3)
