@@ -57,8 +57,10 @@ snac_status hip_fail(hipError_t e, const char* what) {
 
 snac_tuning g_tuning = {0, 0, 0, 0, 0, 0, {0, 0}};
 
-constexpr uint32_t kDefaultPipeTile = 64u * 1024u;
-constexpr size_t kDefaultStaging = 8u * 1024u * 1024u;
+constexpr uint32_t kMaxPipeTile = 512u * 1024u;
+constexpr uint32_t kMinPipeTile = 4096u;
+constexpr uint32_t kMinAutoSlots = 64u;
+constexpr size_t kDefaultStaging = 32u * 1024u * 1024u;
 constexpr int kDefaultSpinLog2 = 22;
 
 LaunchCfg launch_cfg() { return LaunchCfg{g_tuning.wgs_per_cu, g_tuning.cache_policy}; }
@@ -302,7 +304,7 @@ snac_status snac_get_tuning(snac_tuning* out) {
 snac_status snac_set_tuning(const snac_tuning* in) {
   if (!in) return fail(SNAC_E_ARG, "in is NULL");
   if (in->wgs_per_cu < 0 || in->wgs_per_cu > 32) return fail(SNAC_E_ARG, "wgs_per_cu out of range [0, 32]");
-  if (in->cache_policy < 0 || in->cache_policy > 3) return fail(SNAC_E_ARG, "cache_policy out of range [0, 3]");
+  if (in->cache_policy < 0 || in->cache_policy > 4) return fail(SNAC_E_ARG, "cache_policy out of range [0, 4]");
   if (in->pipeline_tile_bytes < 0 || in->pipeline_tile_bytes % 4096)
     return fail(SNAC_E_ARG, "pipeline_tile_bytes must be a non-negative multiple of 4096");
   if (in->pipeline_lookahead < 0) return fail(SNAC_E_ARG, "pipeline_lookahead must be >= 0");
@@ -317,8 +319,14 @@ snac_status snac_init(int nranks, size_t staging_bytes_per_rank, snac_stream str
   if (!out) return fail(SNAC_E_ARG, "out is NULL");
   *out = nullptr;
   if (nranks < 1 || nranks > SNAC_MAX_RANKS) return fail(SNAC_E_ARG, "nranks %d outside 1..%d", nranks, SNAC_MAX_RANKS);
-  const uint32_t tile = g_tuning.pipeline_tile_bytes ? (uint32_t)g_tuning.pipeline_tile_bytes : kDefaultPipeTile;
   const size_t staging = staging_bytes_per_rank ? staging_bytes_per_rank : kDefaultStaging;
+  // pipeline tile: the tuning value, else the largest power of two up to
+  // 512 KiB that still leaves at least 64 slots in the ring
+  uint32_t tile = (uint32_t)g_tuning.pipeline_tile_bytes;
+  if (!tile) {
+    tile = kMaxPipeTile;
+    while (tile > kMinPipeTile && staging / tile < kMinAutoSlots) tile >>= 1;
+  }
   if (staging % tile) return fail(SNAC_E_ARG, "staging_bytes_per_rank must be a multiple of the pipeline tile (%u)", tile);
   const uint64_t slots = staging / tile;
   if (slots < 2 || slots > (1u << 20)) return fail(SNAC_E_ARG, "staging ring needs 2 .. 2^20 slots (got %llu)", (unsigned long long)slots);
@@ -333,7 +341,7 @@ snac_status snac_init(int nranks, size_t staging_bytes_per_rank, snac_stream str
   c->slots = (uint32_t)slots;
   c->tile_bytes = tile;
   const uint64_t ready_words = (uint64_t)nranks * slots * kFlagStride;
-  const uint64_t free_words = slots * kFlagStride;
+  const uint64_t free_words = (uint64_t)nranks * slots * kFlagStride;
   c->signal_words = ready_words + free_words + kCtrlWords;
   const size_t staging_total = (size_t)nranks * staging;
   const size_t bytes = staging_total + c->signal_words * sizeof(uint64_t);

@@ -22,8 +22,10 @@ typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-// Cache policies for collective inputs and outputs.
-enum : int { kCacheDefault = 0, kCacheStream = 1, kCacheStreamStores = 2, kCacheStreamLoads = 3 };
+// Cache policies for collective inputs and outputs: streaming accesses carry
+// the non-temporal hint (global_load/store ... nt), so single-use data does
+// not displace other lines.
+enum : int { kCached = 0, kCacheStream = 1, kCacheStreamStores = 2, kCacheStreamLoads = 3 };
 
 template <int CP>
 __device__ __forceinline__ u32x4 ld16(const char* p) {

@@ -85,6 +85,11 @@ __device__ uint32_t build_table(const CollDesc& d, uint32_t tile_bytes, JobL* jo
 // NU > 0 unrolls the multicast for the common case ndst == NU.
 template <int U, int CP>
 __device__ __forceinline__ void store_one(char* p, uint32_t lane, uint32_t rem, const u32x4 (&v)[U]) {
+  if (rem == tile_of<U>()) {  // full tile: no per-unit guards
+#pragma unroll
+    for (int u = 0; u < U; ++u) st16<CP>(p + lane + (uint32_t)u * kThreads * 16u, v[u]);
+    return;
+  }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const uint32_t o = lane + (uint32_t)u * kThreads * 16u;
@@ -110,6 +115,65 @@ __device__ __forceinline__ void store_units(const CollDesc& d, int32_t dst_rank,
   for (int k = 0; k < nd; ++k) store_one<U, CP>(static_cast<char*>(d.dst[k]) + base, lane, rem, v);
 }
 
+// A tile resolved against its job: everything the loads and stores need.
+struct TileRef {
+  JobL J;
+  uint32_t lt;     // tile index within the job
+  uint64_t toff;   // byte offset of the tile's first 16-byte unit in the job
+  uint32_t rem;    // body bytes of this tile (multiple of 16; 0 for an edge-only tile)
+  uint32_t head;   // job head bytes (generic path)
+  uint64_t body;   // job body bytes
+};
+
+// Walks the job table in tile order.  The current job lives in scalar
+// registers; LDS is read only when a tile crosses into a later job, so a
+// tile of a long job costs a compare and a few scalar ops.
+template <int U, bool ALIGNED>
+struct JobCursor {
+  const JobL* jobs;
+  int nj;
+  int j;
+  uint32_t next_tile0;  // first tile of job j + 1 (or ~0)
+  JobL J;
+
+  __device__ __forceinline__ void load_job() {
+    J.src_off = uniform64(jobs[j].src_off);
+    J.dst_off = uniform64(jobs[j].dst_off);
+    J.bytes = uniform64(jobs[j].bytes);
+    J.src_rank = (int32_t)uniform((uint32_t)jobs[j].src_rank);
+    J.dst_rank = (int32_t)uniform((uint32_t)jobs[j].dst_rank);
+    J.head = ALIGNED ? 0u : uniform(jobs[j].head);
+    J.tile0 = uniform(jobs[j].tile0);
+    next_tile0 = j + 1 < nj ? uniform(jobs[j + 1].tile0) : 0xffffffffu;
+  }
+
+  __device__ __forceinline__ void init(const JobL* t, int n, uint32_t tile) {
+    jobs = t;
+    nj = n;
+    j = 0;
+    while (j + 1 < nj && jobs[j + 1].tile0 <= tile) ++j;
+    load_job();
+  }
+
+  __device__ __forceinline__ TileRef at(uint32_t tile) {
+    if (tile >= next_tile0) {
+      while (j + 1 < nj && jobs[j + 1].tile0 <= tile) ++j;
+      load_job();
+    }
+    constexpr uint32_t TILE = tile_of<U>();
+    TileRef r;
+    r.J = J;
+    r.lt = tile - J.tile0;
+    r.head = J.head;
+    r.body = ALIGNED ? J.bytes : ((J.bytes - r.head) & ~(uint64_t)15);
+    r.toff = (uint64_t)r.head + (uint64_t)r.lt * TILE;
+    const uint64_t end = (uint64_t)r.head + r.body;
+    const uint64_t left = end > r.toff ? end - r.toff : 0;
+    r.rem = left > TILE ? TILE : (uint32_t)left;
+    return r;
+  }
+};
+
 // ---------------------------------------------------------------- reduce
 
 template <typename T, int N>
@@ -130,39 +194,29 @@ __device__ void reduce_edges(const CollDesc& d, const JobL& J, uint32_t head, ui
   }
 }
 
-template <typename T, int N, int U, int CP, bool ALIGNED>
-__device__ __forceinline__ void reduce_tile(const CollDesc& d, const JobL& J, uint32_t lt) {
-  constexpr uint32_t TILE = tile_of<U>();
-  const uint32_t head = ALIGNED ? 0u : J.head;
-  const uint64_t body = ALIGNED ? J.bytes : ((J.bytes - head) & ~(uint64_t)15);
-  if constexpr (!ALIGNED) {
-    if (lt == 0) reduce_edges<T, N>(d, J, head, body);
-    if (body == 0) return;
+// Issue the U*N loads of one tile.
+template <int N, int U, int CP, bool ALIGNED>
+__device__ __forceinline__ void reduce_load(const CollDesc& d, const TileRef& t, u32x4 (&v)[U][N]) {
+  const uint32_t lane = threadIdx.x * 16u;
+  if (ALIGNED && t.rem == tile_of<U>()) {  // full tile: no per-unit guards
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      const char* sp = static_cast<const char*>(d.src[k]) + t.J.src_off + t.toff + lane;
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u][k] = ld16<CP>(sp + (uint32_t)u * kThreads * 16u);
+    }
+    return;
   }
-  const uint64_t toff = (uint64_t)head + (uint64_t)lt * TILE;
-  const uint64_t left = (uint64_t)head + body - toff;
-  const uint32_t rem = left > TILE ? TILE : (uint32_t)left;
-  const char* sp[N];
-  uint32_t m[N];
 #pragma unroll
   for (int k = 0; k < N; ++k) {
-    sp[k] = static_cast<const char*>(d.src[k]) + J.src_off + toff;
-    m[k] = uniform((uint32_t)(uintptr_t)sp[k] & 3u);
-  }
-  const uint32_t lane = threadIdx.x * 16u;
-  u32x4 v[U][N];
+    const char* sp = static_cast<const char*>(d.src[k]) + t.J.src_off + t.toff;
+    const uint32_t m = ALIGNED ? 0u : uniform((uint32_t)(uintptr_t)sp & 3u);
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const uint32_t o = lane + (uint32_t)u * kThreads * 16u;
-    if (o < rem) {
-#pragma unroll
-      for (int k = 0; k < N; ++k) v[u][k] = ALIGNED ? ld16<CP>(sp[k] + o) : ld16_any(sp[k] + o, m[k]);
+    for (int u = 0; u < U; ++u) {
+      const uint32_t o = lane + (uint32_t)u * kThreads * 16u;
+      if (o < t.rem) v[u][k] = ALIGNED ? ld16<CP>(sp + o) : ld16_any(sp + o, m);
     }
   }
-  u32x4 r[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) r[u] = reduce_unit<T, N>(v[u]);
-  store_units<U, CP, N>(d, J.dst_rank, J.dst_off + toff, lane, rem, r);
 }
 
 // ------------------------------------------------------------------ copy
@@ -181,32 +235,29 @@ __device__ void copy_edges(const CollDesc& d, const JobL& J, uint32_t head, uint
 }
 
 template <int U, int CP, bool ALIGNED>
-__device__ __forceinline__ void copy_tile(const CollDesc& d, const JobL& J, uint32_t lt) {
-  constexpr uint32_t TILE = tile_of<U>();
-  const uint32_t head = ALIGNED ? 0u : J.head;
-  const uint64_t body = ALIGNED ? J.bytes : ((J.bytes - head) & ~(uint64_t)15);
-  if constexpr (!ALIGNED) {
-    if (lt == 0) copy_edges(d, J, head, body);
-    if (body == 0) return;
-  }
-  const uint64_t toff = (uint64_t)head + (uint64_t)lt * TILE;
-  const uint64_t left = (uint64_t)head + body - toff;
-  const uint32_t rem = left > TILE ? TILE : (uint32_t)left;
-  const char* sp = static_cast<const char*>(d.src[J.src_rank]) + J.src_off + toff;
-  const uint32_t m = uniform((uint32_t)(uintptr_t)sp & 3u);
+__device__ __forceinline__ void copy_load(const CollDesc& d, const TileRef& t, u32x4 (&v)[U]) {
+  const char* sp = static_cast<const char*>(d.src[t.J.src_rank]) + t.J.src_off + t.toff;
   const uint32_t lane = threadIdx.x * 16u;
-  u32x4 v[U];
+  if (ALIGNED && t.rem == tile_of<U>()) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = ld16<CP>(sp + lane + (uint32_t)u * kThreads * 16u);
+    return;
+  }
+  const uint32_t m = ALIGNED ? 0u : uniform((uint32_t)(uintptr_t)sp & 3u);
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const uint32_t o = lane + (uint32_t)u * kThreads * 16u;
-    if (o < rem) v[u] = ALIGNED ? ld16<CP>(sp + o) : ld16_any(sp + o, m);
+    if (o < t.rem) v[u] = ALIGNED ? ld16<CP>(sp + o) : ld16_any(sp + o, m);
   }
-  store_units<U, CP, 0>(d, J.dst_rank, J.dst_off + toff, lane, rem, v);
 }
 
 // ---------------------------------------------------------------- kernel
 
 // N > 0: N-to-1 reduce of element type T.  N == 0: byte copy.
+//
+// The reduce loop is software-pipelined: once a tile's sources are summed
+// into r, the loads of the workgroup's next tile are issued before r is
+// stored, so loads stay in flight while the stores drain.
 template <int N, typename T, int CP, bool ALIGNED>
 __global__ __launch_bounds__(kThreads) void coll_kernel(const CollDesc d) {
   constexpr int U = N > 0 ? reduce_unroll<N>() : kCopyUnroll;
@@ -214,22 +265,44 @@ __global__ __launch_bounds__(kThreads) void coll_kernel(const CollDesc d) {
   __shared__ uint32_t scan[kThreads];
   int nj;
   const uint32_t total = build_table<ALIGNED>(d, tile_of<U>(), jobs, scan, nj);
-  int j = 0;
-  for (uint32_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
-    while (j + 1 < nj && jobs[j + 1].tile0 <= tile) ++j;
-    JobL J;
-    J.src_off = uniform64(jobs[j].src_off);
-    J.dst_off = uniform64(jobs[j].dst_off);
-    J.bytes = uniform64(jobs[j].bytes);
-    J.src_rank = (int32_t)uniform((uint32_t)jobs[j].src_rank);
-    J.dst_rank = (int32_t)uniform((uint32_t)jobs[j].dst_rank);
-    J.head = uniform(jobs[j].head);
-    J.tile0 = uniform(jobs[j].tile0);
-    const uint32_t lt = tile - J.tile0;
-    if constexpr (N > 0)
-      reduce_tile<T, N, U, CP, ALIGNED>(d, J, lt);
-    else
-      copy_tile<U, CP, ALIGNED>(d, J, lt);
+  uint32_t tile = blockIdx.x;
+  if (tile >= total) return;
+  const uint32_t lane = threadIdx.x * 16u;
+  JobCursor<U, ALIGNED> jc;
+  jc.init(jobs, nj, tile);
+  if constexpr (N > 0) {
+    TileRef cur = jc.at(tile);
+    u32x4 v[U][N];
+    reduce_load<N, U, CP, ALIGNED>(d, cur, v);
+    for (;;) {
+      const uint32_t next = tile + gridDim.x;
+      u32x4 r[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) r[u] = reduce_unit<T, N>(v[u]);
+      TileRef nxt;
+      const bool more = next < total;
+      if (more) {
+        nxt = jc.at(next);
+        reduce_load<N, U, CP, ALIGNED>(d, nxt, v);
+      }
+      if constexpr (!ALIGNED) {
+        if (cur.lt == 0) reduce_edges<T, N>(d, cur.J, cur.head, cur.body);
+      }
+      store_units<U, CP, N>(d, cur.J.dst_rank, cur.J.dst_off + cur.toff, lane, cur.rem, r);
+      if (!more) break;
+      cur = nxt;
+      tile = next;
+    }
+  } else {
+    for (; tile < total; tile += gridDim.x) {
+      const TileRef cur = jc.at(tile);
+      u32x4 v[U];
+      copy_load<U, CP, ALIGNED>(d, cur, v);
+      if constexpr (!ALIGNED) {
+        if (cur.lt == 0) copy_edges(d, cur.J, cur.head, cur.body);
+      }
+      store_units<U, CP, 0>(d, cur.J.dst_rank, cur.J.dst_off + cur.toff, lane, cur.rem, v);
+    }
   }
 }
 
@@ -267,22 +340,22 @@ KernelFn reduce_kernel(int n) {
 
 template <typename T>
 KernelFn reduce_kernel_cp(int n, int cp, bool aligned) {
-  if (!aligned) return reduce_kernel<T, kCacheDefault, false>(n);
+  if (!aligned) return reduce_kernel<T, kCached, false>(n);
   switch (cp) {
     case kCacheStream: return reduce_kernel<T, kCacheStream, true>(n);
     case kCacheStreamStores: return reduce_kernel<T, kCacheStreamStores, true>(n);
     case kCacheStreamLoads: return reduce_kernel<T, kCacheStreamLoads, true>(n);
-    default: return reduce_kernel<T, kCacheDefault, true>(n);
+    default: return reduce_kernel<T, kCached, true>(n);
   }
 }
 
 static KernelFn copy_kernel(int cp, bool aligned) {
-  if (!aligned) return kernel_ptr<0, F32, kCacheDefault, false>();
+  if (!aligned) return kernel_ptr<0, F32, kCached, false>();
   switch (cp) {
     case kCacheStream: return kernel_ptr<0, F32, kCacheStream, true>();
     case kCacheStreamStores: return kernel_ptr<0, F32, kCacheStreamStores, true>();
     case kCacheStreamLoads: return kernel_ptr<0, F32, kCacheStreamLoads, true>();
-    default: return kernel_ptr<0, F32, kCacheDefault, true>();
+    default: return kernel_ptr<0, F32, kCached, true>();
   }
 }
 
@@ -324,18 +397,22 @@ hipError_t launch_collective(const CollDesc& d, bool aligned, uint64_t tiles, co
                              hipStream_t stream) {
   if (tiles == 0) return hipSuccess;
   KernelFn fn = nullptr;
+  // tuning value 0 = library default (streaming loads and stores), 4 = cached
+  const int cp = cfg.cache_policy == 0 ? kCacheStream : (cfg.cache_policy == 4 ? kCached : cfg.cache_policy);
   if (coll_is_reduce(d.coll)) {
-    fn = d.esize == 4 ? reduce_kernel_cp<F32>(d.nsrc, cfg.cache_policy, aligned)
-                      : reduce_kernel_cp<BF16>(d.nsrc, cfg.cache_policy, aligned);
+    fn = d.esize == 4 ? reduce_kernel_cp<F32>(d.nsrc, cp, aligned) : reduce_kernel_cp<BF16>(d.nsrc, cp, aligned);
   } else {
-    fn = copy_kernel(cfg.cache_policy, aligned);
+    fn = copy_kernel(cp, aligned);
   }
   if (!fn) return hipErrorInvalidValue;
   int per_cu = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), kThreads, 0);
   if (e != hipSuccess) return e;
   if (per_cu < 1) per_cu = 1;
-  if (cfg.wgs_per_cu > 0 && cfg.wgs_per_cu < per_cu) per_cu = cfg.wgs_per_cu;
+  // Measured on MI355X: the 1:1 read/write streams run fastest with few
+  // workgroups per CU (more concurrent write streams lower HBM efficiency).
+  const int want = cfg.wgs_per_cu > 0 ? cfg.wgs_per_cu : (coll_is_reduce(d.coll) && d.nsrc >= 4 ? 1 : 2);
+  if (want < per_cu) per_cu = want;
   const int cus = device_cu_count();
   uint64_t grid = (uint64_t)(cus > 0 ? cus : 1) * (uint64_t)per_cu;
   if (grid > tiles) grid = tiles;

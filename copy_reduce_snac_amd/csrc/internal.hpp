@@ -24,6 +24,8 @@ hipError_t launch_collective(const CollDesc& d, bool aligned, uint64_t tiles, co
                              hipStream_t stream);
 
 // Device-side SNAC pipeline (y = 0.5 x + r staged, then N-to-1 reduce).
+constexpr int kMaxQueues = 8;
+
 struct PipeArgs {
   const void* x[kMaxRanks];
   void* out;
@@ -31,11 +33,11 @@ struct PipeArgs {
   int32_t nranks;
   int32_t esize;
   char* staging;       // [nranks][slots][tile_bytes]
-  uint64_t* ready;     // [nranks][slots], 16 words (128 B) apart
-  uint64_t* freed;     // [slots], 16 words apart
-  uint64_t* ctrl;      // control words, 16 apart: ticket, done, epoch, status
+  uint64_t* ready;     // [nranks][slots], kFlagStride words apart
+  uint64_t* freed;     // [slots][nranks] (one flag per consumer part)
+  uint64_t* ctrl;      // control words, kFlagStride apart (kCtrl*)
   const uint32_t* abort_word;  // host-mapped
-  uint32_t slots;
+  uint32_t slots;      // total slots = queues * slots_per_queue (+ unused)
   uint32_t tile_bytes;
   uint32_t lookahead;
   uint32_t grid;
@@ -45,12 +47,21 @@ struct PipeArgs {
   // kernel is a scalar (kernel-argument) value: a condition the compiler
   // cannot prove uniform lets it restructure a loop that holds barriers.
   uint32_t tiles;       // ceil(count / tile elements)
-  uint32_t items;       // (tiles + lookahead) * (nranks + 1)
-  uint32_t rounds;      // ceil(tiles / slots)
+  uint32_t queues;      // independent ticket queues (tile t -> queue t % queues)
+  uint32_t qslots;      // slots per queue
+  uint32_t rounds;      // max over queues of ceil(tiles_q / qslots)
   uint32_t tile_elems;  // tile_bytes / esize
+  uint32_t part_elems;  // elements per consumer part (multiple of 16 / esize)
 };
 
-enum : uint32_t { kCtrlTicket = 0, kCtrlDone = 16, kCtrlEpoch = 32, kCtrlStatus = 48, kCtrlWords = 64 };
+// control words (uint64 indices into ctrl)
+enum : uint32_t {
+  kCtrlTicket = 0,  // kMaxQueues tickets, kFlagStride apart
+  kCtrlDone = kMaxQueues * 16,
+  kCtrlEpoch = kCtrlDone + 16,
+  kCtrlStatus = kCtrlEpoch + 16,
+  kCtrlWords = kCtrlStatus + 16
+};
 constexpr uint32_t kFlagStride = 16;  // uint64 words between flags (128 B)
 
 hipError_t launch_pipeline(const PipeArgs& a, int dtype_bf16, const LaunchCfg& cfg, hipStream_t stream,

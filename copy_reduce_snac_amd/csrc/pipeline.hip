@@ -3,35 +3,47 @@
 // "Samples" calls a collective from inside a kernel between other work).
 //
 // Work items.  The message (count elements per rank) is cut into tiles of
-// tile_bytes per rank.  Tile t of rank r has a producer item P(t, r) and
-// tile t has one consumer item C(t).  Items are handed out in a fixed order
-// by an atomic ticket counter: group g holds P(g, 0..N-1) followed by
-// C(g - L), so a consumer trails its producers by L tiles (the lookahead).
+// tile_bytes per rank.  Tile t of rank r has a producer item P(t, r); the
+// reduction of tile t is split into N consumer parts C(t, p), each reducing
+// 1/N of the tile's elements across all N ranks, so every item moves about
+// the same number of bytes.  Tiles are dealt round-robin to Q independent
+// queues (tile t -> queue t % Q), each with its own ring of staging slots
+// and its own ticket counter; workgroup b draws tickets from queue b % Q.
+// Within a queue, local tile g has group g of the ticket order holding
+// P(g, 0..N-1) followed by C(g - L, 0..N-1), so consumers trail their
+// producers by L tiles (the lookahead).
 //
-//   P(t, r)  Stage:   wait until slot t mod S of rank r is free, compute
+//   P(t, r)  Stage:   wait until the tile's slot is free (all N consumer
+//                     parts of the slot's previous tile are done), compute
 //                     y = 0.5 * x_r + r in binary32, round to the data type,
 //                     store into staging[r][slot].
-//            Notify:  every wave fences (release, agent scope), the
-//                     workgroup meets at a barrier, one lane stores
-//                     ready[r][slot] = seq with release semantics.
-//   C(t)     Consume: one lane polls ready[r][slot] >= seq for every r
-//                     (relaxed loads, s_sleep back-off, then an acquire
-//                     fence); the workgroup meets at a barrier and every
-//                     wave fences (acquire, agent scope); N-to-1 reduce of
-//                     the staged tiles into out; barrier; one lane releases
-//                     free[slot] = seq.
+//            Notify:  every wave waits until its stores are accepted by
+//                     the L2, the workgroup meets at a barrier, and one lane
+//                     issues the agent-scope release fence (L2 write-back),
+//                     waits for it, and stores ready[r][slot] = seq.
+//   C(t, p)  Consume: one lane polls ready[r][slot] >= seq for every r
+//                     (relaxed loads with s_sleep back-off) and issues one
+//                     agent-scope acquire fence; barrier; N-to-1 reduce of
+//                     part p of the staged tile into out; barrier; one lane
+//                     stores freed[slot][p] = seq.
 //
-// Forward progress: a workgroup only ever waits for items with smaller
-// tickets (P(t) waits for C(t - S), ticketed in group t - S + L < t because
-// L <= S - 1; C(t) waits for P(t, *), ticketed in group t).  Tickets are
-// taken only by running workgroups, so the smallest unfinished ticket can
-// always advance -- no co-residency assumption about the grid is needed.
+// One fence per item, not one per wave: agent-scope fences write back or
+// invalidate a whole L2 and serialise across the GPU (measured on MI355X at
+// about 28 ns per workgroup-fence with every CU fencing), so they set the
+// cost of small tiles.
+//
+// Forward progress: within a queue a workgroup only ever waits for items
+// with smaller tickets of the same queue (P(g) waits for C(g - S), ticketed
+// in group g - S + L < g because L <= S - 1; C(g) waits for P(g, *),
+// ticketed in group g).  Tickets are taken only by running workgroups, so
+// the smallest unfinished ticket of each queue can always advance; no
+// co-residency assumption about the grid is needed.
 //
 // Sequence numbers are monotonic across calls: seq = epoch + round + 1 with
-// round = t / S.  The last workgroup to finish (an acq_rel counter) adds the
-// number of rounds to the epoch and clears the ticket and done counters, all
-// in device memory, so consecutive launches (also inside a replayed graph)
-// need no host bookkeeping and no reset pass.
+// round = g / S.  The last workgroup to finish (an acq_rel counter) adds the
+// largest round count to the epoch and clears the ticket and done counters,
+// all in device memory, so consecutive launches (also inside a replayed
+// graph) need no host bookkeeping and no reset pass.
 //
 // Waits are bounded: after 2^spin_limit_log2 polls a wait latches
 // SNAC_E_TIMEOUT in the status word and gives up; a host-mapped abort word
@@ -56,8 +68,14 @@ __device__ __forceinline__ void latch_status(uint64_t* ctrl, uint64_t code) {
                                        __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// One lane waits until *flag >= target.  Returns false (and the status word
-// is set) on timeout, abort, or an error latched elsewhere.
+// Wait until every vector memory operation this wave has issued is done
+// (s_waitcnt vmcnt(0); the gfx9 encoding leaves expcnt and lgkmcnt free).
+// A store is done once the L2 has accepted it.
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// One lane waits until *flag >= target with relaxed agent-scope loads.
+// Returns false (and the status word is set) on timeout, abort, or an error
+// latched elsewhere.  The caller adds the acquire fence where it needs one.
 __device__ bool wait_geq(uint64_t* flag, uint64_t target, const PipeArgs& a) {
   const uint64_t limit = 1ull << a.spin_limit_log2;
   uint64_t spins = 0;
@@ -76,7 +94,6 @@ __device__ bool wait_geq(uint64_t* flag, uint64_t target, const PipeArgs& a) {
     }
     __builtin_amdgcn_s_sleep(1);
   }
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   return true;
 }
 
@@ -99,24 +116,32 @@ __device__ __forceinline__ u32x4 scale_unit(u32x4 x, float r) {
 // compiler cannot prove a loop exit uniform it may restructure the loop so
 // that lanes of one wave reach a barrier on different iterations.
 
-template <typename T>
-__device__ void produce(const PipeArgs& a, uint32_t t, uint32_t r, uint64_t epoch, uint32_t* s_ok) {
+// Elements of tile t (the last tile may be short).
+__device__ __forceinline__ uint32_t tile_count(const PipeArgs& a, uint32_t t) {
+  const uint64_t e0 = (uint64_t)t * a.tile_elems;
+  return uniform(t + 1 < a.tiles ? a.tile_elems : (uint32_t)(a.count - e0));
+}
+
+template <typename T, int N>
+__device__ void produce(const PipeArgs& a, uint32_t t, uint32_t gslot, uint32_t round, uint32_t r, uint64_t epoch,
+                        uint32_t* s_ok) {
   constexpr uint32_t E = T::kSize;
-  const uint32_t S = a.slots;
-  const uint32_t slot = uniform(t % S);
-  const uint32_t round = uniform(t / S);
   if (round > 0) {
-    if (threadIdx.x == 0) *s_ok = wait_geq(&a.freed[(uint64_t)slot * kFlagStride], epoch + round, a) ? 1u : 0u;
+    if (threadIdx.x == 0) {
+      bool ok = true;
+      for (int p = 0; p < N && ok; ++p)
+        ok = wait_geq(&a.freed[((uint64_t)gslot * N + p) * kFlagStride], epoch + round, a);
+      *s_ok = ok ? 1u : 0u;
+    }
     __syncthreads();
     const uint32_t ok = uniform(*s_ok);
     __syncthreads();
     if (ok == 0) return;
   }
   const uint64_t e0 = (uint64_t)t * a.tile_elems;
-  const uint32_t ne = uniform(t + 1 < a.tiles ? a.tile_elems : (uint32_t)(a.count - e0));
-  const uint32_t nbytes = ne * E;
+  const uint32_t nbytes = tile_count(a, t) * E;
   const char* src = static_cast<const char*>(a.x[r]) + e0 * E;
-  char* stg = a.staging + ((uint64_t)r * S + slot) * a.tile_bytes;
+  char* stg = a.staging + ((uint64_t)r * a.slots + gslot) * a.tile_bytes;
   const float rf = (float)r;
   const uint32_t nvec = nbytes & ~15u;
   constexpr int U = 4;
@@ -130,7 +155,7 @@ __device__ void produce(const PipeArgs& a, uint32_t t, uint32_t r, uint64_t epoc
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t o = base + (threadIdx.x + (uint32_t)u * kThreads) * 16u;
-      if (o < nvec) st16<kCacheDefault>(stg + o, scale_unit<T>(v[u], rf));
+      if (o < nvec) st16<kCached>(stg + o, scale_unit<T>(v[u], rf));
     }
   }
   const uint32_t tail = (nbytes - nvec) / E;
@@ -138,37 +163,49 @@ __device__ void produce(const PipeArgs& a, uint32_t t, uint32_t r, uint64_t epoc
     const uint32_t o = nvec + threadIdx.x * E;
     store_elem<T>(stg + o, load_elem<T>(src + o) * 0.5f + rf);
   }
-  // Notify: every wave's staging stores are written back at agent scope
-  // before any lane can observe the flag
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  // Notify.  Every wave waits until the L2 has accepted its staging stores;
+  // after the barrier one lane writes the L2 back at agent scope (a single
+  // release fence per tile: these fences serialise across the GPU, so one per
+  // wave would cost four times as much), waits for the write-back, and only
+  // then stores the flag.
+  wait_vm();
   __syncthreads();
-  if (threadIdx.x == 0 && a.drop_notify != (int32_t)r + 1)
-    __hip_atomic_store(&a.ready[((uint64_t)r * S + slot) * kFlagStride], epoch + round + 1, __ATOMIC_RELEASE,
+  if (threadIdx.x == 0 && a.drop_notify != (int32_t)r + 1) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    wait_vm();
+    __hip_atomic_store(&a.ready[((uint64_t)r * a.slots + gslot) * kFlagStride], epoch + round + 1, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 template <typename T, int N>
-__device__ void consume(const PipeArgs& a, uint32_t t, uint64_t epoch, uint32_t* s_ok) {
+__device__ void consume(const PipeArgs& a, uint32_t t, uint32_t gslot, uint32_t round, uint32_t part, uint64_t epoch,
+                        uint32_t* s_ok) {
   constexpr uint32_t E = T::kSize;
-  const uint32_t S = a.slots;
-  const uint32_t slot = uniform(t % S);
-  const uint64_t seq = epoch + uniform(t / S) + 1;
+  const uint64_t seq = epoch + round + 1;
+  // Consume: one lane sees every rank's flag, then one acquire fence (an L2
+  // and L1 invalidate shared by the whole workgroup's CU) before the barrier
+  // releases the other waves to read the staged data.
   if (threadIdx.x == 0) {
     bool ok = true;
-    for (int r = 0; r < N && ok; ++r) ok = wait_geq(&a.ready[((uint64_t)r * S + slot) * kFlagStride], seq, a);
+    for (int r = 0; r < N && ok; ++r) ok = wait_geq(&a.ready[((uint64_t)r * a.slots + gslot) * kFlagStride], seq, a);
+    if (ok) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      wait_vm();
+    }
     *s_ok = ok ? 1u : 0u;
   }
   __syncthreads();
   const uint32_t ok = uniform(*s_ok);
   __syncthreads();
   if (ok == 0) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  const uint64_t e0 = (uint64_t)t * a.tile_elems;
-  const uint32_t ne = uniform(t + 1 < a.tiles ? a.tile_elems : (uint32_t)(a.count - e0));
-  const uint32_t nbytes = ne * E;
-  const uint64_t rank_stride = (uint64_t)S * a.tile_bytes;
-  const char* stg = a.staging + (uint64_t)slot * a.tile_bytes;
-  char* out = static_cast<char*>(a.out) + e0 * E;
+  const uint32_t ne = tile_count(a, t);
+  const uint32_t p0 = part * a.part_elems;
+  const uint32_t pn = p0 >= ne ? 0u : (ne - p0 < a.part_elems ? ne - p0 : a.part_elems);
+  const uint32_t nbytes = pn * E;
+  const uint64_t rank_stride = (uint64_t)a.slots * a.tile_bytes;
+  const char* stg = a.staging + (uint64_t)gslot * a.tile_bytes + (uint64_t)p0 * E;
+  char* out = static_cast<char*>(a.out) + ((uint64_t)t * a.tile_elems + p0) * E;
   const uint32_t nvec = nbytes & ~15u;
   constexpr int U = N <= 4 ? 2 : 1;
   for (uint32_t base = 0; base < nvec; base += kThreads * 16u * U) {
@@ -178,13 +215,13 @@ __device__ void consume(const PipeArgs& a, uint32_t t, uint64_t epoch, uint32_t*
       const uint32_t o = base + (threadIdx.x + (uint32_t)u * kThreads) * 16u;
       if (o < nvec) {
 #pragma unroll
-        for (int k = 0; k < N; ++k) v[u][k] = ld16<kCacheDefault>(stg + k * rank_stride + o);
+        for (int k = 0; k < N; ++k) v[u][k] = ld16<kCached>(stg + k * rank_stride + o);
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t o = base + (threadIdx.x + (uint32_t)u * kThreads) * 16u;
-      if (o < nvec) st16<kCacheDefault>(out + o, reduce_unit<T, N>(v[u]));
+      if (o < nvec) st16<kCacheStreamStores>(out + o, reduce_unit<T, N>(v[u]));
     }
   }
   const uint32_t tail = (nbytes - nvec) / E;
@@ -195,11 +232,16 @@ __device__ void consume(const PipeArgs& a, uint32_t t, uint64_t epoch, uint32_t*
     for (int k = 1; k < N; ++k) acc = acc + load_elem<T>(stg + k * rank_stride + o);
     store_elem<T>(out + o, acc);
   }
-  // every wave has its staged values in registers (they were used above);
-  // the slot may be overwritten once the flag is seen
+  // Free the slot.  This edge only has to order this workgroup's staging
+  // loads before the producer's next stores to the slot: every load has
+  // returned its data (the values were used above) before the barrier, and
+  // the producer issues its stores only after it has seen the flag, so a
+  // relaxed store and a relaxed wait suffice and no cache maintenance is
+  // spent on it.
   __syncthreads();
   if (threadIdx.x == 0)
-    __hip_atomic_store(&a.freed[(uint64_t)slot * kFlagStride], seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&a.freed[((uint64_t)gslot * N + part) * kFlagStride], seq, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <typename T, int N>
@@ -207,9 +249,14 @@ __global__ __launch_bounds__(kThreads) void pipeline_kernel(const PipeArgs a) {
   __shared__ uint32_t s_item;
   __shared__ uint32_t s_ok;
   const uint64_t epoch = uniform64(ld_relaxed(&a.ctrl[kCtrlEpoch]));
-  const uint32_t items = a.items;
-  const uint32_t L = a.lookahead;
-  const uint32_t tiles = a.tiles;
+  const uint32_t Q = a.queues;
+  const uint32_t S = a.qslots;
+  const uint32_t q = uniform(blockIdx.x % Q);
+  // local tiles of this queue: t = g * Q + q
+  const uint32_t qtiles = uniform(a.tiles > q ? (a.tiles - q + Q - 1) / Q : 0u);
+  const uint32_t L = uniform(a.lookahead < qtiles ? a.lookahead : qtiles);
+  const uint32_t items = uniform((qtiles + L) * (uint32_t)(2 * N));
+  uint64_t* ticket = &a.ctrl[kCtrlTicket + q * kFlagStride];
   for (;;) {
     // The barrier at the top closes the previous item's single-lane flag
     // store before the next single-lane ticket fetch; without it the
@@ -219,24 +266,26 @@ __global__ __launch_bounds__(kThreads) void pipeline_kernel(const PipeArgs a) {
     // overwritten before every wave has read it.
     __syncthreads();
     if (threadIdx.x == 0)
-      s_item = (uint32_t)__hip_atomic_fetch_add(&a.ctrl[kCtrlTicket], (uint64_t)1, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
+      s_item = (uint32_t)__hip_atomic_fetch_add(ticket, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     const uint32_t item = uniform(s_item);
     if (item >= items) break;
-    const uint32_t g = item / (uint32_t)(N + 1);
-    const uint32_t w = item - g * (uint32_t)(N + 1);
+    const uint32_t g = uniform(item / (uint32_t)(2 * N));
+    const uint32_t w = uniform(item - g * (uint32_t)(2 * N));
     if (w < (uint32_t)N) {
-      if (g < tiles) produce<T>(a, g, w, epoch, &s_ok);
+      if (g < qtiles) produce<T, N>(a, g * Q + q, uniform(q * S + g % S), uniform(g / S), w, epoch, &s_ok);
     } else if (g >= L) {
-      consume<T, N>(a, g - L, epoch, &s_ok);
+      const uint32_t gc = g - L;
+      consume<T, N>(a, gc * Q + q, uniform(q * S + gc % S), uniform(gc / S), w - (uint32_t)N, epoch, &s_ok);
     }
   }
   if (threadIdx.x == 0) {
     const uint64_t old =
         __hip_atomic_fetch_add(&a.ctrl[kCtrlDone], (uint64_t)1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     if (old == (uint64_t)gridDim.x - 1) {
-      __hip_atomic_store(&a.ctrl[kCtrlTicket], (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (uint32_t i = 0; i < Q; ++i)
+        __hip_atomic_store(&a.ctrl[kCtrlTicket + i * kFlagStride], (uint64_t)0, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&a.ctrl[kCtrlDone], (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(&a.ctrl[kCtrlEpoch], epoch + a.rounds, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -282,23 +331,37 @@ hipError_t launch_pipeline(const PipeArgs& in, int dtype_bf16, const LaunchCfg& 
   hipError_t err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), kThreads, 0);
   if (err != hipSuccess) return err;
   if (per_cu < 1) per_cu = 1;
-  if (cfg.wgs_per_cu > 0 && cfg.wgs_per_cu < per_cu) per_cu = cfg.wgs_per_cu;
+  const int want = cfg.wgs_per_cu > 0 ? cfg.wgs_per_cu : 2;
+  if (want < per_cu) per_cu = want;
   const int cus = device_cu_count();
   uint64_t grid = (uint64_t)(cus > 0 ? cus : 1) * (uint64_t)per_cu;
-  // lookahead: enough tiles staged ahead that a consumer's producers have
-  // usually finished when it is ticketed; at most S - 1 (forward progress)
-  uint64_t L = a.lookahead ? a.lookahead : (grid + a.nranks) / (uint64_t)(a.nranks + 1);
-  if (L > a.slots - 1) L = a.slots - 1;
-  if (L > tiles) L = tiles;
+  // queues: as many as there are tiles, workgroups and 2-slot rings allow
+  uint64_t Q = kMaxQueues;
+  if (Q > tiles) Q = tiles;
+  if (Q > a.slots / 2) Q = a.slots / 2;
+  if (Q < 1) return hipErrorInvalidValue;
+  const uint64_t S = a.slots / Q;
+  const uint64_t qtiles = (tiles + Q - 1) / Q;
+  // lookahead: tiles staged ahead of the consumers, at most S - 1 (forward
+  // progress); the whole ring by default
+  uint64_t L = a.lookahead ? a.lookahead : S - 1;
+  if (L > S - 1) L = S - 1;
+  // enough workgroups to keep every queue's lookahead window busy, and a
+  // multiple of Q so that the queues get equal shares
+  const uint64_t items_per_q = (qtiles + L) * (uint64_t)(2 * a.nranks);
+  if (grid > items_per_q * Q) grid = items_per_q * Q;
+  grid = (grid + Q - 1) / Q * Q;
+  a.queues = (uint32_t)Q;
+  a.qslots = (uint32_t)S;
   a.lookahead = (uint32_t)L;
-  const uint64_t items = (tiles + L) * (uint64_t)(a.nranks + 1);
-  if (items > 0xffffffffull - 0x100000ull) return hipErrorInvalidValue;
-  if (grid > items) grid = items;
   a.grid = (uint32_t)grid;
   a.tiles = (uint32_t)tiles;
-  a.items = (uint32_t)items;
-  a.rounds = (uint32_t)((tiles + a.slots - 1) / a.slots);
+  a.rounds = (uint32_t)((qtiles + S - 1) / S);
   a.tile_elems = (uint32_t)te;
+  const uint64_t vec = 16 / e;  // elements per 16-byte unit
+  uint64_t pe = (te + (uint64_t)a.nranks - 1) / (uint64_t)a.nranks;
+  pe = (pe + vec - 1) / vec * vec;
+  a.part_elems = (uint32_t)pe;
   if (grid_out) *grid_out = (uint32_t)grid;
   hipLaunchKernelGGL(fn, dim3((uint32_t)grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();

@@ -96,9 +96,12 @@ const char* snac_last_error(void);
  *   nranks                  1 .. SNAC_MAX_RANKS
  *   staging_bytes_per_rank  size of each rank's staging ring, used by the
  *                           device-side SNAC pipeline.  0 selects the
- *                           default (8 MiB).  It is split into slots of the
- *                           pipeline tile size (64 KiB by default); at least
- *                           2 slots are required.
+ *                           default (32 MiB).  It is split into slots of the
+ *                           pipeline tile size: the tuning value if set,
+ *                           else the largest power of two up to 512 KiB
+ *                           that leaves at least 64 slots (minimum 4 KiB).
+ *                           The size must be a multiple of the tile and
+ *                           give at least 2 slots.
  *   stream                  signals are cleared on this stream.
  *   out                     receives the context; on error *out is NULL.
  *
@@ -297,10 +300,15 @@ snac_status snac_plan(snac_coll coll, int nranks, snac_dtype dtype, size_t bytes
  * for peak performance).  Zero fields select the defaults.
  */
 typedef struct snac_tuning {
-  int32_t wgs_per_cu;      /* workgroups per compute unit in the persistent grid */
-  int32_t cache_policy;    /* 0 default, 1 streaming loads+stores, 2 streaming stores, 3 streaming loads */
-  int32_t pipeline_tile_bytes; /* per-rank bytes per pipeline tile (multiple of 4096) */
-  int32_t pipeline_lookahead;  /* tiles staged ahead of the consumers */
+  int32_t wgs_per_cu;      /* workgroups per compute unit in the persistent grid
+                              (0: 1 for reduces of >= 4 sources, else 2) */
+  int32_t cache_policy;    /* 0 library default (= 1), 1 streaming (non-temporal)
+                              loads and stores, 2 streaming stores only,
+                              3 streaming loads only, 4 cached loads and stores */
+  int32_t pipeline_tile_bytes; /* per-rank bytes per pipeline tile (multiple of
+                                  4096), fixed when a context is created */
+  int32_t pipeline_lookahead;  /* tiles staged ahead of the consumers (0: as
+                                  many as the ring allows) */
   int32_t spin_limit_log2;     /* device waits give up after 2^k polls */
   int32_t debug_drop_notify;   /* test hook: when r+1, rank r's producers never
                                   raise their ready flags, so consumers time out */

@@ -261,7 +261,7 @@ def test_v_equal_counts_match_fixed(ctxs):
 
 # -------------------------------------------------------- SNAC pipeline
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("n", [1, 2, 8])
+@pytest.mark.parametrize("n", [1, 2, 3, 8])
 def test_pipeline(n, dtype):
     ctx = snac.snac_init(n, 4 * 65536)  # 4 slots: the ring wraps many times
     try:
@@ -272,6 +272,45 @@ def test_pipeline(n, dtype):
             snac.snac_pipeline_scale_reduce(ctx, [b.ptr for b in xb], ob.ptr, count, dtype)
             snac.snac_check(ctx)
             run_and_check([ob], [oracle.pipeline_scale_reduce(xs, dtype)], dtype, f"pipeline N={n} count={count}")
+    finally:
+        snac.snac_finalize(ctx)
+
+
+@pytest.mark.parametrize("tile,lookahead,wgs", [(4096, 1, 1), (16384, 3, 2), (65536, 0, 4), (262144, 7, 1)])
+def test_pipeline_tunings(tile, lookahead, wgs):
+    n, dtype = 5, "bf16"
+    t0 = snac.snac_get_tuning()
+    try:
+        snac.snac_set_tuning(pipeline_tile_bytes=tile, pipeline_lookahead=lookahead, wgs_per_cu=wgs)
+        ctx = snac.snac_init(n, 16 * tile)
+        try:
+            for count in [tile // 2 * 3 + 7, 40 * tile // 2 + 1]:
+                xs = gen(n, count, dtype, seed=count + tile)
+                xb = [DevBuf(x.nbytes, data=x) for x in xs]
+                ob = DevBuf(xs[0].nbytes)
+                snac.snac_pipeline_scale_reduce(ctx, [b.ptr for b in xb], ob.ptr, count, dtype)
+                snac.snac_check(ctx)
+                run_and_check([ob], [oracle.pipeline_scale_reduce(xs, dtype)], dtype, f"pipeline tile={tile} count={count}")
+        finally:
+            snac.snac_finalize(ctx)
+    finally:
+        snac.snac_set_tuning(**t0)
+
+
+def test_pipeline_alternating_inputs():
+    """Consecutive calls with different inputs: a consumer that read stale
+    staged data from an earlier call would produce the other output."""
+    n, count, dtype = 8, 150_001, "bf16"
+    ctx = snac.snac_init(n, 16 * 32768)
+    try:
+        sets = [gen(n, count, dtype, seed=s) for s in (41, 42)]
+        want = [oracle.pipeline_scale_reduce(xs, dtype) for xs in sets]
+        bufs = [[DevBuf(x.nbytes, data=x) for x in xs] for xs in sets]
+        outs = [DevBuf(sets[0][0].nbytes) for _ in range(12)]
+        for i, ob in enumerate(outs):
+            snac.snac_pipeline_scale_reduce(ctx, [b.ptr for b in bufs[i % 2]], ob.ptr, count, dtype)
+        snac.snac_check(ctx)
+        run_and_check(outs, [want[i % 2] for i in range(len(outs))], dtype, "pipeline alternating inputs")
     finally:
         snac.snac_finalize(ctx)
 
