@@ -50,10 +50,14 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# sources of the collective kernel (the dominant kernel of the benchmark)
+KERNEL_SOURCES = ("atoms.hpp", "collectives.hip", "internal.hpp", "layout.hpp")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "copy_reduce_snac_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in KERNEL_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
