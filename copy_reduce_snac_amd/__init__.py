@@ -55,7 +55,8 @@ class snac_tuning(ctypes.Structure):
         ("pipeline_lookahead", ctypes.c_int32),
         ("spin_limit_log2", ctypes.c_int32),
         ("debug_drop_notify", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 2),
+        ("copy_multicast", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 1),
     ]
 
 

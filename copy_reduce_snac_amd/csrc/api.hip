@@ -55,7 +55,7 @@ snac_status hip_fail(hipError_t e, const char* what) {
   return fail(SNAC_E_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-snac_tuning g_tuning = {0, 0, 0, 0, 0, 0, {0, 0}};
+snac_tuning g_tuning = {0, 0, 0, 0, 0, 0, 0, {0}};
 
 constexpr uint32_t kMaxPipeTile = 512u * 1024u;
 constexpr uint32_t kMinPipeTile = 4096u;
@@ -116,6 +116,9 @@ void finish_plan(Plan& p) {
   p.tiles = tiles;
 }
 
+// Copy multicasts split into one job per destination when asked to.
+int split_copy(void* const* dst, int ndst);
+
 // Multicast jobs need one destination residue modulo 16.
 int needs_split(void* const* dst, int ndst) {
   for (int i = 1; i < ndst; ++i)
@@ -124,6 +127,11 @@ int needs_split(void* const* dst, int ndst) {
 }
 
 // A buffer may be NULL only when its extent (in_bytes/out_bytes) is zero.
+int split_copy(void* const* dst, int ndst) {
+  if (g_tuning.copy_multicast == 2) return 1;
+  return needs_split(dst, ndst);
+}
+
 snac_status check_ptrs(const void* const* src, const uint64_t* in_bytes, int nsrc, void* const* dst,
                        const uint64_t* out_bytes, int ndst, int esize) {
   if (!src || !dst) return fail(SNAC_E_ARG, "src and dst pointer arrays must not be NULL");
@@ -220,7 +228,8 @@ snac_status fixed_collective(int32_t coll, snac_ctx* ctx, const void* const* src
     p.d.src[i] = src[i];
     p.d.dst[i] = dst[i];
   }
-  if (coll == kAllReduce || coll == kAllGather) p.d.split_multicast = needs_split(dst, n);
+  if (coll == kAllReduce) p.d.split_multicast = needs_split(dst, n);
+  if (coll == kAllGather) p.d.split_multicast = split_copy(dst, n);
   return run(p, (hipStream_t)stream);
 }
 
@@ -267,7 +276,7 @@ snac_status v_collective(int32_t coll, snac_ctx* ctx, const void* const* src, vo
     p.d.dst[i] = dst[i];
   }
   for (int i = 0; i < nc; ++i) p.d.counts[i] = counts[i];
-  if (coll == kAllGatherV) p.d.split_multicast = needs_split(dst, n);
+  if (coll == kAllGatherV) p.d.split_multicast = split_copy(dst, n);
   return run(p, (hipStream_t)stream);
 }
 
@@ -311,6 +320,7 @@ snac_status snac_set_tuning(const snac_tuning* in) {
   if (in->spin_limit_log2 < 0 || in->spin_limit_log2 > 40) return fail(SNAC_E_ARG, "spin_limit_log2 out of range");
   if (in->debug_drop_notify < 0 || in->debug_drop_notify > SNAC_MAX_RANKS)
     return fail(SNAC_E_ARG, "debug_drop_notify out of range");
+  if (in->copy_multicast < 0 || in->copy_multicast > 2) return fail(SNAC_E_ARG, "copy_multicast out of range [0, 2]");
   g_tuning = *in;
   return ok();
 }

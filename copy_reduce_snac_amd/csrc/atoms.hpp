@@ -48,10 +48,19 @@ __device__ __forceinline__ void st16(char* p, u32x4 v) {
 // dword below p are loaded (every dword touched holds at least one wanted
 // byte, so nothing outside the source range's dwords is read) and shifted
 // into place with v_alignbyte_b32.
+template <int CP>
+__device__ __forceinline__ u32x4 ld16_a4(const char* p) {
+  if constexpr (CP == kCacheStream || CP == kCacheStreamLoads)
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_a4*>(p));
+  else
+    return *reinterpret_cast<const u32x4_a4*>(p);
+}
+
+template <int CP>
 __device__ __forceinline__ u32x4 ld16_any(const char* p, uint32_t m) {
-  if (m == 0) return *reinterpret_cast<const u32x4_a4*>(p);
+  if (m == 0) return ld16_a4<CP>(p);
   const char* b = p - m;
-  const u32x4 a = *reinterpret_cast<const u32x4_a4*>(b);
+  const u32x4 a = ld16_a4<CP>(b);
   const uint32_t e = *reinterpret_cast<const uint32_t*>(b + 16);
   u32x4 r;
   r.x = __builtin_amdgcn_alignbyte(a.y, a.x, m);

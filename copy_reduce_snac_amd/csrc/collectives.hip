@@ -13,9 +13,10 @@
 //  * aligned: every job address is 16-byte aligned and every job length a
 //    multiple of 16 (the normal case for tensor buffers): plain dwordx4.
 //  * generic: any element-aligned address.  Each job is split into a head
-//    (bytes until the destination is 16-byte aligned), a body of aligned
+//    (bytes until the destination reaches a 128-byte line), a body of aligned
 //    16-byte stores whose sources are read with ld16_any, and a tail; head
-//    and tail are moved one element per lane by tile 0 of the job.
+//    and tail are moved one element per lane by tile 0 of the job.  The
+//    generic variant exists with streaming (default) and cached accesses.
 #include <hip/hip_runtime.h>
 
 #include "atoms.hpp"
@@ -198,12 +199,16 @@ __device__ void reduce_edges(const CollDesc& d, const JobL& J, uint32_t head, ui
 template <int N, int U, int CP, bool ALIGNED>
 __device__ __forceinline__ void reduce_load(const CollDesc& d, const TileRef& t, u32x4 (&v)[U][N]) {
   const uint32_t lane = threadIdx.x * 16u;
-  if (ALIGNED && t.rem == tile_of<U>()) {  // full tile: no per-unit guards
+  if (t.rem == tile_of<U>()) {  // full tile: no per-unit guards
 #pragma unroll
     for (int k = 0; k < N; ++k) {
-      const char* sp = static_cast<const char*>(d.src[k]) + t.J.src_off + t.toff + lane;
+      const char* sp = static_cast<const char*>(d.src[k]) + t.J.src_off + t.toff;
+      const uint32_t m = ALIGNED ? 0u : uniform((uint32_t)(uintptr_t)sp & 3u);
 #pragma unroll
-      for (int u = 0; u < U; ++u) v[u][k] = ld16<CP>(sp + (uint32_t)u * kThreads * 16u);
+      for (int u = 0; u < U; ++u) {
+        const char* q = sp + lane + (uint32_t)u * kThreads * 16u;
+        v[u][k] = ALIGNED ? ld16<CP>(q) : ld16_any<CP>(q, m);
+      }
     }
     return;
   }
@@ -214,7 +219,7 @@ __device__ __forceinline__ void reduce_load(const CollDesc& d, const TileRef& t,
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t o = lane + (uint32_t)u * kThreads * 16u;
-      if (o < t.rem) v[u][k] = ALIGNED ? ld16<CP>(sp + o) : ld16_any(sp + o, m);
+      if (o < t.rem) v[u][k] = ALIGNED ? ld16<CP>(sp + o) : ld16_any<CP>(sp + o, m);
     }
   }
 }
@@ -238,16 +243,19 @@ template <int U, int CP, bool ALIGNED>
 __device__ __forceinline__ void copy_load(const CollDesc& d, const TileRef& t, u32x4 (&v)[U]) {
   const char* sp = static_cast<const char*>(d.src[t.J.src_rank]) + t.J.src_off + t.toff;
   const uint32_t lane = threadIdx.x * 16u;
-  if (ALIGNED && t.rem == tile_of<U>()) {
+  const uint32_t m = ALIGNED ? 0u : uniform((uint32_t)(uintptr_t)sp & 3u);
+  if (t.rem == tile_of<U>()) {  // full tile: no per-unit guards
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = ld16<CP>(sp + lane + (uint32_t)u * kThreads * 16u);
+    for (int u = 0; u < U; ++u) {
+      const char* q = sp + lane + (uint32_t)u * kThreads * 16u;
+      v[u] = ALIGNED ? ld16<CP>(q) : ld16_any<CP>(q, m);
+    }
     return;
   }
-  const uint32_t m = ALIGNED ? 0u : uniform((uint32_t)(uintptr_t)sp & 3u);
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const uint32_t o = lane + (uint32_t)u * kThreads * 16u;
-    if (o < t.rem) v[u] = ALIGNED ? ld16<CP>(sp + o) : ld16_any(sp + o, m);
+    if (o < t.rem) v[u] = ALIGNED ? ld16<CP>(sp + o) : ld16_any<CP>(sp + o, m);
   }
 }
 
@@ -340,7 +348,7 @@ KernelFn reduce_kernel(int n) {
 
 template <typename T>
 KernelFn reduce_kernel_cp(int n, int cp, bool aligned) {
-  if (!aligned) return reduce_kernel<T, kCached, false>(n);
+  if (!aligned) return cp == kCached ? reduce_kernel<T, kCached, false>(n) : reduce_kernel<T, kCacheStream, false>(n);
   switch (cp) {
     case kCacheStream: return reduce_kernel<T, kCacheStream, true>(n);
     case kCacheStreamStores: return reduce_kernel<T, kCacheStreamStores, true>(n);
@@ -350,7 +358,7 @@ KernelFn reduce_kernel_cp(int n, int cp, bool aligned) {
 }
 
 static KernelFn copy_kernel(int cp, bool aligned) {
-  if (!aligned) return kernel_ptr<0, F32, kCached, false>();
+  if (!aligned) return cp == kCached ? kernel_ptr<0, F32, kCached, false>() : kernel_ptr<0, F32, kCacheStream, false>();
   switch (cp) {
     case kCacheStream: return kernel_ptr<0, F32, kCacheStream, true>();
     case kCacheStreamStores: return kernel_ptr<0, F32, kCacheStreamStores, true>();

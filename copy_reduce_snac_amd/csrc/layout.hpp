@@ -168,12 +168,17 @@ SNAC_HD Job make_job(const CollDesc& d, int j) {
   return r;
 }
 
-// Bytes of a job before its destination reaches a 16-byte boundary (0 when
-// the job is 16-byte aligned); always a multiple of the element size.
+// Bytes of a job before its destination reaches a 128-byte (cache line)
+// boundary, always a multiple of the element size.  The body that follows
+// is stored in whole 16-byte units starting on a line, so a wave's 1 KiB
+// store covers whole lines instead of straddling nine.  Head (< 128 bytes)
+// plus tail (< 16 bytes) fit in one workgroup's lanes, one element each.
+constexpr uint32_t kHeadAlign = 128;
+
 SNAC_HD uint32_t job_head_bytes(const CollDesc& d, const Job& j) {
   const int dr = j.dst_rank < 0 ? 0 : j.dst_rank;
   const uint64_t a = (uint64_t)(uintptr_t)d.dst[dr] + j.dst_off;
-  uint64_t h = (16u - (uint32_t)(a & 15u)) & 15u;
+  uint64_t h = (kHeadAlign - (uint32_t)(a & (kHeadAlign - 1))) & (kHeadAlign - 1);
   if (h > j.bytes) h = j.bytes;
   return (uint32_t)h;
 }

@@ -312,7 +312,12 @@ typedef struct snac_tuning {
   int32_t spin_limit_log2;     /* device waits give up after 2^k polls */
   int32_t debug_drop_notify;   /* test hook: when r+1, rank r's producers never
                                   raise their ready flags, so consumers time out */
-  int32_t reserved[2];
+  int32_t copy_multicast;      /* copy collectives that send one source to
+                                  every destination (AllGather, AllGatherV):
+                                  0 library default, 1 one job per source
+                                  writing all N destinations (one read),
+                                  2 one job per (source, destination) */
+  int32_t reserved[1];
 } snac_tuning;
 
 snac_status snac_get_tuning(snac_tuning* out);
