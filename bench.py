@@ -19,7 +19,8 @@ ReduceScatterV, the SNAC pipeline, and a plain copy) measured the same way.
 
 Other modes:
     --only NAME     run one workload (allreduce, copy, rs_ag, a2a, a2av, agv,
-                    rsv, pipeline_bf16, pipeline_f32) -- for profiler runs
+                    rsv, pipeline_bf16, pipeline_f32, pipeline_latency) --
+                    for profiler runs
     --sweep         AllReduce bf16 N=8 over 1 KiB .. 1 GiB per rank (JSON
                     lines to stdout; small sizes batched in a HIP graph)
 """
@@ -273,11 +274,62 @@ def run_pipeline(env: Env, steps: int, warmup: int, dtype: str):
     else:
         xs = [env.upload(wl.normal_f32(count, wl.CFG_PIPELINE_N8, r)) for r in range(N)]
     out = env.empty(count * es)
-    t = env.time_calls(lambda: snac.snac_pipeline_scale_reduce(env.ctx, xs, out, count, dtype, env.stream),
-                       steps, warmup)
-    snac.snac_check(env.ctx, env.stream)
+    # a staging ring that holds a whole 4096x8192 message (f32: 128 MiB) per rank
+    ctx = snac.snac_init(N, 128 * MiB, env.stream)
+    try:
+        t = env.time_calls(lambda: snac.snac_pipeline_scale_reduce(ctx, xs, out, count, dtype, env.stream),
+                           steps, warmup)
+        snac.snac_check(ctx, env.stream)
+    finally:
+        snac.snac_finalize(ctx, env.stream)
     per_rank = count * es
-    return result(f"snac_pipeline {dtype} N={N} ({rows}x{cols})/rank", t, 3 * N * per_rank + per_rank, per_rank)
+    return result(f"snac_pipeline {dtype} N={N} ({rows}x{cols})/rank", t, 3 * N * per_rank + per_rank, per_rank,
+                  staging_bytes_per_rank=128 * MiB)
+
+
+def graph_time(env: Env, call, batch: int = 10, reps: int = 20) -> float:
+    """Median seconds per call: `batch` calls captured in one HIP graph,
+    replayed `reps` times, each replay timed with events."""
+    torch = env.torch
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        call(torch.cuda.current_stream())  # first launch outside the capture
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(batch):
+                call(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    for _ in range(reps):
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / 1e3 / batch)
+    return float(np.median(times))
+
+
+def run_pipeline_latency(env: Env):
+    """SNAC pipeline bf16 N=8, 1 KiB .. 1 MiB per rank: microseconds per call."""
+    from copy_reduce_snac_amd import workloads as wl
+
+    snac = env.snac
+    top = MiB
+    xs = [env.upload(gen_bf16(top // 2, wl.CFG_PIPELINE_N8, r)) for r in range(N)]
+    out = env.empty(top)
+    lat = {}
+    for p in range(10, 21):
+        b = 1 << p
+        t = graph_time(env, lambda st: snac.snac_pipeline_scale_reduce(env.ctx, xs, out, b // 2, "bf16", st))
+        lat[str(b)] = round(t * 1e6, 2)
+    snac.snac_check(env.ctx, env.stream)
+    return {"workload": f"snac_pipeline bf16 N={N} latency, bytes/rank -> us/call (HIP graph, 10 calls)",
+            "us_per_call": lat}
 
 
 def run_sweep(env: Env):
@@ -285,7 +337,6 @@ def run_sweep(env: Env):
     are captured 10 at a time in a HIP graph and the graph is replayed."""
     from copy_reduce_snac_amd import workloads as wl
 
-    torch = env.torch
     snac = env.snac
     top = GiB
     src = [env.upload(gen_bf16(top // 2, wl.CFG_AR_BF16_N8, r)) for r in range(N)]
@@ -294,27 +345,7 @@ def run_sweep(env: Env):
     while (1 << p) <= top:
         b = 1 << p
         if b < 64 * MiB:
-            s = torch.cuda.Stream()
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.stream(s):
-                snac.snac_all_reduce(env.ctx, src, dst, b, "bf16", s)  # warm the launch path
-                torch.cuda.synchronize()
-                with torch.cuda.graph(g, stream=s):
-                    for _ in range(10):
-                        snac.snac_all_reduce(env.ctx, src, dst, b, "bf16", torch.cuda.current_stream())
-            torch.cuda.synchronize()
-            for _ in range(3):
-                g.replay()
-            torch.cuda.synchronize()
-            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            times = []
-            for _ in range(20):
-                ev0.record()
-                g.replay()
-                ev1.record()
-                torch.cuda.synchronize()
-                times.append(ev0.elapsed_time(ev1) / 1e3 / 10)
-            t = float(np.median(times))
+            t = graph_time(env, lambda st: snac.snac_all_reduce(env.ctx, src, dst, b, "bf16", st))
         else:
             t = env.time_calls(lambda: snac.snac_all_reduce(env.ctx, src, dst, b, "bf16", env.stream), 10, 3)
         r = result(f"allreduce_sum bf16 N={N} {b} B/rank", t, 2 * N * b, b,
@@ -351,6 +382,8 @@ def main() -> int:
             r = run_rs_ag(env, args.steps, args.warmup)
         elif name in ("a2a", "a2av", "agv", "rsv"):
             r = run_a2a(env, args.steps, args.warmup, name)
+        elif name == "pipeline_latency":
+            r = run_pipeline_latency(env)
         elif name.startswith("pipeline_"):
             r = run_pipeline(env, args.steps, args.warmup, name.split("_", 1)[1])
         else:
@@ -369,6 +402,7 @@ def main() -> int:
             env.torch.cuda.empty_cache()
         for dt in ("bf16", "f32"):
             extra.append(run_pipeline(env, args.steps, args.warmup, dt))
+        extra.append(run_pipeline_latency(env))
     t = head["ms_per_call"] / 1e3
     achieved = head["hbm_GBps"]
     traffic = recorded_traffic()

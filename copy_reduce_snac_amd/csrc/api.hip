@@ -20,8 +20,9 @@ struct snac_ctx {
   int nranks;
   int device;
   size_t staging_bytes;  // per rank
-  uint32_t slots;
-  uint32_t tile_bytes;
+  uint32_t slots;       // staging slots at the context's tile size
+  uint32_t tile_bytes;  // the context's (largest) pipeline tile
+  uint32_t flag_slots;  // slots the flag arrays cover (>= slots)
   char* workspace;  // device: staging then signal area
   char* staging;
   uint64_t* ready;
@@ -57,10 +58,12 @@ snac_status hip_fail(hipError_t e, const char* what) {
 
 snac_tuning g_tuning = {0, 0, 0, 0, 0, 0, 0, {0}};
 
-constexpr uint32_t kMaxPipeTile = 512u * 1024u;
+constexpr uint32_t kMaxPipeTile = 1024u * 1024u;
 constexpr uint32_t kMinPipeTile = 4096u;
 constexpr uint32_t kMinAutoSlots = 64u;
-constexpr size_t kDefaultStaging = 32u * 1024u * 1024u;
+constexpr uint32_t kMaxFlagSlots = 4096u;
+constexpr uint64_t kTargetTiles = 128u;  // tiles per message the pipeline aims for
+constexpr size_t kDefaultStaging = 64u * 1024u * 1024u;
 constexpr int kDefaultSpinLog2 = 22;
 
 LaunchCfg launch_cfg() { return LaunchCfg{g_tuning.wgs_per_cu, g_tuning.cache_policy}; }
@@ -331,7 +334,7 @@ snac_status snac_init(int nranks, size_t staging_bytes_per_rank, snac_stream str
   if (nranks < 1 || nranks > SNAC_MAX_RANKS) return fail(SNAC_E_ARG, "nranks %d outside 1..%d", nranks, SNAC_MAX_RANKS);
   const size_t staging = staging_bytes_per_rank ? staging_bytes_per_rank : kDefaultStaging;
   // pipeline tile: the tuning value, else the largest power of two up to
-  // 512 KiB that still leaves at least 64 slots in the ring
+  // 1 MiB that still leaves at least 64 slots in the ring
   uint32_t tile = (uint32_t)g_tuning.pipeline_tile_bytes;
   if (!tile) {
     tile = kMaxPipeTile;
@@ -350,8 +353,13 @@ snac_status snac_init(int nranks, size_t staging_bytes_per_rank, snac_stream str
   c->staging_bytes = staging;
   c->slots = (uint32_t)slots;
   c->tile_bytes = tile;
-  const uint64_t ready_words = (uint64_t)nranks * slots * kFlagStride;
-  const uint64_t free_words = (uint64_t)nranks * slots * kFlagStride;
+  // flags for the smaller tiles a call may cut the same ring into
+  uint64_t fslots = staging / kMinPipeTile;
+  if (fslots > kMaxFlagSlots) fslots = kMaxFlagSlots;
+  if (fslots < slots) fslots = slots;
+  c->flag_slots = (uint32_t)fslots;
+  const uint64_t ready_words = (uint64_t)nranks * fslots * kFlagStride;
+  const uint64_t free_words = (uint64_t)nranks * fslots * kFlagStride;
   c->signal_words = ready_words + free_words + kCtrlWords;
   const size_t staging_total = (size_t)nranks * staging;
   const size_t bytes = staging_total + c->signal_words * sizeof(uint64_t);
@@ -521,8 +529,19 @@ snac_status snac_pipeline_scale_reduce(snac_ctx* ctx, const void* const* x, void
   a.freed = ctx->freed;
   a.ctrl = ctx->ctrl;
   a.abort_word = ctx->abort_dev;
-  a.slots = ctx->slots;
-  a.tile_bytes = ctx->tile_bytes;
+  // Tile of this call: the context's, halved (doubling the slots of the same
+  // ring) while the message would have fewer than kTargetTiles tiles; on
+  // MI355X about 128 tiles per message balanced producers and consumers best.
+  uint32_t tile = ctx->tile_bytes, slots = ctx->slots;
+  if (!g_tuning.pipeline_tile_bytes) {
+    while (tile > kMinPipeTile && (uint64_t)slots * 2 <= ctx->flag_slots &&
+           (count * (uint64_t)e + tile - 1) / tile < kTargetTiles) {
+      tile >>= 1;
+      slots <<= 1;
+    }
+  }
+  a.slots = slots;
+  a.tile_bytes = tile;
   a.lookahead = (uint32_t)g_tuning.pipeline_lookahead;
   a.spin_limit_log2 = (uint32_t)(g_tuning.spin_limit_log2 ? g_tuning.spin_limit_log2 : kDefaultSpinLog2);
   a.drop_notify = g_tuning.debug_drop_notify;

@@ -327,25 +327,29 @@ hipError_t launch_pipeline(const PipeArgs& in, int dtype_bf16, const LaunchCfg& 
   const uint64_t tiles = (a.count + te - 1) / te;
   if (tiles == 0) return hipSuccess;
   if (tiles > 0x3fffffffull || te > 0xffffffffull) return hipErrorInvalidValue;
-  int per_cu = 0;
-  hipError_t err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), kThreads, 0);
-  if (err != hipSuccess) return err;
-  if (per_cu < 1) per_cu = 1;
-  const int want = cfg.wgs_per_cu > 0 ? cfg.wgs_per_cu : 2;
-  if (want < per_cu) per_cu = want;
-  const int cus = device_cu_count();
-  uint64_t grid = (uint64_t)(cus > 0 ? cus : 1) * (uint64_t)per_cu;
-  // queues: as many as there are tiles, workgroups and 2-slot rings allow
+  // queues: as many as there are tiles and 2-slot rings allow
   uint64_t Q = kMaxQueues;
   if (Q > tiles) Q = tiles;
   if (Q > a.slots / 2) Q = a.slots / 2;
   if (Q < 1) return hipErrorInvalidValue;
   const uint64_t S = a.slots / Q;
   const uint64_t qtiles = (tiles + Q - 1) / Q;
+  int per_cu = 0;
+  hipError_t err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), kThreads, 0);
+  if (err != hipSuccess) return err;
+  if (per_cu < 1) per_cu = 1;
+  // Measured on MI355X: when the ring holds the whole message no producer
+  // waits for a slot and 4 workgroups per CU keep HBM busiest; when slots
+  // are reused, more workgroups only add waiting ones, and 2 did best.
+  const int want = cfg.wgs_per_cu > 0 ? cfg.wgs_per_cu : (qtiles <= S ? 4 : 2);
+  if (want < per_cu) per_cu = want;
+  const int cus = device_cu_count();
+  uint64_t grid = (uint64_t)(cus > 0 ? cus : 1) * (uint64_t)per_cu;
   // lookahead: tiles staged ahead of the consumers, at most S - 1 (forward
   // progress); the whole ring by default
   uint64_t L = a.lookahead ? a.lookahead : S - 1;
   if (L > S - 1) L = S - 1;
+  if (L > qtiles) L = qtiles;  // as the kernel does: sizes the grid to the real work
   // enough workgroups to keep every queue's lookahead window busy, and a
   // multiple of Q so that the queues get equal shares
   const uint64_t items_per_q = (qtiles + L) * (uint64_t)(2 * a.nranks);
