@@ -63,6 +63,7 @@ constexpr uint32_t kMinPipeTile = 4096u;
 constexpr uint32_t kMinAutoSlots = 64u;
 constexpr uint32_t kMaxFlagSlots = 4096u;
 constexpr uint64_t kTargetTiles = 128u;  // tiles per message the pipeline aims for
+constexpr uint32_t kMinSplitTile = 65536u;  // ... but no smaller tiles than this
 constexpr size_t kDefaultStaging = 64u * 1024u * 1024u;
 constexpr int kDefaultSpinLog2 = 22;
 
@@ -530,11 +531,12 @@ snac_status snac_pipeline_scale_reduce(snac_ctx* ctx, const void* const* x, void
   a.ctrl = ctx->ctrl;
   a.abort_word = ctx->abort_dev;
   // Tile of this call: the context's, halved (doubling the slots of the same
-  // ring) while the message would have fewer than kTargetTiles tiles; on
-  // MI355X about 128 tiles per message balanced producers and consumers best.
+  // ring) while the message would have fewer than kTargetTiles tiles, down
+  // to 64 KiB; on MI355X about 128 tiles per message balanced producers and
+  // consumers best, and smaller tiles only add per-item overhead.
   uint32_t tile = ctx->tile_bytes, slots = ctx->slots;
   if (!g_tuning.pipeline_tile_bytes) {
-    while (tile > kMinPipeTile && (uint64_t)slots * 2 <= ctx->flag_slots &&
+    while (tile / 2 >= kMinSplitTile && (uint64_t)slots * 2 <= ctx->flag_slots &&
            (count * (uint64_t)e + tile - 1) / tile < kTargetTiles) {
       tile >>= 1;
       slots <<= 1;

@@ -56,8 +56,9 @@ struct PipeArgs {
 
 // control words (uint64 indices into ctrl)
 enum : uint32_t {
-  kCtrlTicket = 0,  // kMaxQueues tickets, kFlagStride apart
-  kCtrlDone = kMaxQueues * 16,
+  kCtrlTicket = 0,                   // kMaxQueues tickets, kFlagStride apart
+  kCtrlQDone = kMaxQueues * 16,      // kMaxQueues per-queue done counters
+  kCtrlDone = kCtrlQDone + kMaxQueues * 16,  // queues finished
   kCtrlEpoch = kCtrlDone + 16,
   kCtrlStatus = kCtrlEpoch + 16,
   kCtrlWords = kCtrlStatus + 16

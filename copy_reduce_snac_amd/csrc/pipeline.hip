@@ -40,9 +40,9 @@
 // co-residency assumption about the grid is needed.
 //
 // Sequence numbers are monotonic across calls: seq = epoch + round + 1 with
-// round = g / S.  The last workgroup to finish (an acq_rel counter) adds the
-// largest round count to the epoch and clears the ticket and done counters,
-// all in device memory, so consecutive launches (also inside a replayed
+// round = g / S.  The last workgroup to finish (acq_rel counters, per queue
+// then global) adds the largest round count to the epoch and clears the
+// ticket and done counters, all in device memory, so consecutive launches (also inside a replayed
 // graph) need no host bookkeeping and no reset pass.
 //
 // Waits are bounded: after 2^spin_limit_log2 polls a wait latches
@@ -279,15 +279,24 @@ __global__ __launch_bounds__(kThreads) void pipeline_kernel(const PipeArgs a) {
       consume<T, N>(a, gc * Q + q, uniform(q * S + gc % S), uniform(gc / S), w - (uint32_t)N, epoch, &s_ok);
     }
   }
+  // Completion, counted per queue first (each queue's workgroups hit their
+  // own counter; a same-address atomic costs ~12 ns, so one global counter
+  // would serialise the whole grid), then once per queue globally.  The last
+  // workgroup of a queue resets that queue's counters; the last queue to
+  // finish advances the epoch.
   if (threadIdx.x == 0) {
-    const uint64_t old =
-        __hip_atomic_fetch_add(&a.ctrl[kCtrlDone], (uint64_t)1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == (uint64_t)gridDim.x - 1) {
-      for (uint32_t i = 0; i < Q; ++i)
-        __hip_atomic_store(&a.ctrl[kCtrlTicket + i * kFlagStride], (uint64_t)0, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&a.ctrl[kCtrlDone], (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&a.ctrl[kCtrlEpoch], epoch + a.rounds, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t per_queue = gridDim.x / Q;  // the grid is a multiple of Q
+    uint64_t* qdone = &a.ctrl[kCtrlQDone + q * kFlagStride];
+    const uint64_t oq = __hip_atomic_fetch_add(qdone, (uint64_t)1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (oq == per_queue - 1) {
+      __hip_atomic_store(ticket, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(qdone, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint64_t old =
+          __hip_atomic_fetch_add(&a.ctrl[kCtrlDone], (uint64_t)1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      if (old == (uint64_t)Q - 1) {
+        __hip_atomic_store(&a.ctrl[kCtrlDone], (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&a.ctrl[kCtrlEpoch], epoch + a.rounds, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   }
 }

@@ -102,7 +102,7 @@ const char* snac_last_error(void);
  *                           leaves at least 64 slots (minimum 4 KiB).  Without
  *                           a tuning value a call halves the tile (doubling
  *                           the slots) while its message would have fewer
- *                           than 128 tiles.  The size must be a multiple of
+ *                           than 128 tiles, down to 64 KiB.  The size must be a multiple of
  *                           the tile and give at least 2 slots.  A ring that
  *                           holds a whole message runs fastest.
  *   stream                  signals are cleared on this stream.
