@@ -43,6 +43,38 @@ __device__ __forceinline__ void st16(char* p, u32x4 v) {
     *reinterpret_cast<u32x4*>(p) = v;
 }
 
+// Buffer-resource accesses.  A raw buffer resource covers [base, base +
+// bytes); the hardware returns zero for a load whose offset is at or past
+// `bytes` and drops such a store.  Sizing the resource to the bytes left in
+// a tile lets full and partial tiles run the same branch-free code, with a
+// scalar base and 32-bit lane offsets.  Word 3 selects the 32-bit data
+// format that untyped (raw) loads and stores on gfx9-family parts need.
+constexpr uint32_t kRawBufferWord3 = 0x00020000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kRawBufferWord3);
+}
+
+// cache-policy bits of a buffer access: 2 = nt (streaming)
+template <int CP>
+constexpr int load_aux() {
+  return (CP == kCacheStream || CP == kCacheStreamLoads) ? 2 : 0;
+}
+template <int CP>
+constexpr int store_aux() {
+  return (CP == kCacheStream || CP == kCacheStreamStores) ? 2 : 0;
+}
+
+template <int CP>
+__device__ __forceinline__ u32x4 bld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, load_aux<CP>());
+}
+
+template <int CP>
+__device__ __forceinline__ void bst16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, store_aux<CP>());
+}
+
 // 16 bytes from any address.  m = p & 3 must be uniform across the wave.
 // m == 0: one dword-aligned dwordx4.  Otherwise the 20 bytes starting at the
 // dword below p are loaded (every dword touched holds at least one wanted
@@ -116,6 +148,50 @@ __device__ __forceinline__ u32x4 reduce_unit(const u32x4 (&v)[N]) {
   }
   return out;
 }
+
+// Binary32 accumulator of one 16-byte unit: 4 lanes for F32, 8 for BF16
+// (lane 2c is the low half of word c, lane 2c + 1 its high half).  Sources
+// are added one at a time, so a reduce holds one accumulator per unit
+// instead of all N source values.
+template <typename T>
+struct UnitAcc {
+  static constexpr int kLanes = 16 / T::kSize;
+  float a[kLanes];
+
+  __device__ __forceinline__ void set(const u32x4& w) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if constexpr (T::kSize == 4) {
+        a[c] = __uint_as_float(w[c]);
+      } else {
+        a[2 * c] = bf16_lo(w[c]);
+        a[2 * c + 1] = bf16_hi(w[c]);
+      }
+    }
+  }
+  __device__ __forceinline__ void add(const u32x4& w) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if constexpr (T::kSize == 4) {
+        a[c] = a[c] + __uint_as_float(w[c]);
+      } else {
+        a[2 * c] = a[2 * c] + bf16_lo(w[c]);
+        a[2 * c + 1] = a[2 * c + 1] + bf16_hi(w[c]);
+      }
+    }
+  }
+  __device__ __forceinline__ u32x4 out() const {
+    u32x4 r;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if constexpr (T::kSize == 4)
+        r[c] = __float_as_uint(a[c]);
+      else
+        r[c] = pack_bf16(a[2 * c], a[2 * c + 1]);
+    }
+    return r;
+  }
+};
 
 template <typename T>
 __device__ __forceinline__ float load_elem(const char* p) {

@@ -5,9 +5,18 @@
 // Every workgroup rebuilds the job table in LDS from the kernel argument
 // (layout.hpp), numbers the tiles of all jobs with an exclusive scan, and
 // walks tiles blockIdx.x, blockIdx.x + gridDim.x, ...  A tile is
-// kThreads * 16 * U bytes of each source; each lane moves U 16-byte units,
-// issuing all U*N loads before the first add, then stores the result to one
-// destination or to all of them (a multicast: one read, N writes).
+// TH * 16 * U bytes of each source; each lane moves U 16-byte units.
+//
+//  * copy (256 threads, U = 4): the U loads of a tile, then its stores to one
+//    destination or to all of them (a multicast: one read, N writes).
+//  * reduce (128 threads, U = 8, 16 KiB per source): the sources are taken
+//    one at a time -- source k + 1's U loads are in flight while source k is
+//    added into binary32 accumulators -- and the finished tile is stored to
+//    each destination as one contiguous 16 KiB run.  Holding accumulators
+//    rather than all N sources keeps the register footprint independent of
+//    N, and a workgroup writes one destination at a time; on MI355X this
+//    beat loading all N sources at once and storing every destination per
+//    unit by 3-6 %.
 //
 // Two variants per Atom:
 //  * aligned: every job address is 16-byte aligned and every job length a
@@ -35,22 +44,23 @@ struct JobL {
   uint32_t tile0;
 };
 
-// Units per lane per tile: enough independent 16-byte loads in flight
-// (about 16 per lane) without exceeding the register budget.
-template <int N>
-constexpr int reduce_unroll() {
-  return N <= 4 ? 4 : (N <= 5 ? 3 : (N <= 8 ? 2 : 1));
-}
+constexpr int kCopyThreads = kThreads;
 constexpr int kCopyUnroll = 4;
+constexpr int kReduceThreads = 128;
+constexpr int kReduceUnroll = 8;
+// reduce collectives have at most kMaxRanks jobs (one per destination)
+static_assert(kMaxRanks <= kReduceThreads, "job scan needs a thread per job");
+// head (< 128 bytes) plus tail (< 16 bytes) edge elements, one per lane
+static_assert(kHeadAlign / 2 + 16 / 2 <= kReduceThreads, "edge elements need a lane each");
 
-template <int U>
+template <int TH, int U>
 constexpr uint32_t tile_of() {
-  return (uint32_t)kThreads * 16u * (uint32_t)U;
+  return (uint32_t)TH * 16u * (uint32_t)U;
 }
 
 // Build the job table and its tile numbering in LDS.  Returns the total
 // number of tiles; every thread of the workgroup must call it.
-template <bool ALIGNED>
+template <int TH, bool ALIGNED>
 __device__ uint32_t build_table(const CollDesc& d, uint32_t tile_bytes, JobL* jobs, uint32_t* scan, int& nj) {
   nj = num_jobs(d);
   const int t = threadIdx.x;
@@ -69,51 +79,57 @@ __device__ uint32_t build_table(const CollDesc& d, uint32_t tile_bytes, JobL* jo
   scan[t] = tiles;
   __syncthreads();
 #pragma unroll
-  for (int off = 1; off < kThreads; off <<= 1) {
+  for (int off = 1; off < TH; off <<= 1) {
     const uint32_t v = t >= off ? scan[t - off] : 0u;
     __syncthreads();
     scan[t] += v;
     __syncthreads();
   }
   if (t < nj) jobs[t].tile0 = scan[t] - tiles;
-  const uint32_t total = scan[kThreads - 1];
+  const uint32_t total = scan[TH - 1];
   __syncthreads();
   return total;
 }
 
-// Store U units (unit u at lane + u * kThreads * 16 bytes past base, if
-// below rem) to one destination or, for a multicast, to every destination.
-// NU > 0 unrolls the multicast for the common case ndst == NU.
-template <int U, int CP>
+// Store U units (unit u at lane + u * TH * 16 bytes past base, if below
+// rem) to one destination or, for a multicast, to every destination in
+// turn.  NU > 0 unrolls the multicast for the common case ndst == NU.
+template <int TH, int U, int CP, bool ALIGNED>
 __device__ __forceinline__ void store_one(char* p, uint32_t lane, uint32_t rem, const u32x4 (&v)[U]) {
-  if (rem == tile_of<U>()) {  // full tile: no per-unit guards
+  if constexpr (ALIGNED) {  // units at or past rem fall outside the resource
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(p, rem);
 #pragma unroll
-    for (int u = 0; u < U; ++u) st16<CP>(p + lane + (uint32_t)u * kThreads * 16u, v[u]);
+    for (int u = 0; u < U; ++u) bst16<CP>(r, lane + (uint32_t)u * TH * 16u, v[u]);
+    return;
+  }
+  if (rem == tile_of<TH, U>()) {  // full tile: no per-unit guards
+#pragma unroll
+    for (int u = 0; u < U; ++u) st16<CP>(p + lane + (uint32_t)u * TH * 16u, v[u]);
     return;
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const uint32_t o = lane + (uint32_t)u * kThreads * 16u;
+    const uint32_t o = lane + (uint32_t)u * TH * 16u;
     if (o < rem) st16<CP>(p + o, v[u]);
   }
 }
 
-template <int U, int CP, int NU>
+template <int TH, int U, int CP, int NU, bool ALIGNED>
 __device__ __forceinline__ void store_units(const CollDesc& d, int32_t dst_rank, uint64_t base, uint32_t lane,
                                             uint32_t rem, const u32x4 (&v)[U]) {
   if (dst_rank >= 0) {
-    store_one<U, CP>(static_cast<char*>(d.dst[dst_rank]) + base, lane, rem, v);
+    store_one<TH, U, CP, ALIGNED>(static_cast<char*>(d.dst[dst_rank]) + base, lane, rem, v);
     return;
   }
   if constexpr (NU > 0) {
     if (d.ndst == NU) {
 #pragma unroll
-      for (int k = 0; k < NU; ++k) store_one<U, CP>(static_cast<char*>(d.dst[k]) + base, lane, rem, v);
+      for (int k = 0; k < NU; ++k) store_one<TH, U, CP, ALIGNED>(static_cast<char*>(d.dst[k]) + base, lane, rem, v);
       return;
     }
   }
   const int nd = d.ndst;
-  for (int k = 0; k < nd; ++k) store_one<U, CP>(static_cast<char*>(d.dst[k]) + base, lane, rem, v);
+  for (int k = 0; k < nd; ++k) store_one<TH, U, CP, ALIGNED>(static_cast<char*>(d.dst[k]) + base, lane, rem, v);
 }
 
 // A tile resolved against its job: everything the loads and stores need.
@@ -129,7 +145,7 @@ struct TileRef {
 // Walks the job table in tile order.  The current job lives in scalar
 // registers; LDS is read only when a tile crosses into a later job, so a
 // tile of a long job costs a compare and a few scalar ops.
-template <int U, bool ALIGNED>
+template <uint32_t TILE, bool ALIGNED>
 struct JobCursor {
   const JobL* jobs;
   int nj;
@@ -161,7 +177,6 @@ struct JobCursor {
       while (j + 1 < nj && jobs[j + 1].tile0 <= tile) ++j;
       load_job();
     }
-    constexpr uint32_t TILE = tile_of<U>();
     TileRef r;
     r.J = J;
     r.lt = tile - J.tile0;
@@ -195,33 +210,63 @@ __device__ void reduce_edges(const CollDesc& d, const JobL& J, uint32_t head, ui
   }
 }
 
-// Issue the U*N loads of one tile.
-template <int N, int U, int CP, bool ALIGNED>
-__device__ __forceinline__ void reduce_load(const CollDesc& d, const TileRef& t, u32x4 (&v)[U][N]) {
+// Issue the U loads of source k of one tile.  FULL: the tile holds U whole
+// units per lane; otherwise units past the tile's body are left zero (and
+// are never stored).
+template <int TH, int U, int CP, bool ALIGNED, bool FULL>
+__device__ __forceinline__ void reduce_load(const CollDesc& d, const TileRef& t, int k, u32x4 (&v)[U]) {
   const uint32_t lane = threadIdx.x * 16u;
-  if (t.rem == tile_of<U>()) {  // full tile: no per-unit guards
+  const char* sp = static_cast<const char*>(d.src[k]) + t.J.src_off + t.toff;
+  if constexpr (ALIGNED) {  // units at or past rem read as zero
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(sp, t.rem);
 #pragma unroll
-    for (int k = 0; k < N; ++k) {
-      const char* sp = static_cast<const char*>(d.src[k]) + t.J.src_off + t.toff;
-      const uint32_t m = ALIGNED ? 0u : uniform((uint32_t)(uintptr_t)sp & 3u);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const char* q = sp + lane + (uint32_t)u * kThreads * 16u;
-        v[u][k] = ALIGNED ? ld16<CP>(q) : ld16_any<CP>(q, m);
-      }
-    }
+    for (int u = 0; u < U; ++u) v[u] = bld16<CP>(r, lane + (uint32_t)u * TH * 16u);
     return;
   }
+  const uint32_t m = ALIGNED ? 0u : uniform((uint32_t)(uintptr_t)sp & 3u);
 #pragma unroll
-  for (int k = 0; k < N; ++k) {
-    const char* sp = static_cast<const char*>(d.src[k]) + t.J.src_off + t.toff;
-    const uint32_t m = ALIGNED ? 0u : uniform((uint32_t)(uintptr_t)sp & 3u);
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t o = lane + (uint32_t)u * kThreads * 16u;
-      if (o < t.rem) v[u][k] = ALIGNED ? ld16<CP>(sp + o) : ld16_any<CP>(sp + o, m);
+  for (int u = 0; u < U; ++u) {
+    const uint32_t o = lane + (uint32_t)u * TH * 16u;
+    if constexpr (FULL) {
+      v[u] = ALIGNED ? ld16<CP>(sp + o) : ld16_any<CP>(sp + o, m);
+    } else {
+      v[u] = u32x4{0u, 0u, 0u, 0u};
+      if (o < t.rem) v[u] = ALIGNED ? ld16<CP>(sp + o) : ld16_any<CP>(sp + o, m);
     }
   }
+}
+
+// The reduced units of one tile, sources added in rank order.  Two register
+// buffers alternate: while source k is added from one, source k + 1 loads
+// into the other.  The source loop is deliberately not unrolled: unrolled,
+// the compiler issues every source's loads before the first add, which
+// measured about 5 % slower on MI355X than keeping two sources in flight.
+template <int N, typename T, int TH, int U, int CP, bool ALIGNED, bool FULL>
+__device__ __forceinline__ void reduce_tile(const CollDesc& d, const TileRef& t, u32x4 (&r)[U]) {
+  u32x4 a[U], b[U];
+  UnitAcc<T> acc[U];
+  reduce_load<TH, U, CP, ALIGNED, FULL>(d, t, 0, a);
+  if constexpr (N > 1) reduce_load<TH, U, CP, ALIGNED, FULL>(d, t, 1, b);
+#pragma unroll
+  for (int u = 0; u < U; ++u) acc[u].set(a[u]);
+  int k = 1;  // next source to add; it is in b
+#pragma unroll 1
+  for (; k + 1 < N; k += 2) {
+    reduce_load<TH, U, CP, ALIGNED, FULL>(d, t, k + 1, a);
+    __builtin_amdgcn_sched_barrier(0);  // issue these loads before waiting on b
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc[u].add(b[u]);
+    if (k + 2 < N) reduce_load<TH, U, CP, ALIGNED, FULL>(d, t, k + 2, b);
+    __builtin_amdgcn_sched_barrier(0);  // ... and these before waiting on a
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc[u].add(a[u]);
+  }
+  if (k < N) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc[u].add(b[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) r[u] = acc[u].out();
 }
 
 // ------------------------------------------------------------------ copy
@@ -239,78 +284,87 @@ __device__ void copy_edges(const CollDesc& d, const JobL& J, uint32_t head, uint
   }
 }
 
-template <int U, int CP, bool ALIGNED>
+template <int TH, int U, int CP, bool ALIGNED>
 __device__ __forceinline__ void copy_load(const CollDesc& d, const TileRef& t, u32x4 (&v)[U]) {
   const char* sp = static_cast<const char*>(d.src[t.J.src_rank]) + t.J.src_off + t.toff;
   const uint32_t lane = threadIdx.x * 16u;
+  if constexpr (ALIGNED) {  // units at or past rem read as zero (never stored)
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(sp, t.rem);
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = bld16<CP>(r, lane + (uint32_t)u * TH * 16u);
+    return;
+  }
   const uint32_t m = ALIGNED ? 0u : uniform((uint32_t)(uintptr_t)sp & 3u);
-  if (t.rem == tile_of<U>()) {  // full tile: no per-unit guards
+  if (t.rem == tile_of<TH, U>()) {  // full tile: no per-unit guards
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const char* q = sp + lane + (uint32_t)u * kThreads * 16u;
+      const char* q = sp + lane + (uint32_t)u * TH * 16u;
       v[u] = ALIGNED ? ld16<CP>(q) : ld16_any<CP>(q, m);
     }
     return;
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const uint32_t o = lane + (uint32_t)u * kThreads * 16u;
+    const uint32_t o = lane + (uint32_t)u * TH * 16u;
     if (o < t.rem) v[u] = ALIGNED ? ld16<CP>(sp + o) : ld16_any<CP>(sp + o, m);
   }
 }
 
-// ---------------------------------------------------------------- kernel
+// ---------------------------------------------------------------- kernels
 
-// N > 0: N-to-1 reduce of element type T.  N == 0: byte copy.
-//
-// The reduce loop is software-pipelined: once a tile's sources are summed
-// into r, the loads of the workgroup's next tile are issued before r is
-// stored, so loads stay in flight while the stores drain.
+// N-to-1 reduce of element type T over N sources.
 template <int N, typename T, int CP, bool ALIGNED>
-__global__ __launch_bounds__(kThreads) void coll_kernel(const CollDesc d) {
-  constexpr int U = N > 0 ? reduce_unroll<N>() : kCopyUnroll;
-  __shared__ JobL jobs[kMaxJobs];
-  __shared__ uint32_t scan[kThreads];
+__global__ __launch_bounds__(kReduceThreads) void reduce_kernel(const CollDesc d) {
+  constexpr int TH = kReduceThreads;
+  constexpr int U = kReduceUnroll;
+  constexpr uint32_t TILE = tile_of<TH, U>();
+  __shared__ JobL jobs[kMaxRanks];
+  __shared__ uint32_t scan[TH];
   int nj;
-  const uint32_t total = build_table<ALIGNED>(d, tile_of<U>(), jobs, scan, nj);
+  const uint32_t total = build_table<TH, ALIGNED>(d, TILE, jobs, scan, nj);
   uint32_t tile = blockIdx.x;
   if (tile >= total) return;
   const uint32_t lane = threadIdx.x * 16u;
-  JobCursor<U, ALIGNED> jc;
+  JobCursor<TILE, ALIGNED> jc;
   jc.init(jobs, nj, tile);
-  if constexpr (N > 0) {
-    TileRef cur = jc.at(tile);
-    u32x4 v[U][N];
-    reduce_load<N, U, CP, ALIGNED>(d, cur, v);
-    for (;;) {
-      const uint32_t next = tile + gridDim.x;
-      u32x4 r[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) r[u] = reduce_unit<T, N>(v[u]);
-      TileRef nxt;
-      const bool more = next < total;
-      if (more) {
-        nxt = jc.at(next);
-        reduce_load<N, U, CP, ALIGNED>(d, nxt, v);
-      }
-      if constexpr (!ALIGNED) {
-        if (cur.lt == 0) reduce_edges<T, N>(d, cur.J, cur.head, cur.body);
-      }
-      store_units<U, CP, N>(d, cur.J.dst_rank, cur.J.dst_off + cur.toff, lane, cur.rem, r);
-      if (!more) break;
-      cur = nxt;
-      tile = next;
+  for (; tile < total; tile += gridDim.x) {
+    const TileRef t = jc.at(tile);
+    u32x4 r[U];
+    if (ALIGNED || t.rem == TILE)
+      reduce_tile<N, T, TH, U, CP, ALIGNED, true>(d, t, r);
+    else
+      reduce_tile<N, T, TH, U, CP, ALIGNED, false>(d, t, r);
+    if constexpr (!ALIGNED) {
+      if (t.lt == 0) reduce_edges<T, N>(d, t.J, t.head, t.body);
     }
-  } else {
-    for (; tile < total; tile += gridDim.x) {
-      const TileRef cur = jc.at(tile);
-      u32x4 v[U];
-      copy_load<U, CP, ALIGNED>(d, cur, v);
-      if constexpr (!ALIGNED) {
-        if (cur.lt == 0) copy_edges(d, cur.J, cur.head, cur.body);
-      }
-      store_units<U, CP, 0>(d, cur.J.dst_rank, cur.J.dst_off + cur.toff, lane, cur.rem, v);
+    store_units<TH, U, CP, N, ALIGNED>(d, t.J.dst_rank, t.J.dst_off + t.toff, lane, t.rem, r);
+  }
+}
+
+// Byte copy of the collective's jobs.
+template <int CP, bool ALIGNED>
+__global__ __launch_bounds__(kCopyThreads) void copy_kernel(const CollDesc d) {
+  constexpr int TH = kCopyThreads;
+  constexpr int U = kCopyUnroll;
+  constexpr uint32_t TILE = tile_of<TH, U>();
+  __shared__ JobL jobs[kMaxJobs];
+  __shared__ uint32_t scan[TH];
+  static_assert(kMaxJobs <= TH, "job scan needs a thread per job");
+  int nj;
+  const uint32_t total = build_table<TH, ALIGNED>(d, TILE, jobs, scan, nj);
+  uint32_t tile = blockIdx.x;
+  if (tile >= total) return;
+  const uint32_t lane = threadIdx.x * 16u;
+  JobCursor<TILE, ALIGNED> jc;
+  jc.init(jobs, nj, tile);
+  for (; tile < total; tile += gridDim.x) {
+    const TileRef cur = jc.at(tile);
+    u32x4 v[U];
+    copy_load<TH, U, CP, ALIGNED>(d, cur, v);
+    if constexpr (!ALIGNED) {
+      if (cur.lt == 0) copy_edges(d, cur.J, cur.head, cur.body);
     }
+    store_units<TH, U, CP, 0, ALIGNED>(d, cur.J.dst_rank, cur.J.dst_off + cur.toff, lane, cur.rem, v);
   }
 }
 
@@ -320,11 +374,11 @@ using KernelFn = void (*)(const CollDesc);
 
 template <int N, typename T, int CP, bool A>
 KernelFn kernel_ptr() {
-  return &coll_kernel<N, T, CP, A>;
+  return &reduce_kernel<N, T, CP, A>;
 }
 
 template <typename T, int CP, bool A>
-KernelFn reduce_kernel(int n) {
+KernelFn reduce_kernel_n(int n) {
   switch (n) {
     case 1: return kernel_ptr<1, T, CP, A>();
     case 2: return kernel_ptr<2, T, CP, A>();
@@ -348,43 +402,28 @@ KernelFn reduce_kernel(int n) {
 
 template <typename T>
 KernelFn reduce_kernel_cp(int n, int cp, bool aligned) {
-  if (!aligned) return cp == kCached ? reduce_kernel<T, kCached, false>(n) : reduce_kernel<T, kCacheStream, false>(n);
+  if (!aligned) return cp == kCached ? reduce_kernel_n<T, kCached, false>(n) : reduce_kernel_n<T, kCacheStream, false>(n);
   switch (cp) {
-    case kCacheStream: return reduce_kernel<T, kCacheStream, true>(n);
-    case kCacheStreamStores: return reduce_kernel<T, kCacheStreamStores, true>(n);
-    case kCacheStreamLoads: return reduce_kernel<T, kCacheStreamLoads, true>(n);
-    default: return reduce_kernel<T, kCached, true>(n);
+    case kCacheStream: return reduce_kernel_n<T, kCacheStream, true>(n);
+    case kCacheStreamStores: return reduce_kernel_n<T, kCacheStreamStores, true>(n);
+    case kCacheStreamLoads: return reduce_kernel_n<T, kCacheStreamLoads, true>(n);
+    default: return reduce_kernel_n<T, kCached, true>(n);
   }
 }
 
-static KernelFn copy_kernel(int cp, bool aligned) {
-  if (!aligned) return cp == kCached ? kernel_ptr<0, F32, kCached, false>() : kernel_ptr<0, F32, kCacheStream, false>();
+static KernelFn copy_kernel_cp(int cp, bool aligned) {
+  if (!aligned) return cp == kCached ? &copy_kernel<kCached, false> : &copy_kernel<kCacheStream, false>;
   switch (cp) {
-    case kCacheStream: return kernel_ptr<0, F32, kCacheStream, true>();
-    case kCacheStreamStores: return kernel_ptr<0, F32, kCacheStreamStores, true>();
-    case kCacheStreamLoads: return kernel_ptr<0, F32, kCacheStreamLoads, true>();
-    default: return kernel_ptr<0, F32, kCached, true>();
-  }
-}
-
-static int unroll_for(const CollDesc& d) {
-  if (!coll_is_reduce(d.coll)) return kCopyUnroll;
-  switch (d.nsrc) {
-    case 1: return reduce_unroll<1>();
-    case 2: return reduce_unroll<2>();
-    case 3: return reduce_unroll<3>();
-    case 4: return reduce_unroll<4>();
-    case 5: return reduce_unroll<5>();
-    case 6: return reduce_unroll<6>();
-    case 7: return reduce_unroll<7>();
-    case 8: return reduce_unroll<8>();
-    default: return reduce_unroll<16>();
+    case kCacheStream: return &copy_kernel<kCacheStream, true>;
+    case kCacheStreamStores: return &copy_kernel<kCacheStreamStores, true>;
+    case kCacheStreamLoads: return &copy_kernel<kCacheStreamLoads, true>;
+    default: return &copy_kernel<kCached, true>;
   }
 }
 
 uint32_t coll_tile_bytes(const CollDesc& d, bool aligned) {
   (void)aligned;
-  return (uint32_t)kThreads * 16u * (uint32_t)unroll_for(d);
+  return coll_is_reduce(d.coll) ? tile_of<kReduceThreads, kReduceUnroll>() : tile_of<kCopyThreads, kCopyUnroll>();
 }
 
 int device_cu_count() {
@@ -407,24 +446,27 @@ hipError_t launch_collective(const CollDesc& d, bool aligned, uint64_t tiles, co
   KernelFn fn = nullptr;
   // tuning value 0 = library default (streaming loads and stores), 4 = cached
   const int cp = cfg.cache_policy == 0 ? kCacheStream : (cfg.cache_policy == 4 ? kCached : cfg.cache_policy);
-  if (coll_is_reduce(d.coll)) {
+  const bool reduce = coll_is_reduce(d.coll);
+  if (reduce) {
+    if (num_jobs(d) > kMaxRanks) return hipErrorInvalidValue;
     fn = d.esize == 4 ? reduce_kernel_cp<F32>(d.nsrc, cp, aligned) : reduce_kernel_cp<BF16>(d.nsrc, cp, aligned);
   } else {
-    fn = copy_kernel(cp, aligned);
+    fn = copy_kernel_cp(cp, aligned);
   }
   if (!fn) return hipErrorInvalidValue;
+  const int threads = reduce ? kReduceThreads : kCopyThreads;
   int per_cu = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), kThreads, 0);
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), threads, 0);
   if (e != hipSuccess) return e;
   if (per_cu < 1) per_cu = 1;
   // Measured on MI355X: the 1:1 read/write streams run fastest with few
   // workgroups per CU (more concurrent write streams lower HBM efficiency).
-  const int want = cfg.wgs_per_cu > 0 ? cfg.wgs_per_cu : (coll_is_reduce(d.coll) && d.nsrc >= 4 ? 1 : 2);
+  const int want = cfg.wgs_per_cu > 0 ? cfg.wgs_per_cu : (reduce && d.nsrc >= 4 ? 1 : 2);
   if (want < per_cu) per_cu = want;
   const int cus = device_cu_count();
   uint64_t grid = (uint64_t)(cus > 0 ? cus : 1) * (uint64_t)per_cu;
   if (grid > tiles) grid = tiles;
-  hipLaunchKernelGGL(fn, dim3((uint32_t)grid), dim3(kThreads), 0, stream, d);
+  hipLaunchKernelGGL(fn, dim3((uint32_t)grid), dim3(threads), 0, stream, d);
   return hipGetLastError();
 }
 
