@@ -52,14 +52,14 @@ def log(*a):
 
 
 # sources of the collective kernel (the dominant kernel of the benchmark)
-KERNEL_SOURCES = ("atoms.hpp", "collectives.hip", "internal.hpp", "layout.hpp")
+KERNEL_SOURCES = ("include/snac_device.hpp", "include/snac_layout.hpp", "include/snac.h",
+                  "copy_reduce_snac_amd/csrc/collectives.hip", "copy_reduce_snac_amd/csrc/internal.hpp")
 
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "copy_reduce_snac_amd", "csrc")
     for name in KERNEL_SOURCES:
-        with open(os.path.join(csrc, name), "rb") as f:
+        with open(os.path.join(ROOT, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
     return h.hexdigest()[:16]

@@ -60,6 +60,41 @@ class snac_tuning(ctypes.Structure):
     ]
 
 
+SNAC_MAX_COUNTS = SNAC_MAX_RANKS * SNAC_MAX_RANKS
+SNAC_DESC_ALIGNED = 1
+SNAC_FLAG_STRIDE = 16
+
+
+class snac_dev_ctx(ctypes.Structure):
+    _fields_ = [
+        ("nranks", ctypes.c_int32),
+        ("spin_limit_log2", ctypes.c_uint32),
+        ("status", ctypes.c_void_p),
+        ("abort_word", ctypes.c_void_p),
+        ("barrier", ctypes.c_void_p),
+        ("flags", ctypes.c_void_p),
+        ("nflags", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint32),
+        ("staging", ctypes.c_void_p),
+        ("staging_bytes", ctypes.c_uint64),
+    ]
+
+
+class snac_coll_desc(ctypes.Structure):
+    _fields_ = [
+        ("coll", ctypes.c_int32),
+        ("nsrc", ctypes.c_int32),
+        ("ndst", ctypes.c_int32),
+        ("esize", ctypes.c_int32),
+        ("split_multicast", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
+        ("bytes", ctypes.c_uint64),
+        ("src", ctypes.c_void_p * SNAC_MAX_RANKS),
+        ("dst", ctypes.c_void_p * SNAC_MAX_RANKS),
+        ("counts", ctypes.c_uint64 * SNAC_MAX_COUNTS),
+    ]
+
+
 _lib = None
 _VP = ctypes.c_void_p
 _SZ = ctypes.c_size_t
@@ -86,6 +121,9 @@ _SIGS = {
     "snac_all_to_all_v": (_I, [_VP, ctypes.POINTER(_VP), ctypes.POINTER(_VP), ctypes.POINTER(_SZ), _I, _VP]),
     "snac_pipeline_scale_reduce": (_I, [_VP, ctypes.POINTER(_VP), _VP, _SZ, _I, _VP]),
     "snac_plan": (_I, [_I, _I, _I, _SZ, ctypes.POINTER(_SZ), ctypes.POINTER(snac_job), _I, ctypes.POINTER(_I)]),
+    "snac_get_device_context": (_I, [_VP, ctypes.POINTER(snac_dev_ctx)]),
+    "snac_describe": (_I, [_VP, _I, ctypes.POINTER(_VP), ctypes.POINTER(_VP), _SZ, ctypes.POINTER(_SZ), _I,
+                           ctypes.POINTER(snac_coll_desc)]),
     "snac_get_tuning": (_I, [ctypes.POINTER(snac_tuning)]),
     "snac_set_tuning": (_I, [ctypes.POINTER(snac_tuning)]),
 }
@@ -245,6 +283,24 @@ def snac_all_to_all_v(ctx, srcs, dsts, counts, dtype, stream=None):
 def snac_pipeline_scale_reduce(ctx, xs, out, count, dtype, stream=None):
     _check(lib().snac_pipeline_scale_reduce(ctx, _ptrs(xs), _ptr(out), count, _dtype(dtype), _stream(stream)),
            "snac_pipeline_scale_reduce")
+
+
+# -------------------------------------------------------- device-side API
+def snac_get_device_context(ctx: int) -> snac_dev_ctx:
+    """The device view of a context, for kernels using include/snac_device.hpp."""
+    out = snac_dev_ctx()
+    _check(lib().snac_get_device_context(ctx, ctypes.byref(out)), "snac_get_device_context")
+    return out
+
+
+def snac_describe(ctx: int, coll: int, srcs: Sequence, dsts: Sequence, nbytes: int = 0,
+                  counts: Iterable[int] | None = None, dtype="byte") -> snac_coll_desc:
+    """A validated, laid-out collective for snac::collective() in a user kernel."""
+    out = snac_coll_desc()
+    cnt = _sizes(counts) if counts is not None else None
+    _check(lib().snac_describe(ctx, coll, _ptrs(srcs), _ptrs(dsts), nbytes, cnt, _dtype(dtype), ctypes.byref(out)),
+           "snac_describe")
+    return out
 
 
 # ---------------------------------------------------------- layout, tuning

@@ -9,10 +9,9 @@
 #include <new>
 #include <string>
 
-#include "../../include/snac.h"
-#include "atoms.hpp"
 #include "internal.hpp"
-#include "layout.hpp"
+#include "snac.h"
+#include "snac_layout.hpp"
 
 using namespace snac;
 
@@ -28,6 +27,7 @@ struct snac_ctx {
   uint64_t* ready;
   uint64_t* freed;
   uint64_t* ctrl;
+  uint64_t* user_flags;  // kUserFlags flags for device-side users
   uint64_t signal_words;
   uint32_t* abort_host;  // host-mapped word (hipHostMalloc)
   uint32_t* abort_dev;   // its device-visible address
@@ -179,8 +179,17 @@ snac_status check_ctx(const snac_ctx* ctx) {
   return SNAC_OK;
 }
 
+// Set by snac_describe around a call of fixed_collective / v_collective:
+// the validated plan is copied out instead of launched.
+thread_local snac_coll_desc* g_describe = nullptr;
+
 snac_status run(Plan& p, hipStream_t stream) {
   finish_plan(p);
+  p.d.flags = p.aligned ? SNAC_DESC_ALIGNED : 0;
+  if (g_describe) {
+    *g_describe = p.d;
+    return ok();
+  }
   if (p.tiles == 0) return ok();
   hipError_t e = launch_collective(p.d, p.aligned, p.tiles, launch_cfg(), stream);
   if (e != hipSuccess) return hip_fail(e, "collective launch");
@@ -197,6 +206,16 @@ Plan base_plan(int32_t coll, int nsrc, int ndst, int esize) {
   return p;
 }
 
+// A request with nothing to move: no launch, or an empty descriptor.
+snac_status describe_empty(int32_t coll, int n, int e) {
+  if (g_describe) {
+    Plan p = base_plan(coll, n, n, e);
+    p.d.flags = SNAC_DESC_ALIGNED;
+    *g_describe = p.d;
+  }
+  return ok();
+}
+
 // fixed-size collectives share their checks
 snac_status fixed_collective(int32_t coll, snac_ctx* ctx, const void* const* src, void* const* dst, size_t bytes,
                              snac_dtype dtype, snac_stream stream) {
@@ -210,7 +229,7 @@ snac_status fixed_collective(int32_t coll, snac_ctx* ctx, const void* const* src
   if (bytes % (size_t)e) return fail(SNAC_E_ARG, "bytes (%zu) is not a multiple of the element size %d", bytes, e);
   if ((coll == kReduceScatter || coll == kAllToAll) && bytes % ((size_t)n * e))
     return fail(SNAC_E_ARG, "bytes (%zu) is not a multiple of N * element size (%d)", bytes, n * e);
-  if (bytes == 0) return ok();
+  if (bytes == 0) return describe_empty(coll, n, e);
   uint64_t in_b[kMaxRanks], out_b[kMaxRanks];
   for (int i = 0; i < n; ++i) {
     in_b[i] = bytes;
@@ -252,7 +271,7 @@ snac_status v_collective(int32_t coll, snac_ctx* ctx, const void* const* src, vo
     if (counts[i] > ((uint64_t)1 << 40)) return fail(SNAC_E_ARG, "counts[%d] is implausibly large", i);
     total += counts[i];
   }
-  if (total == 0) return ok();
+  if (total == 0) return describe_empty(coll, n, e);
   uint64_t in_b[kMaxRanks], out_b[kMaxRanks];
   for (int i = 0; i < n; ++i) {
     if (coll == kAllGatherV) {
@@ -361,7 +380,7 @@ snac_status snac_init(int nranks, size_t staging_bytes_per_rank, snac_stream str
   c->flag_slots = (uint32_t)fslots;
   const uint64_t ready_words = (uint64_t)nranks * fslots * kFlagStride;
   const uint64_t free_words = (uint64_t)nranks * fslots * kFlagStride;
-  c->signal_words = ready_words + free_words + kCtrlWords;
+  c->signal_words = ready_words + free_words + kCtrlWords + (uint64_t)kUserFlags * kFlagStride;
   const size_t staging_total = (size_t)nranks * staging;
   const size_t bytes = staging_total + c->signal_words * sizeof(uint64_t);
   e = hipMalloc(reinterpret_cast<void**>(&c->workspace), bytes);
@@ -373,6 +392,7 @@ snac_status snac_init(int nranks, size_t staging_bytes_per_rank, snac_stream str
   c->ready = reinterpret_cast<uint64_t*>(c->workspace + staging_total);
   c->freed = c->ready + ready_words;
   c->ctrl = c->freed + free_words;
+  c->user_flags = c->ctrl + kCtrlWords;
   e = hipHostMalloc(reinterpret_cast<void**>(&c->abort_host), sizeof(uint32_t), hipHostMallocMapped | hipHostMallocCoherent);
   if (e != hipSuccess) {
     (void)hipFree(c->workspace);
@@ -407,6 +427,8 @@ snac_status snac_check(snac_ctx* ctx, snac_stream stream) {
   if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "re-arming the signal area");
   if (status == SNAC_E_TIMEOUT) return fail(SNAC_E_TIMEOUT, "a device-side SNAC wait exceeded its spin limit");
+  if (status == SNAC_E_ARG)
+    return fail(SNAC_E_ARG, "a device-side collective's template arguments did not match its descriptor");
   return fail(SNAC_E_ABORTED, "device-side SNAC waits were aborted");
 }
 
@@ -550,6 +572,43 @@ snac_status snac_pipeline_scale_reduce(snac_ctx* ctx, const void* const* x, void
   hipError_t err = launch_pipeline(a, dtype == SNAC_BF16, launch_cfg(), (hipStream_t)stream, nullptr);
   if (err != hipSuccess) return hip_fail(err, "pipeline launch");
   return ok();
+}
+
+snac_status snac_get_device_context(const snac_ctx* ctx, snac_dev_ctx* out) {
+  if (!ctx || !out) return fail(SNAC_E_ARG, "NULL argument");
+  std::memset(out, 0, sizeof *out);
+  out->nranks = ctx->nranks;
+  out->spin_limit_log2 = (uint32_t)(g_tuning.spin_limit_log2 ? g_tuning.spin_limit_log2 : kDefaultSpinLog2);
+  out->status = ctx->ctrl + kCtrlStatus;
+  out->abort_word = ctx->abort_dev;
+  out->barrier = ctx->ctrl + kCtrlBarrier;
+  out->flags = ctx->user_flags;
+  out->nflags = kUserFlags;
+  out->staging = ctx->staging;
+  out->staging_bytes = ctx->staging_bytes;
+  return ok();
+}
+
+snac_status snac_describe(const snac_ctx* ctx, snac_coll coll, const void* const* src, void* const* dst, size_t bytes,
+                          const size_t* counts, snac_dtype dtype, snac_coll_desc* out) {
+  if (!out) return fail(SNAC_E_ARG, "out is NULL");
+  std::memset(out, 0, sizeof *out);
+  snac_ctx* c = const_cast<snac_ctx*>(ctx);
+  g_describe = out;
+  snac_status st;
+  switch (coll) {
+    case SNAC_COLL_ALL_REDUCE:
+    case SNAC_COLL_REDUCE_SCATTER:
+    case SNAC_COLL_ALL_GATHER:
+    case SNAC_COLL_ALL_TO_ALL: st = fixed_collective((int32_t)coll, c, src, dst, bytes, dtype, nullptr); break;
+    case SNAC_COLL_ALL_GATHER_V:
+    case SNAC_COLL_REDUCE_SCATTER_V:
+    case SNAC_COLL_ALL_TO_ALL_V: st = v_collective((int32_t)coll, c, src, dst, counts, dtype, nullptr); break;
+    default: st = fail(SNAC_E_ARG, "unknown collective %d", (int)coll);
+  }
+  g_describe = nullptr;
+  if (st != SNAC_OK) std::memset(out, 0, sizeof *out);
+  return st;
 }
 
 snac_status snac_plan(snac_coll coll, int nranks, snac_dtype dtype, size_t bytes, const size_t* counts,

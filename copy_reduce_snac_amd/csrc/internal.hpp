@@ -4,9 +4,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "layout.hpp"
+#include "snac_layout.hpp"
 
 namespace snac {
+
+constexpr int kThreads = 256;  // workgroup size of the pipeline and copy kernels
 
 struct LaunchCfg {
   int wgs_per_cu;    // 0: as many as fit
@@ -61,9 +63,11 @@ enum : uint32_t {
   kCtrlDone = kCtrlQDone + kMaxQueues * 16,  // queues finished
   kCtrlEpoch = kCtrlDone + 16,
   kCtrlStatus = kCtrlEpoch + 16,
-  kCtrlWords = kCtrlStatus + 16
+  kCtrlBarrier = kCtrlStatus + 16,   // group barrier: count, then generation
+  kCtrlWords = kCtrlBarrier + 32
 };
-constexpr uint32_t kFlagStride = 16;  // uint64 words between flags (128 B)
+constexpr uint32_t kFlagStride = SNAC_FLAG_STRIDE;  // uint64 words between flags (128 B)
+constexpr uint32_t kUserFlags = 1024;               // flags handed to device-side users
 
 hipError_t launch_pipeline(const PipeArgs& a, int dtype_bf16, const LaunchCfg& cfg, hipStream_t stream,
                            uint32_t* grid_out);

@@ -51,50 +51,15 @@
 // later wait gives up at once, so the grid always drains.
 #include <hip/hip_runtime.h>
 
-#include "atoms.hpp"
 #include "internal.hpp"
+#include "snac_device.hpp"
 
 namespace snac {
 
-enum : uint64_t { kStatusTimeout = 5, kStatusAborted = 7 };
-
-__device__ __forceinline__ uint64_t ld_relaxed(uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ void latch_status(uint64_t* ctrl, uint64_t code) {
-  uint64_t expected = 0;
-  __hip_atomic_compare_exchange_strong(&ctrl[kCtrlStatus], &expected, code, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Wait until every vector memory operation this wave has issued is done
-// (s_waitcnt vmcnt(0); the gfx9 encoding leaves expcnt and lgkmcnt free).
-// A store is done once the L2 has accepted it.
-__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// One lane waits until *flag >= target with relaxed agent-scope loads.
-// Returns false (and the status word is set) on timeout, abort, or an error
-// latched elsewhere.  The caller adds the acquire fence where it needs one.
-__device__ bool wait_geq(uint64_t* flag, uint64_t target, const PipeArgs& a) {
-  const uint64_t limit = 1ull << a.spin_limit_log2;
-  uint64_t spins = 0;
-  while (ld_relaxed(flag) < target) {
-    if ((spins & 15u) == 15u) {
-      if (ld_relaxed(&a.ctrl[kCtrlStatus]) != 0) return false;
-      uint32_t* ab = const_cast<uint32_t*>(a.abort_word);
-      if (__hip_atomic_load(ab, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != 0) {
-        latch_status(a.ctrl, kStatusAborted);
-        return false;
-      }
-    }
-    if (++spins >= limit) {
-      latch_status(a.ctrl, kStatusTimeout);
-      return false;
-    }
-    __builtin_amdgcn_s_sleep(1);
-  }
-  return true;
+// The bounded waits of this kernel: status word and abort word of the
+// context, its poll budget (the flag primitives are snac_device.hpp's).
+__device__ __forceinline__ WaitCtl pipe_wait(const PipeArgs& a) {
+  return WaitCtl{&a.ctrl[kCtrlStatus], a.abort_word, a.spin_limit_log2};
 }
 
 // y = 0.5 * x + r on one 16-byte unit, rounded to T.
@@ -123,14 +88,14 @@ __device__ __forceinline__ uint32_t tile_count(const PipeArgs& a, uint32_t t) {
 }
 
 template <typename T, int N>
-__device__ void produce(const PipeArgs& a, uint32_t t, uint32_t gslot, uint32_t round, uint32_t r, uint64_t epoch,
+__device__ void stage_item(const PipeArgs& a, uint32_t t, uint32_t gslot, uint32_t round, uint32_t r, uint64_t epoch,
                         uint32_t* s_ok) {
   constexpr uint32_t E = T::kSize;
   if (round > 0) {
     if (threadIdx.x == 0) {
       bool ok = true;
       for (int p = 0; p < N && ok; ++p)
-        ok = wait_geq(&a.freed[((uint64_t)gslot * N + p) * kFlagStride], epoch + round, a);
+        ok = wait_geq(&a.freed[((uint64_t)gslot * N + p) * kFlagStride], epoch + round, pipe_wait(a));
       *s_ok = ok ? 1u : 0u;
     }
     __syncthreads();
@@ -179,7 +144,7 @@ __device__ void produce(const PipeArgs& a, uint32_t t, uint32_t gslot, uint32_t 
 }
 
 template <typename T, int N>
-__device__ void consume(const PipeArgs& a, uint32_t t, uint32_t gslot, uint32_t round, uint32_t part, uint64_t epoch,
+__device__ void consume_item(const PipeArgs& a, uint32_t t, uint32_t gslot, uint32_t round, uint32_t part, uint64_t epoch,
                         uint32_t* s_ok) {
   constexpr uint32_t E = T::kSize;
   const uint64_t seq = epoch + round + 1;
@@ -188,7 +153,8 @@ __device__ void consume(const PipeArgs& a, uint32_t t, uint32_t gslot, uint32_t 
   // releases the other waves to read the staged data.
   if (threadIdx.x == 0) {
     bool ok = true;
-    for (int r = 0; r < N && ok; ++r) ok = wait_geq(&a.ready[((uint64_t)r * a.slots + gslot) * kFlagStride], seq, a);
+    for (int r = 0; r < N && ok; ++r)
+      ok = wait_geq(&a.ready[((uint64_t)r * a.slots + gslot) * kFlagStride], seq, pipe_wait(a));
     if (ok) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       wait_vm();
@@ -273,10 +239,10 @@ __global__ __launch_bounds__(kThreads) void pipeline_kernel(const PipeArgs a) {
     const uint32_t g = uniform(item / (uint32_t)(2 * N));
     const uint32_t w = uniform(item - g * (uint32_t)(2 * N));
     if (w < (uint32_t)N) {
-      if (g < qtiles) produce<T, N>(a, g * Q + q, uniform(q * S + g % S), uniform(g / S), w, epoch, &s_ok);
+      if (g < qtiles) stage_item<T, N>(a, g * Q + q, uniform(q * S + g % S), uniform(g / S), w, epoch, &s_ok);
     } else if (g >= L) {
       const uint32_t gc = g - L;
-      consume<T, N>(a, gc * Q + q, uniform(q * S + gc % S), uniform(gc / S), w - (uint32_t)N, epoch, &s_ok);
+      consume_item<T, N>(a, gc * Q + q, uniform(q * S + gc % S), uniform(gc / S), w - (uint32_t)N, epoch, &s_ok);
     }
   }
   // Completion, counted per queue first (each queue's workgroups hit their

@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define SNAC_ABI_VERSION 1
+#define SNAC_ABI_VERSION 2
 #define SNAC_MAX_RANKS 16
 
 typedef enum snac_status {
@@ -72,6 +72,51 @@ typedef enum snac_coll {
 
 typedef void* snac_stream; /* hipStream_t */
 typedef struct snac_ctx snac_ctx;
+
+/*
+ * snac_coll_desc -- one collective call, validated and laid out: what the
+ * collective kernels take as their argument, and what a user kernel passes
+ * to snac::collective() (include/snac_device.hpp) to run the same
+ * collective inside its own grid.  Filled by snac_describe(); plain data, so
+ * it can be copied into a kernel argument by value (2336 bytes).
+ */
+#define SNAC_MAX_COUNTS (SNAC_MAX_RANKS * SNAC_MAX_RANKS)
+#define SNAC_DESC_ALIGNED 1 /* flags: every job's addresses and length are 16-byte aligned */
+typedef struct snac_coll_desc {
+  int32_t coll;            /* snac_coll value (internal Atom kinds use 100, 101) */
+  int32_t nsrc;            /* source buffers (= N for collectives) */
+  int32_t ndst;            /* destination buffers (= N for collectives) */
+  int32_t esize;           /* element size in bytes */
+  int32_t split_multicast; /* multicast jobs split into one job per destination */
+  int32_t flags;           /* SNAC_DESC_* bits */
+  uint64_t bytes;          /* per-rank input bytes (fixed-size collectives) */
+  const void* src[SNAC_MAX_RANKS];
+  void* dst[SNAC_MAX_RANKS];
+  uint64_t counts[SNAC_MAX_COUNTS]; /* V collectives: element counts */
+} snac_coll_desc;
+
+/*
+ * snac_dev_ctx -- what device code needs of a context: the signal words and
+ * the staging rings, for kernels that use the device-side API of
+ * include/snac_device.hpp.  Filled by snac_get_device_context(); plain data,
+ * passed to a kernel by value.  The pointers stay valid until
+ * snac_finalize().  (Purlin 0.6.5 "Samples": the host-created context is
+ * passed to the kernel, which hands it to the collective.)
+ */
+#define SNAC_FLAG_STRIDE 16 /* uint64 words between flags: one 128-byte line each */
+typedef struct snac_dev_ctx {
+  int32_t nranks;
+  uint32_t spin_limit_log2;   /* device waits give up after 2^k polls */
+  uint64_t* status;           /* first device error latched here; snac_check() reports and clears it */
+  const uint32_t* abort_word; /* host-mapped; nonzero after snac_abort() */
+  uint64_t* barrier;          /* two words (count, generation) for snac::group_barrier */
+  uint64_t* flags;            /* user SNAC flags: flag i at flags + i * SNAC_FLAG_STRIDE; zero after
+                                 snac_init and after a re-arming snac_check; the library never writes them */
+  uint32_t nflags;            /* number of user flags */
+  uint32_t reserved;
+  char* staging;              /* rank r's staging ring at staging + r * staging_bytes */
+  uint64_t staging_bytes;     /* per rank; shared with snac_pipeline_scale_reduce (not concurrently) */
+} snac_dev_ctx;
 
 /* ------------------------------------------------------------------ info */
 
@@ -125,7 +170,10 @@ snac_status snac_finalize(snac_ctx* ctx, snac_stream stream);
 
 /*
  * snac_check -- synchronise `stream`, read the context's device status word
- * and clear it.  Returns SNAC_OK, SNAC_E_TIMEOUT or SNAC_E_ABORTED.
+ * and clear it.  Returns SNAC_OK, or the latched code: SNAC_E_TIMEOUT,
+ * SNAC_E_ABORTED, or SNAC_E_ARG (a device-side collective whose template
+ * arguments did not match its descriptor).  A latched error also re-arms
+ * the context: every signal word (flags, barrier, tickets) is cleared.
  */
 snac_status snac_check(snac_ctx* ctx, snac_stream stream);
 
@@ -264,6 +312,31 @@ snac_status snac_all_to_all_v(snac_ctx* ctx, const void* const* src, void* const
  */
 snac_status snac_pipeline_scale_reduce(snac_ctx* ctx, const void* const* x, void* out, size_t count,
                                        snac_dtype dtype, snac_stream stream);
+
+/* ----------------------------------------------------- device-side API */
+
+/*
+ * snac_get_device_context -- the device view of a context (snac_dev_ctx) for
+ * kernels that call the device-side API.  Errors: SNAC_E_ARG.
+ */
+snac_status snac_get_device_context(const snac_ctx* ctx, snac_dev_ctx* out);
+
+/*
+ * snac_describe -- validate a collective exactly as the matching host entry
+ * point would and lay it out into *out instead of launching it, for a
+ * kernel that runs the collective itself with snac::collective()
+ * (Purlin 0.6.5 "Samples": a collective called from inside a kernel).
+ *   coll    which collective
+ *   src, dst, dtype
+ *           as for the host entry point
+ *   bytes   per-rank input bytes (fixed-size collectives; ignored for V)
+ *   counts  element counts (V collectives: N, or N*N for ALL_TO_ALL_V;
+ *           ignored otherwise)
+ * A request that the host call would treat as a no-op (zero bytes) gives a
+ * descriptor with no jobs.  Errors: SNAC_E_ARG, SNAC_E_STATE.
+ */
+snac_status snac_describe(const snac_ctx* ctx, snac_coll coll, const void* const* src, void* const* dst, size_t bytes,
+                          const size_t* counts, snac_dtype dtype, snac_coll_desc* out);
 
 /* -------------------------------------------------------- layout engine */
 

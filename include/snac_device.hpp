@@ -1,0 +1,873 @@
+// snac_device.hpp -- the device-side API: the copy and N-to-1 reduce Atoms,
+// the Stage / Notify / And Consume flag primitives and the single-kernel
+// collectives, callable from inside any HIP kernel for gfx950 (MI355X).
+//
+// Purlin 0.6.5 ("Device-side", "Samples") lets a kernel call an Atom or a
+// whole collective between pieces of its own work, with the collective's
+// arguments and a context passed in by value.  This header is that layer
+// for one MI355X whose N logical ranks all live in its HBM:
+//
+//   snac::copy(dst, src, bytes)                workgroup-cooperative copy of
+//                                              one slice, any alignment
+//   snac::reduce<T, N>(dst, ndst, src, count)  workgroup-cooperative N-to-1
+//                                              reduce of one slice
+//   snac::wait_geq / snac::notify              SNAC flag primitives (bounded
+//                                              acquire polls, release stores)
+//   snac::group_barrier(ctx, blocks)           all `blocks` workgroups meet;
+//                                              stores before it are visible
+//                                              to every one of them after it
+//   snac::collective<T, N, TH>(desc, ctx, block, blocks, coll_blocks)
+//                                              any of the seven collectives
+//                                              of a snac_coll_desc, run by
+//                                              the calling workgroups
+//
+// The library's own collective kernels are thin wrappers over the same
+// tile engine (run_reduce / run_copy), so host and device calls move data
+// with identical code and give identical bits.
+//
+// Arithmetic: binary32 accumulation in source order 0..N-1 starting from the
+// source-0 value, one rounding to the output type (bf16: round to nearest
+// even with v_cvt_pk_bf16_f32).  Translation units including this header
+// should be built with -ffp-contract=off so that no add is fused.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "snac.h"
+#include "snac_layout.hpp"
+
+namespace snac {
+
+// ======================================================== gfx950 primitives
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// same vector with 4-byte alignment: still one global_load_dwordx4 (the
+// hardware needs only dword alignment for multi-dword accesses)
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Cache policies for collective inputs and outputs: streaming accesses carry
+// the non-temporal hint, so single-use data does not displace other lines.
+enum : int { kCached = 0, kCacheStream = 1, kCacheStreamStores = 2, kCacheStreamLoads = 3 };
+
+template <int CP>
+__device__ __forceinline__ u32x4 ld16(const char* p) {
+  if constexpr (CP == kCacheStream || CP == kCacheStreamLoads)
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  else
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
+template <int CP>
+__device__ __forceinline__ void st16(char* p, u32x4 v) {
+  if constexpr (CP == kCacheStream || CP == kCacheStreamStores)
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+  else
+    *reinterpret_cast<u32x4*>(p) = v;
+}
+
+// Buffer-resource accesses.  A raw buffer resource covers [base, base +
+// bytes); the hardware returns zero for a load whose offset is at or past
+// `bytes` and drops such a store.  Sizing the resource to the bytes left in
+// a tile lets full and partial tiles run the same branch-free code, with a
+// scalar base and 32-bit lane offsets.  Word 3 selects the 32-bit data
+// format that untyped (raw) loads and stores on gfx9-family parts need.
+constexpr uint32_t kRawBufferWord3 = 0x00020000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kRawBufferWord3);
+}
+
+// cache-policy bits of a buffer access: 2 = nt (streaming)
+template <int CP>
+constexpr int load_aux() {
+  return (CP == kCacheStream || CP == kCacheStreamLoads) ? 2 : 0;
+}
+template <int CP>
+constexpr int store_aux() {
+  return (CP == kCacheStream || CP == kCacheStreamStores) ? 2 : 0;
+}
+
+template <int CP>
+__device__ __forceinline__ u32x4 bld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, load_aux<CP>());
+}
+
+template <int CP>
+__device__ __forceinline__ void bst16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, store_aux<CP>());
+}
+
+template <int CP>
+__device__ __forceinline__ u32x4 ld16_a4(const char* p) {
+  if constexpr (CP == kCacheStream || CP == kCacheStreamLoads)
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_a4*>(p));
+  else
+    return *reinterpret_cast<const u32x4_a4*>(p);
+}
+
+// 16 bytes from any address.  m = p & 3 must be uniform across the wave.
+// m == 0: one dword-aligned dwordx4.  Otherwise the 20 bytes starting at the
+// dword below p are loaded (every dword touched holds at least one wanted
+// byte, so nothing outside the source range's dwords is read) and shifted
+// into place with v_alignbyte_b32.
+template <int CP>
+__device__ __forceinline__ u32x4 ld16_any(const char* p, uint32_t m) {
+  if (m == 0) return ld16_a4<CP>(p);
+  const char* b = p - m;
+  const u32x4 a = ld16_a4<CP>(b);
+  const uint32_t e = *reinterpret_cast<const uint32_t*>(b + 16);
+  u32x4 r;
+  r.x = __builtin_amdgcn_alignbyte(a.y, a.x, m);
+  r.y = __builtin_amdgcn_alignbyte(a.z, a.y, m);
+  r.z = __builtin_amdgcn_alignbyte(a.w, a.z, m);
+  r.w = __builtin_amdgcn_alignbyte(e, a.w, m);
+  return r;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two binary32 values -> two bf16 (round to nearest even), lo in bits 0..15.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const f32x2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+__device__ __forceinline__ uint16_t to_bf16(float x) { return (uint16_t)(pack_bf16(x, 0.0f) & 0xffffu); }
+
+// Element types of the reduce: tags carrying the storage size.
+struct F32 {
+  static constexpr int kSize = 4;
+};
+struct BF16 {
+  static constexpr int kSize = 2;
+};
+
+// One 16-byte unit of the N-to-1 reduce from all N source values at once:
+// out = R(v[0] + v[1] + ... + v[N-1]) per element, added in index order.
+template <typename T, int N>
+__device__ __forceinline__ u32x4 reduce_unit(const u32x4 (&v)[N]) {
+  u32x4 out;
+  if constexpr (T::kSize == 4) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      float acc = __uint_as_float(v[0][c]);
+#pragma unroll
+      for (int k = 1; k < N; ++k) acc = acc + __uint_as_float(v[k][c]);
+      out[c] = __float_as_uint(acc);
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      float lo = bf16_lo(v[0][c]);
+      float hi = bf16_hi(v[0][c]);
+#pragma unroll
+      for (int k = 1; k < N; ++k) {
+        lo = lo + bf16_lo(v[k][c]);
+        hi = hi + bf16_hi(v[k][c]);
+      }
+      out[c] = pack_bf16(lo, hi);
+    }
+  }
+  return out;
+}
+
+// Binary32 accumulator of one 16-byte unit: 4 lanes for F32, 8 for BF16
+// (lane 2c is the low half of word c, lane 2c + 1 its high half).  Sources
+// are added one at a time, so a reduce holds one accumulator per unit
+// instead of all N source values.
+template <typename T>
+struct UnitAcc {
+  static constexpr int kLanes = 16 / T::kSize;
+  float a[kLanes];
+
+  __device__ __forceinline__ void set(const u32x4& w) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if constexpr (T::kSize == 4) {
+        a[c] = __uint_as_float(w[c]);
+      } else {
+        a[2 * c] = bf16_lo(w[c]);
+        a[2 * c + 1] = bf16_hi(w[c]);
+      }
+    }
+  }
+  __device__ __forceinline__ void add(const u32x4& w) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if constexpr (T::kSize == 4) {
+        a[c] = a[c] + __uint_as_float(w[c]);
+      } else {
+        a[2 * c] = a[2 * c] + bf16_lo(w[c]);
+        a[2 * c + 1] = a[2 * c + 1] + bf16_hi(w[c]);
+      }
+    }
+  }
+  __device__ __forceinline__ u32x4 out() const {
+    u32x4 r;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if constexpr (T::kSize == 4)
+        r[c] = __float_as_uint(a[c]);
+      else
+        r[c] = pack_bf16(a[2 * c], a[2 * c + 1]);
+    }
+    return r;
+  }
+};
+
+template <typename T>
+__device__ __forceinline__ float load_elem(const char* p) {
+  if constexpr (T::kSize == 4)
+    return *reinterpret_cast<const float*>(p);
+  else
+    return __uint_as_float((uint32_t)(*reinterpret_cast<const uint16_t*>(p)) << 16);
+}
+
+template <typename T>
+__device__ __forceinline__ void store_elem(char* p, float v) {
+  if constexpr (T::kSize == 4)
+    *reinterpret_cast<float*>(p) = v;
+  else
+    *reinterpret_cast<uint16_t*>(p) = to_bf16(v);
+}
+
+// Force a wave-uniform value into a scalar register.
+__device__ __forceinline__ uint32_t uniform(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ uint64_t uniform64(uint64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// ================================================= workgroup-level Atoms
+//
+// Every thread of the calling workgroup calls these with the same arguments
+// (blockDim.x threads, a multiple of 64).  They move one slice; splitting a
+// buffer into slices across workgroups is the caller's business, as in the
+// copy sample of Purlin 0.6.5.
+
+// dst[0..bytes) = src[0..bytes), bytewise, any alignment; the ranges must
+// not overlap.  The destination is stored in aligned 16-byte units after a
+// head of at most 15 bytes; the source is read with ld16_any.
+template <int CP = kCacheStream>
+__device__ void copy(void* dst, const void* src, uint64_t bytes) {
+  char* d = static_cast<char*>(dst);
+  const char* s = static_cast<const char*>(src);
+  const uint32_t nt = blockDim.x;
+  uint64_t head = (16u - ((uintptr_t)d & 15u)) & 15u;
+  if (head > bytes) head = bytes;
+  const uint64_t body = (bytes - head) & ~(uint64_t)15;
+  const char* sb = s + head;
+  char* db = d + head;
+  const uint32_t m = (uint32_t)((uintptr_t)sb & 3u);
+  constexpr int U = 4;
+  const uint64_t step = (uint64_t)nt * 16u * U;
+  for (uint64_t base = 0; base < body; base += step) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint64_t o = base + ((uint64_t)threadIdx.x + (uint64_t)u * nt) * 16u;
+      if (o < body) v[u] = ld16_any<CP>(sb + o, m);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint64_t o = base + ((uint64_t)threadIdx.x + (uint64_t)u * nt) * 16u;
+      if (o < body) st16<CP>(db + o, v[u]);
+    }
+  }
+  const uint64_t tail = bytes - head - body;
+  for (uint64_t i = threadIdx.x; i < head + tail; i += nt) {
+    const uint64_t o = i < head ? i : head + body + (i - head);
+    d[o] = s[o];
+  }
+}
+
+// for d < ndst, i < count: dst[d][i] = R(src[0][i] + ... + src[N-1][i]),
+// binary32 in source order, R the rounding to T.  Every pointer must be
+// aligned to the element size; a destination may equal a source (in place),
+// no other overlap.  Destinations must share their address residue modulo
+// 16 (they are stored in aligned 16-byte units after a common head).
+template <typename T, int N, int CP = kCacheStream>
+__device__ void reduce(void* const* dst, int ndst, const void* const* src, uint64_t count) {
+  constexpr uint32_t E = T::kSize;
+  const uint32_t nt = blockDim.x;
+  const uint64_t bytes = count * E;
+  uint64_t head = (16u - ((uintptr_t)dst[0] & 15u)) & 15u;
+  if (head > bytes) head = bytes;
+  const uint64_t body = (bytes - head) & ~(uint64_t)15;
+  uint32_t m[N];
+#pragma unroll
+  for (int k = 0; k < N; ++k) m[k] = (uint32_t)(((uintptr_t)src[k] + head) & 3u);
+  for (uint64_t o = (uint64_t)threadIdx.x * 16u; o < body; o += (uint64_t)nt * 16u) {
+    UnitAcc<T> acc;
+    acc.set(ld16_any<CP>(static_cast<const char*>(src[0]) + head + o, m[0]));
+#pragma unroll
+    for (int k = 1; k < N; ++k) acc.add(ld16_any<CP>(static_cast<const char*>(src[k]) + head + o, m[k]));
+    const u32x4 r = acc.out();
+    for (int d = 0; d < ndst; ++d) st16<CP>(static_cast<char*>(dst[d]) + head + o, r);
+  }
+  const uint64_t ne = (head + (bytes - head - body)) / E;
+  for (uint64_t i = threadIdx.x; i < ne; i += nt) {
+    const uint64_t o = i * E < head ? i * E : body + i * E;
+    float acc = load_elem<T>(static_cast<const char*>(src[0]) + o);
+#pragma unroll
+    for (int k = 1; k < N; ++k) acc = acc + load_elem<T>(static_cast<const char*>(src[k]) + o);
+    for (int d = 0; d < ndst; ++d) store_elem<T>(static_cast<char*>(dst[d]) + o, acc);
+  }
+}
+
+// ============================================= SNAC signal primitives
+//
+// Flags are uint64 words, one per 128-byte line (SNAC_FLAG_STRIDE words
+// apart), carrying monotonic sequence numbers: a producer stores seq, a
+// consumer waits for flag >= seq.  Ordering follows the HIP agent-scope
+// memory model: release = write the L2 back (buffer_wbl2) then store,
+// acquire = relaxed polls then invalidate (buffer_inv).  Each is issued by
+// one lane for the whole workgroup, because on MI355X these fences
+// serialise across the GPU.
+
+enum : uint64_t { kStatusTimeout = SNAC_E_TIMEOUT, kStatusAborted = SNAC_E_ABORTED };
+
+__device__ __forceinline__ uint64_t ld_relaxed(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void st_relaxed(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Latch the first device error in a status word (later codes are dropped).
+__device__ __forceinline__ void latch_status(uint64_t* status, uint64_t code) {
+  uint64_t expected = 0;
+  __hip_atomic_compare_exchange_strong(status, &expected, code, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until every vector memory operation this wave has issued is done
+// (s_waitcnt vmcnt(0); the gfx9 encoding leaves expcnt and lgkmcnt free).
+// A store is done once the L2 has accepted it.
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// What a bounded wait needs to know: where errors latch, the host-mapped
+// abort word, and the poll budget.
+struct WaitCtl {
+  uint64_t* status;
+  const uint32_t* abort_word;
+  uint32_t spin_limit_log2;
+};
+
+__device__ __forceinline__ WaitCtl wait_ctl(const snac_dev_ctx& c) {
+  return WaitCtl{c.status, c.abort_word, c.spin_limit_log2};
+}
+
+// One lane waits until *flag >= target with relaxed agent-scope loads and
+// s_sleep back-off.  Returns false, with the status word set, after
+// 2^spin_limit_log2 polls (SNAC_E_TIMEOUT), when the abort word is set
+// (SNAC_E_ABORTED), or at once when an error is already latched -- so every
+// wait ends.  The caller adds the acquire fence where it needs one.
+__device__ inline bool wait_geq(const uint64_t* flag, uint64_t target, const WaitCtl& w) {
+  const uint64_t limit = 1ull << w.spin_limit_log2;
+  uint64_t spins = 0;
+  while (ld_relaxed(flag) < target) {
+    if ((spins & 15u) == 15u) {
+      if (ld_relaxed(w.status) != 0) return false;
+      uint32_t* ab = const_cast<uint32_t*>(w.abort_word);
+      if (ab && __hip_atomic_load(ab, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != 0) {
+        latch_status(w.status, kStatusAborted);
+        return false;
+      }
+    }
+    if (++spins >= limit) {
+      latch_status(w.status, kStatusTimeout);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return true;
+}
+
+// Notify (workgroup-level; every thread calls it): once every wave's stores
+// are accepted by the L2, one lane writes the L2 back at agent scope and
+// stores *flag = value.  After a consumer's acquire sees the value, every
+// store this workgroup made before notify() is visible to it.
+__device__ inline void notify(uint64_t* flag, uint64_t value) {
+  wait_vm();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    wait_vm();
+    st_relaxed(flag, value);
+  }
+}
+
+// Consume (workgroup-level): one lane waits for flags[i * stride] >= target
+// for i < n, then issues one acquire fence; the workgroup meets at a
+// barrier.  Returns false on timeout or abort (the same in every thread).
+__device__ inline bool consume(const uint64_t* flags, int n, uint64_t stride, uint64_t target, const WaitCtl& w) {
+  __shared__ uint32_t s_ok;
+  if (threadIdx.x == 0) {
+    bool ok = true;
+    for (int i = 0; i < n && ok; ++i) ok = wait_geq(flags + (uint64_t)i * stride, target, w);
+    if (ok) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      wait_vm();
+    }
+    s_ok = ok ? 1u : 0u;
+  }
+  __syncthreads();
+  const uint32_t ok = uniform(s_ok);
+  __syncthreads();
+  return ok != 0;
+}
+
+// All `blocks` calling workgroups meet (a grid barrier over a subset of the
+// grid).  Stores made before it by any of them are visible to all of them
+// after it.  The workgroups must be co-resident (at most what the device
+// runs at once for this kernel), and only one group may use a context's
+// barrier at a time.  Returns false on timeout or abort.
+//
+// Words: barrier[0] counts arrivals, barrier[SNAC_FLAG_STRIDE] is the
+// generation.  A workgroup reads the generation before it arrives; the last
+// arrival resets the count and then advances the generation with a release
+// store, which the others wait for.
+__device__ inline bool group_barrier(uint64_t* barrier, uint32_t blocks, const WaitCtl& w) {
+  __shared__ uint32_t s_ok;
+  wait_vm();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint64_t* count = barrier;
+    uint64_t* gen = barrier + SNAC_FLAG_STRIDE;
+    const uint64_t g = ld_relaxed(gen);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const uint64_t old = __hip_atomic_fetch_add(count, (uint64_t)1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    bool ok = true;
+    if (old + 1 == blocks) {
+      st_relaxed(count, 0);
+      __hip_atomic_store(gen, g + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      ok = wait_geq(gen, g + 1, w);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    s_ok = ok ? 1u : 0u;
+  }
+  __syncthreads();
+  const uint32_t ok = uniform(s_ok);
+  __syncthreads();
+  return ok != 0;
+}
+
+__device__ inline bool group_barrier(const snac_dev_ctx& c, uint32_t blocks) {
+  return group_barrier(c.barrier, blocks, wait_ctl(c));
+}
+
+// ======================================================== the tile engine
+//
+// A collective's jobs (snac_layout.hpp) are cut into tiles of kTileBytes of
+// each source.  Every workgroup rebuilds the job table in LDS from the
+// descriptor, numbers the tiles of all jobs with an exclusive scan, and
+// walks tiles block, block + blocks, ...  A lane moves U = kTileBytes /
+// (TH * 16) 16-byte units per tile.
+//
+//  * copy: the U loads of a tile, then its stores to one destination or to
+//    all of them (a multicast: one read, N writes).
+//  * reduce: the sources are taken one at a time -- source k + 1's loads are
+//    in flight while source k is added into binary32 accumulators -- and
+//    the finished tile goes to each destination as one contiguous run.
+//    Accumulators rather than all N sources keep the register footprint
+//    independent of N, and a workgroup writes one destination at a time; on
+//    MI355X this beat loading all N sources at once and storing every
+//    destination per unit by 3-6 %.
+//
+// Two variants of each:
+//  * aligned (SNAC_DESC_ALIGNED): every job address 16-byte aligned and every
+//    job length a multiple of 16 -- raw buffer loads and stores whose
+//    resource is sized to the tile, so partial tiles need no guards.
+//  * generic: any element-aligned address.  Each job is split into a head
+//    (bytes until the destination reaches a 128-byte line), a body of
+//    aligned 16-byte stores whose sources are read with ld16_any, and a
+//    tail; head and tail move one element per lane in tile 0 of the job.
+
+constexpr uint32_t kTileBytes = 16384;
+
+template <int TH>
+constexpr int tile_units() {
+  static_assert(TH % 64 == 0 && TH >= 64 && TH <= 1024, "workgroup size must be a multiple of 64, at most 1024");
+  return (int)(kTileBytes / (TH * 16u));
+}
+
+struct JobL {
+  uint64_t src_off;
+  uint64_t dst_off;
+  uint64_t bytes;
+  int32_t src_rank;
+  int32_t dst_rank;
+  uint32_t head;
+  uint32_t tile0;
+};
+
+// Build the job table and its tile numbering in LDS.  Returns the total
+// number of tiles; every thread of the workgroup must call it.  Thread t
+// owns jobs t*K .. t*K + K - 1 (K = ceil(MAXJ / TH)).
+template <int TH, int MAXJ, bool ALIGNED>
+__device__ uint32_t build_table(const CollDesc& d, uint32_t tile_bytes, JobL* jobs, uint32_t* scan, int& nj) {
+  constexpr int K = (MAXJ + TH - 1) / TH;
+  nj = num_jobs(d);
+  const int t = threadIdx.x;
+  uint32_t mine[K];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    const int j = t * K + i;
+    mine[i] = 0;
+    if (j < nj) {
+      const Job jb = make_job(d, j);
+      const uint32_t head = ALIGNED ? 0u : job_head_bytes(d, jb);
+      mine[i] = (uint32_t)job_tiles(jb, head, tile_bytes);
+      jobs[j] = JobL{jb.src_off, jb.dst_off, jb.bytes, jb.src_rank, jb.dst_rank, head, 0u};
+    }
+    sum += mine[i];
+  }
+  scan[t] = sum;
+  __syncthreads();
+#pragma unroll
+  for (int off = 1; off < TH; off <<= 1) {
+    const uint32_t v = t >= off ? scan[t - off] : 0u;
+    __syncthreads();
+    scan[t] += v;
+    __syncthreads();
+  }
+  uint32_t run = scan[t] - sum;
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    const int j = t * K + i;
+    if (j < nj) jobs[j].tile0 = run;
+    run += mine[i];
+  }
+  const uint32_t total = scan[TH - 1];
+  __syncthreads();
+  return total;
+}
+
+// Store U units (unit u at lane + u * TH * 16 bytes past base, if below
+// rem) to one destination or, for a multicast, to every destination in
+// turn.  NU > 0 unrolls the multicast for the common case ndst == NU.
+template <int TH, int U, int CP, bool ALIGNED>
+__device__ __forceinline__ void store_one(char* p, uint32_t lane, uint32_t rem, const u32x4 (&v)[U]) {
+  if constexpr (ALIGNED) {  // units at or past rem fall outside the resource
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(p, rem);
+#pragma unroll
+    for (int u = 0; u < U; ++u) bst16<CP>(r, lane + (uint32_t)u * TH * 16u, v[u]);
+    return;
+  }
+  if (rem == (uint32_t)TH * 16u * U) {  // full tile: no per-unit guards
+#pragma unroll
+    for (int u = 0; u < U; ++u) st16<CP>(p + lane + (uint32_t)u * TH * 16u, v[u]);
+    return;
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t o = lane + (uint32_t)u * TH * 16u;
+    if (o < rem) st16<CP>(p + o, v[u]);
+  }
+}
+
+template <int TH, int U, int CP, int NU, bool ALIGNED>
+__device__ __forceinline__ void store_units(const CollDesc& d, int32_t dst_rank, uint64_t base, uint32_t lane,
+                                            uint32_t rem, const u32x4 (&v)[U]) {
+  if (dst_rank >= 0) {
+    store_one<TH, U, CP, ALIGNED>(static_cast<char*>(d.dst[dst_rank]) + base, lane, rem, v);
+    return;
+  }
+  if constexpr (NU > 0) {
+    if (d.ndst == NU) {
+#pragma unroll
+      for (int k = 0; k < NU; ++k) store_one<TH, U, CP, ALIGNED>(static_cast<char*>(d.dst[k]) + base, lane, rem, v);
+      return;
+    }
+  }
+  const int nd = d.ndst;
+  for (int k = 0; k < nd; ++k) store_one<TH, U, CP, ALIGNED>(static_cast<char*>(d.dst[k]) + base, lane, rem, v);
+}
+
+// A tile resolved against its job: everything the loads and stores need.
+struct TileRef {
+  JobL J;
+  uint32_t lt;     // tile index within the job
+  uint64_t toff;   // byte offset of the tile's first 16-byte unit in the job
+  uint32_t rem;    // body bytes of this tile (multiple of 16; 0 for an edge-only tile)
+  uint32_t head;   // job head bytes (generic path)
+  uint64_t body;   // job body bytes
+};
+
+// Walks the job table in tile order.  The current job lives in scalar
+// registers; LDS is read only when a tile crosses into a later job, so a
+// tile of a long job costs a compare and a few scalar ops.
+template <uint32_t TILE, bool ALIGNED>
+struct JobCursor {
+  const JobL* jobs;
+  int nj;
+  int j;
+  uint32_t next_tile0;  // first tile of job j + 1 (or ~0)
+  JobL J;
+
+  __device__ __forceinline__ void load_job() {
+    J.src_off = uniform64(jobs[j].src_off);
+    J.dst_off = uniform64(jobs[j].dst_off);
+    J.bytes = uniform64(jobs[j].bytes);
+    J.src_rank = (int32_t)uniform((uint32_t)jobs[j].src_rank);
+    J.dst_rank = (int32_t)uniform((uint32_t)jobs[j].dst_rank);
+    J.head = ALIGNED ? 0u : uniform(jobs[j].head);
+    J.tile0 = uniform(jobs[j].tile0);
+    next_tile0 = j + 1 < nj ? uniform(jobs[j + 1].tile0) : 0xffffffffu;
+  }
+
+  __device__ __forceinline__ void init(const JobL* t, int n, uint32_t tile) {
+    jobs = t;
+    nj = n;
+    j = 0;
+    while (j + 1 < nj && jobs[j + 1].tile0 <= tile) ++j;
+    load_job();
+  }
+
+  __device__ __forceinline__ TileRef at(uint32_t tile) {
+    if (tile >= next_tile0) {
+      while (j + 1 < nj && jobs[j + 1].tile0 <= tile) ++j;
+      load_job();
+    }
+    TileRef r;
+    r.J = J;
+    r.lt = tile - J.tile0;
+    r.head = J.head;
+    r.body = ALIGNED ? J.bytes : ((J.bytes - r.head) & ~(uint64_t)15);
+    r.toff = (uint64_t)r.head + (uint64_t)r.lt * TILE;
+    const uint64_t end = (uint64_t)r.head + r.body;
+    const uint64_t left = end > r.toff ? end - r.toff : 0;
+    r.rem = left > TILE ? TILE : (uint32_t)left;
+    return r;
+  }
+};
+
+// ------------------------------------------------------------ reduce tiles
+
+// Head and tail elements of a job (< 128 + 16 bytes), one element per lane.
+template <typename T, int N>
+__device__ void reduce_edges(const CollDesc& d, const JobL& J, uint32_t head, uint64_t body) {
+  constexpr uint32_t E = T::kSize;
+  const uint32_t nh = head / E;
+  const uint32_t ne = nh + (uint32_t)(J.bytes - head - body) / E;
+  for (uint32_t t = threadIdx.x; t < ne; t += blockDim.x) {
+    const uint64_t off = t < nh ? (uint64_t)t * E : (uint64_t)head + body + (uint64_t)(t - nh) * E;
+    float acc = load_elem<T>(static_cast<const char*>(d.src[0]) + J.src_off + off);
+#pragma unroll
+    for (int k = 1; k < N; ++k) acc = acc + load_elem<T>(static_cast<const char*>(d.src[k]) + J.src_off + off);
+    if (J.dst_rank >= 0) {
+      store_elem<T>(static_cast<char*>(d.dst[J.dst_rank]) + J.dst_off + off, acc);
+    } else {
+      for (int k = 0; k < d.ndst; ++k) store_elem<T>(static_cast<char*>(d.dst[k]) + J.dst_off + off, acc);
+    }
+  }
+}
+
+// Issue the U loads of source k of one tile.  FULL: the tile holds U whole
+// units per lane; otherwise units past the tile's body are left zero (and
+// are never stored).
+template <int TH, int U, int CP, bool ALIGNED, bool FULL>
+__device__ __forceinline__ void reduce_load(const CollDesc& d, const TileRef& t, int k, u32x4 (&v)[U]) {
+  const uint32_t lane = threadIdx.x * 16u;
+  const char* sp = static_cast<const char*>(d.src[k]) + t.J.src_off + t.toff;
+  if constexpr (ALIGNED) {  // units at or past rem read as zero
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(sp, t.rem);
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = bld16<CP>(r, lane + (uint32_t)u * TH * 16u);
+    return;
+  }
+  const uint32_t m = uniform((uint32_t)(uintptr_t)sp & 3u);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t o = lane + (uint32_t)u * TH * 16u;
+    if constexpr (FULL) {
+      v[u] = ld16_any<CP>(sp + o, m);
+    } else {
+      v[u] = u32x4{0u, 0u, 0u, 0u};
+      if (o < t.rem) v[u] = ld16_any<CP>(sp + o, m);
+    }
+  }
+}
+
+// The reduced units of one tile, sources added in rank order.  Two register
+// buffers alternate: while source k is added from one, source k + 1 loads
+// into the other.  The source loop is deliberately not unrolled: unrolled,
+// the compiler issues every source's loads before the first add, which
+// measured about 5 % slower on MI355X than keeping two sources in flight.
+template <int N, typename T, int TH, int U, int CP, bool ALIGNED, bool FULL>
+__device__ __forceinline__ void reduce_tile(const CollDesc& d, const TileRef& t, u32x4 (&r)[U]) {
+  u32x4 a[U], b[U];
+  UnitAcc<T> acc[U];
+  reduce_load<TH, U, CP, ALIGNED, FULL>(d, t, 0, a);
+  if constexpr (N > 1) reduce_load<TH, U, CP, ALIGNED, FULL>(d, t, 1, b);
+#pragma unroll
+  for (int u = 0; u < U; ++u) acc[u].set(a[u]);
+  int k = 1;  // next source to add; it is in b
+#pragma unroll 1
+  for (; k + 1 < N; k += 2) {
+    reduce_load<TH, U, CP, ALIGNED, FULL>(d, t, k + 1, a);
+    __builtin_amdgcn_sched_barrier(0);  // issue these loads before waiting on b
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc[u].add(b[u]);
+    if (k + 2 < N) reduce_load<TH, U, CP, ALIGNED, FULL>(d, t, k + 2, b);
+    __builtin_amdgcn_sched_barrier(0);  // ... and these before waiting on a
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc[u].add(a[u]);
+  }
+  if (k < N) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc[u].add(b[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) r[u] = acc[u].out();
+}
+
+// -------------------------------------------------------------- copy tiles
+
+__device__ inline void copy_edges(const CollDesc& d, const JobL& J, uint32_t head, uint64_t body) {
+  const uint32_t ne = head + (uint32_t)(J.bytes - head - body);
+  for (uint32_t t = threadIdx.x; t < ne; t += blockDim.x) {
+    const uint64_t off = t < head ? (uint64_t)t : (uint64_t)head + body + (t - head);
+    const uint8_t b = *(static_cast<const uint8_t*>(d.src[J.src_rank]) + J.src_off + off);
+    if (J.dst_rank >= 0) {
+      *(static_cast<uint8_t*>(d.dst[J.dst_rank]) + J.dst_off + off) = b;
+    } else {
+      for (int k = 0; k < d.ndst; ++k) *(static_cast<uint8_t*>(d.dst[k]) + J.dst_off + off) = b;
+    }
+  }
+}
+
+template <int TH, int U, int CP, bool ALIGNED>
+__device__ __forceinline__ void copy_load(const CollDesc& d, const TileRef& t, u32x4 (&v)[U]) {
+  const char* sp = static_cast<const char*>(d.src[t.J.src_rank]) + t.J.src_off + t.toff;
+  const uint32_t lane = threadIdx.x * 16u;
+  if constexpr (ALIGNED) {  // units at or past rem read as zero (never stored)
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(sp, t.rem);
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = bld16<CP>(r, lane + (uint32_t)u * TH * 16u);
+    return;
+  }
+  const uint32_t m = uniform((uint32_t)(uintptr_t)sp & 3u);
+  if (t.rem == (uint32_t)TH * 16u * U) {  // full tile: no per-unit guards
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = ld16_any<CP>(sp + lane + (uint32_t)u * TH * 16u, m);
+    return;
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t o = lane + (uint32_t)u * TH * 16u;
+    if (o < t.rem) v[u] = ld16_any<CP>(sp + o, m);
+  }
+}
+
+// ----------------------------------------------------------- tile loops
+//
+// run_reduce / run_copy: this workgroup's share (tiles block, block +
+// blocks, ...) of a reduce or copy collective.  blockDim.x must equal TH.
+// Every thread of the workgroup calls them; they return once the share is
+// stored (not yet visible to other workgroups: see group_barrier).
+
+template <int N, typename T, int TH, int CP, bool ALIGNED>
+__device__ void run_reduce(const CollDesc& d, uint32_t block, uint32_t blocks) {
+  constexpr int U = tile_units<TH>();
+  constexpr uint32_t TILE = kTileBytes;
+  // edge elements (head < 128 bytes, tail < 16) and jobs are looped over
+  __shared__ JobL jobs[kMaxRanks];
+  __shared__ uint32_t scan[TH];
+  int nj;
+  const uint32_t total = build_table<TH, kMaxRanks, ALIGNED>(d, TILE, jobs, scan, nj);
+  uint32_t tile = block;
+  if (tile >= total) return;
+  const uint32_t lane = threadIdx.x * 16u;
+  JobCursor<TILE, ALIGNED> jc;
+  jc.init(jobs, nj, tile);
+  for (; tile < total; tile += blocks) {
+    const TileRef t = jc.at(tile);
+    u32x4 r[U];
+    if (ALIGNED || t.rem == TILE)
+      reduce_tile<N, T, TH, U, CP, ALIGNED, true>(d, t, r);
+    else
+      reduce_tile<N, T, TH, U, CP, ALIGNED, false>(d, t, r);
+    if constexpr (!ALIGNED) {
+      if (t.lt == 0) reduce_edges<T, N>(d, t.J, t.head, t.body);
+    }
+    store_units<TH, U, CP, N, ALIGNED>(d, t.J.dst_rank, t.J.dst_off + t.toff, lane, t.rem, r);
+  }
+}
+
+template <int TH, int CP, bool ALIGNED>
+__device__ void run_copy(const CollDesc& d, uint32_t block, uint32_t blocks) {
+  constexpr int U = tile_units<TH>();
+  constexpr uint32_t TILE = kTileBytes;
+  __shared__ JobL jobs[kMaxJobs];
+  __shared__ uint32_t scan[TH];
+  int nj;
+  const uint32_t total = build_table<TH, kMaxJobs, ALIGNED>(d, TILE, jobs, scan, nj);
+  uint32_t tile = block;
+  if (tile >= total) return;
+  const uint32_t lane = threadIdx.x * 16u;
+  JobCursor<TILE, ALIGNED> jc;
+  jc.init(jobs, nj, tile);
+  for (; tile < total; tile += blocks) {
+    const TileRef cur = jc.at(tile);
+    u32x4 v[U];
+    copy_load<TH, U, CP, ALIGNED>(d, cur, v);
+    if constexpr (!ALIGNED) {
+      if (cur.lt == 0) copy_edges(d, cur.J, cur.head, cur.body);
+    }
+    store_units<TH, U, CP, 0, ALIGNED>(d, cur.J.dst_rank, cur.J.dst_off + cur.toff, lane, cur.rem, v);
+  }
+}
+
+// ================================================ device-side collectives
+
+// Run the collective of `desc` (from snac_describe) inside the caller's
+// kernel.  Exactly `blocks` workgroups of TH threads call it, each with its
+// own `block` in [0, blocks); workgroups block < coll_blocks move the data
+// (tiles shared round-robin), the others only wait for it.  When it returns
+// true in a workgroup, the whole collective's output is stored and visible
+// to that workgroup.  It returns false (in every participant) on timeout or
+// abort, with the status word latched for snac_check().
+//
+// T and N must match desc.esize and desc.nsrc for reduce collectives
+// (AllReduce, ReduceScatter, ReduceScatterV); copy collectives ignore them.
+// On a mismatch nothing is moved and SNAC_E_ARG latches.  The `blocks`
+// workgroups must be co-resident; the context's barrier serves one group at
+// a time.
+template <typename T = F32, int N = 1, int TH = 256, int CP = kCacheStream>
+__device__ bool collective(const CollDesc& desc, const snac_dev_ctx& ctx, uint32_t block, uint32_t blocks,
+                           uint32_t coll_blocks) {
+  const bool reduce = coll_is_reduce(desc.coll);
+  const bool aligned = desc_aligned(desc);
+  bool good = true;
+  if (reduce && (desc.nsrc != N || desc.esize != T::kSize)) good = false;
+  if (coll_blocks == 0 || coll_blocks > blocks) good = false;
+  if (!good) {
+    if (block == 0 && threadIdx.x == 0) latch_status(ctx.status, SNAC_E_ARG);
+  } else if (block < coll_blocks) {
+    if (reduce) {
+      if (aligned)
+        run_reduce<N, T, TH, CP, true>(desc, block, coll_blocks);
+      else
+        run_reduce<N, T, TH, CP, false>(desc, block, coll_blocks);
+    } else {
+      if (aligned)
+        run_copy<TH, CP, true>(desc, block, coll_blocks);
+      else
+        run_copy<TH, CP, false>(desc, block, coll_blocks);
+    }
+  }
+  const bool met = group_barrier(ctx, blocks);
+  return good && met;
+}
+
+}  // namespace snac

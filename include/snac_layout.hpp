@@ -1,12 +1,12 @@
-// layout.hpp -- the layout engine: a collective -> a list of copy or reduce
-// jobs over byte ranges.
+// snac_layout.hpp -- the layout engine: a collective -> a list of copy or
+// reduce jobs over byte ranges.
 //
 // "Layouts describe the collective: how inputs and outputs are distributed,
 // and whether to copy or reduce" (Purlin 0.6.4 project description, "Key
 // Idea").  The same functions run on the host (snac_plan, argument checks)
 // and in every workgroup of a collective kernel, which rebuilds the job table
-// in LDS from the compact descriptor passed as a kernel argument -- so no
-// per-call host-to-device copy is needed.
+// in LDS from the compact descriptor (snac_coll_desc, include/snac.h) passed
+// as a kernel argument -- so no per-call host-to-device copy is needed.
 //
 // Per-collective layouts (N ranks, B per-rank input bytes, e element size,
 // D(c) exclusive prefix sum of counts, every offset in bytes):
@@ -26,6 +26,8 @@
 
 #include <stdint.h>
 
+#include "snac.h"
+
 #if defined(__HIPCC__)
 #define SNAC_HD __host__ __device__ inline
 #else
@@ -34,7 +36,7 @@
 
 namespace snac {
 
-constexpr int kMaxRanks = 16;
+constexpr int kMaxRanks = SNAC_MAX_RANKS;
 constexpr int kMaxJobs = kMaxRanks * kMaxRanks;
 
 // Collective kinds: the public snac_coll values, plus the two raw Atoms.
@@ -55,18 +57,9 @@ SNAC_HD bool coll_is_reduce(int32_t c) {
 }
 
 // Compact description of one collective call; passed by value to kernels.
-struct CollDesc {
-  int32_t coll;
-  int32_t nsrc;             // source buffers (= N for collectives)
-  int32_t ndst;             // destination buffers (= N for collectives)
-  int32_t esize;            // element size in bytes
-  int32_t split_multicast;  // see above
-  int32_t pad_;
-  uint64_t bytes;           // per-rank input bytes (fixed-size collectives, Atoms)
-  const void* src[kMaxRanks];
-  void* dst[kMaxRanks];
-  uint64_t counts[kMaxJobs];  // V collectives: element counts
-};
+using CollDesc = snac_coll_desc;
+
+SNAC_HD bool desc_aligned(const CollDesc& d) { return (d.flags & SNAC_DESC_ALIGNED) != 0; }
 
 struct Job {
   uint64_t src_off;

@@ -1,0 +1,196 @@
+// devapi_kernels.hip -- kernels that use the device-side API of
+// include/snac_device.hpp the way a user's kernel would, with plain C
+// launchers for the GPU tests (tests/test_gpu_device_api.py).  Test
+// infrastructure: built into tests/devapi/libsnac_devtest.so.
+//
+// Every launcher checks its grid against what the device can run at once
+// (the device-side collective and group barrier need co-resident
+// workgroups) and returns a hipError_t (or -1 for that check).
+#include <hip/hip_runtime.h>
+
+#include "snac_device.hpp"
+
+namespace {
+
+constexpr int TH = 256;
+
+int fits(const void* fn, int grid) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, TH, 0) != hipSuccess) return 0;
+  return grid <= per_cu * cus;
+}
+
+// ---- workgroup Atoms: block b handles slice b (the copy sample's shape)
+
+__global__ __launch_bounds__(TH) void copy_slices_kernel(char* dst, const char* src, uint64_t bytes_per_block) {
+  const uint64_t off = (uint64_t)blockIdx.x * bytes_per_block;
+  snac::copy(dst + off, src + off, bytes_per_block);
+}
+
+template <typename T, int N>
+__global__ __launch_bounds__(TH) void reduce_slices_kernel(snac_coll_desc bufs, uint64_t count_per_block) {
+  // bufs.src / bufs.dst carry the pointers; nothing else of it is used
+  const uint64_t off = (uint64_t)blockIdx.x * count_per_block * T::kSize;
+  const void* src[N];
+  void* dst[SNAC_MAX_RANKS];
+#pragma unroll
+  for (int k = 0; k < N; ++k) src[k] = static_cast<const char*>(bufs.src[k]) + off;
+  for (int k = 0; k < bufs.ndst; ++k) dst[k] = static_cast<char*>(bufs.dst[k]) + off;
+  snac::reduce<T, N>(dst, bufs.ndst, src, count_per_block);
+}
+
+// ---- a described collective run by workgroups [0, blocks) of a larger grid
+
+template <typename T, int N>
+__global__ __launch_bounds__(TH) void collective_kernel(const snac_coll_desc desc, const snac_dev_ctx ctx,
+                                                        uint32_t blocks, uint32_t coll_blocks, uint32_t* ok_out) {
+  if (blockIdx.x >= blocks) return;  // workgroups doing "other work"
+  const bool ok = snac::collective<T, N, TH>(desc, ctx, blockIdx.x, blocks, coll_blocks);
+  if (threadIdx.x == 0) ok_out[blockIdx.x] = ok ? 1u : 0u;
+}
+
+// ---- compute, in-kernel AllReduce, compute on the result
+//
+// Phase 1: every workgroup computes y_r = 0.5 * x_r + r (binary32, rounded
+// to T) for its slice of every rank into tmp[r]; all workgroups meet.
+// Phase 2: AllReduce tmp -> out inside the kernel (desc describes it).
+// Phase 3: every workgroup copies a slice of out[0] -- written by other
+// workgroups in phase 2 -- into check.
+
+template <typename T>
+__device__ void scale_slice(const char* x, char* y, uint64_t first, uint64_t n, float r) {
+  for (uint64_t i = first + threadIdx.x; i < first + n; i += TH)
+    snac::store_elem<T>(y + i * T::kSize, snac::load_elem<T>(x + i * T::kSize) * 0.5f + r);
+}
+
+template <typename T, int N>
+__global__ __launch_bounds__(TH) void fused_kernel(const snac_coll_desc desc, const snac_dev_ctx ctx,
+                                                   snac_coll_desc xs, uint64_t count, char* check,
+                                                   uint32_t* ok_out) {
+  const uint32_t blocks = gridDim.x;
+  const uint64_t per = (count + blocks - 1) / blocks;
+  const uint64_t first = (uint64_t)blockIdx.x * per;
+  const uint64_t n = first >= count ? 0 : (count - first < per ? count - first : per);
+  for (int r = 0; r < N; ++r)
+    scale_slice<T>(static_cast<const char*>(xs.src[r]), static_cast<char*>(const_cast<void*>(desc.src[r])), first, n,
+                   (float)r);
+  bool ok = snac::group_barrier(ctx, blocks);
+  if (ok) ok = snac::collective<T, N, TH>(desc, ctx, blockIdx.x, blocks, blocks);
+  if (ok) {
+    // read another workgroup's part of the result: slice (b + 1) mod blocks
+    const uint32_t other = (blockIdx.x + 1) % blocks;
+    const uint64_t f2 = (uint64_t)other * per;
+    const uint64_t n2 = f2 >= count ? 0 : (count - f2 < per ? count - f2 : per);
+    snac::copy(check + f2 * T::kSize, static_cast<const char*>(desc.dst[0]) + f2 * T::kSize, n2 * T::kSize);
+  }
+  if (threadIdx.x == 0) ok_out[blockIdx.x] = ok ? 1u : 0u;
+}
+
+// N dispatch tables (N in {1, 2, 3, 4, 8, 16})
+#define SNAC_DISPATCH_N(MACRO) MACRO(1) MACRO(2) MACRO(3) MACRO(4) MACRO(8) MACRO(16)
+
+}  // namespace
+
+extern "C" {
+
+int devtest_copy_slices(void* dst, const void* src, uint64_t bytes_per_block, int blocks, hipStream_t s) {
+  if (blocks <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(copy_slices_kernel, dim3(blocks), dim3(TH), 0, s, static_cast<char*>(dst),
+                     static_cast<const char*>(src), bytes_per_block);
+  return hipGetLastError();
+}
+
+// bufs: ndst and src[0..nsrc) / dst[0..ndst) set by the caller
+int devtest_reduce_slices(const snac_coll_desc* bufs, int nsrc, uint64_t count_per_block, int blocks, int bf16,
+                          hipStream_t s) {
+  if (blocks <= 0 || !bufs || bufs->ndst < 1 || bufs->ndst > SNAC_MAX_RANKS) return hipErrorInvalidValue;
+#define SNAC_CASE(NN)                                                                                         \
+  case NN:                                                                                                    \
+    if (bf16)                                                                                                 \
+      hipLaunchKernelGGL((reduce_slices_kernel<snac::BF16, NN>), dim3(blocks), dim3(TH), 0, s, *bufs,         \
+                         count_per_block);                                                                    \
+    else                                                                                                      \
+      hipLaunchKernelGGL((reduce_slices_kernel<snac::F32, NN>), dim3(blocks), dim3(TH), 0, s, *bufs,          \
+                         count_per_block);                                                                    \
+    break;
+  switch (nsrc) {
+    SNAC_DISPATCH_N(SNAC_CASE)
+    default: return hipErrorInvalidValue;
+  }
+#undef SNAC_CASE
+  return hipGetLastError();
+}
+
+// Runs `desc` with workgroups [0, blocks) of a grid of blocks + extra;
+// template arguments from (bf16, nsrc) -- deliberately taken from the
+// caller, so a test can pass a mismatch.  ok_out[b] = 1 where it returned
+// true.
+int devtest_collective(const snac_coll_desc* desc, const snac_dev_ctx* ctx, int bf16, int nsrc, int blocks,
+                       int coll_blocks, int extra, uint32_t* ok_out, hipStream_t s) {
+  if (!desc || !ctx || blocks <= 0 || coll_blocks < 0 || extra < 0) return hipErrorInvalidValue;
+  const int grid = blocks + extra;
+  const void* fn = nullptr;
+#define SNAC_CASE(NN)                                                                                           \
+  case NN:                                                                                                      \
+    fn = bf16 ? (const void*)&collective_kernel<snac::BF16, NN> : (const void*)&collective_kernel<snac::F32, NN>; \
+    break;
+  switch (nsrc) {
+    SNAC_DISPATCH_N(SNAC_CASE)
+    default: return hipErrorInvalidValue;
+  }
+#undef SNAC_CASE
+  if (!fits(fn, grid)) return -1;
+#define SNAC_CASE(NN)                                                                                      \
+  case NN:                                                                                                 \
+    if (bf16)                                                                                              \
+      hipLaunchKernelGGL((collective_kernel<snac::BF16, NN>), dim3(grid), dim3(TH), 0, s, *desc, *ctx,     \
+                         (uint32_t)blocks, (uint32_t)coll_blocks, ok_out);                                 \
+    else                                                                                                   \
+      hipLaunchKernelGGL((collective_kernel<snac::F32, NN>), dim3(grid), dim3(TH), 0, s, *desc, *ctx,      \
+                         (uint32_t)blocks, (uint32_t)coll_blocks, ok_out);                                 \
+    break;
+  switch (nsrc) {
+    SNAC_DISPATCH_N(SNAC_CASE)
+    default: return hipErrorInvalidValue;
+  }
+#undef SNAC_CASE
+  return hipGetLastError();
+}
+
+// desc: AllReduce tmp -> out (snac_describe); xs.src[r]: the inputs x_r.
+int devtest_fused_scale_allreduce(const snac_coll_desc* desc, const snac_dev_ctx* ctx, const snac_coll_desc* xs,
+                                  uint64_t count, void* check, int blocks, uint32_t* ok_out, hipStream_t s) {
+  if (!desc || !ctx || !xs || blocks <= 0) return hipErrorInvalidValue;
+  const int n = desc->nsrc;
+  const bool bf16 = desc->esize == 2;
+  const void* fn = nullptr;
+#define SNAC_CASE(NN)                                                                                  \
+  case NN:                                                                                             \
+    fn = bf16 ? (const void*)&fused_kernel<snac::BF16, NN> : (const void*)&fused_kernel<snac::F32, NN>; \
+    break;
+  switch (n) {
+    SNAC_DISPATCH_N(SNAC_CASE)
+    default: return hipErrorInvalidValue;
+  }
+#undef SNAC_CASE
+  if (!fits(fn, blocks)) return -1;
+#define SNAC_CASE(NN)                                                                                          \
+  case NN:                                                                                                     \
+    if (bf16)                                                                                                  \
+      hipLaunchKernelGGL((fused_kernel<snac::BF16, NN>), dim3(blocks), dim3(TH), 0, s, *desc, *ctx, *xs, count, \
+                         static_cast<char*>(check), ok_out);                                                   \
+    else                                                                                                       \
+      hipLaunchKernelGGL((fused_kernel<snac::F32, NN>), dim3(blocks), dim3(TH), 0, s, *desc, *ctx, *xs, count,  \
+                         static_cast<char*>(check), ok_out);                                                   \
+    break;
+  switch (n) {
+    SNAC_DISPATCH_N(SNAC_CASE)
+    default: return hipErrorInvalidValue;
+  }
+#undef SNAC_CASE
+  return hipGetLastError();
+}
+
+}  // extern "C"

@@ -45,7 +45,7 @@ def test_nm_shows_c_linkage():
 
 
 def test_versions_and_status_strings():
-    assert snac.snac_abi_version() == 1
+    assert snac.snac_abi_version() == 2
     for s in range(8):
         assert snac.snac_status_str(s).startswith("SNAC_")
     assert "unknown" in snac.snac_status_str(99)
@@ -188,3 +188,42 @@ def test_plan_rejects_bad_requests():
     # more jobs than room
     with pytest.raises(snac.SnacError):
         snac.snac_plan(snac.SNAC_COLL_ALL_TO_ALL, 4, "f32", 64, max_jobs=3)
+
+
+# ------------------------------------------------------- device-side API
+def test_device_api_argument_errors_without_gpu():
+    E = snac.SNAC_E_ARG
+    _expect(E, snac.snac_get_device_context, None)
+    _expect(E, snac.snac_describe, None, snac.SNAC_COLL_ALL_REDUCE, [0x1000], [0x2000], 16, None, "f32")
+
+
+def _c_layout(struct: str, fields: list[str]) -> list[int]:
+    """sizeof and offsetof of a snac.h struct as the C compiler lays it out."""
+    import subprocess
+    import tempfile
+
+    body = "\n".join(f'  printf("%zu\\n", offsetof({struct}, {f}));' for f in fields)
+    src = f'#include <stddef.h>\n#include <stdio.h>\n#include "snac.h"\nint main(void) {{\n' \
+          f'  printf("%zu\\n", sizeof({struct}));\n{body}\n  return 0;\n}}\n'
+    with tempfile.TemporaryDirectory() as d:
+        c, exe = os.path.join(d, "l.c"), os.path.join(d, "l")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), c, "-o", exe], check=True)
+        return [int(x) for x in subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()]
+
+
+@pytest.mark.parametrize("cls", [snac.snac_dev_ctx, snac.snac_coll_desc, snac.snac_tuning, snac.snac_job])
+def test_binding_structs_match_c_layout(cls):
+    names = [n for n, _ in cls._fields_]
+    got = _c_layout(cls.__name__, names)
+    assert got[0] == ctypes.sizeof(cls)
+    for n, off in zip(names, got[1:]):
+        assert getattr(cls, n).offset == off, n
+    if cls is snac.snac_coll_desc:
+        assert ctypes.sizeof(cls) == 2336  # as documented in snac.h
+
+
+def test_devtest_fixture_exports_its_launchers():
+    lib = ctypes.CDLL(os.path.join(ROOT, "tests", "devapi", "libsnac_devtest.so"))
+    for n in ("devtest_copy_slices", "devtest_reduce_slices", "devtest_collective", "devtest_fused_scale_allreduce"):
+        assert hasattr(lib, n)
