@@ -60,7 +60,23 @@ class snac_tuning(ctypes.Structure):
     ]
 
 
+SNAC_RULE_ANY, SNAC_RULE_ANY_REDUCE, SNAC_RULE_ANY_COPY = -1, -2, -3
+SNAC_RULE_ATOM_COPY, SNAC_RULE_ATOM_REDUCE, SNAC_RULE_PIPELINE = 100, 101, 200
+SNAC_MAX_TUNING_RULES = 256
 SNAC_MAX_COUNTS = SNAC_MAX_RANKS * SNAC_MAX_RANKS
+
+
+class snac_tuning_rule(ctypes.Structure):
+    _fields_ = [
+        ("coll", ctypes.c_int32),
+        ("min_ranks", ctypes.c_int32),
+        ("max_ranks", ctypes.c_int32),
+        ("esize", ctypes.c_int32),
+        ("min_bytes", ctypes.c_uint64),
+        ("max_bytes", ctypes.c_uint64),
+        ("wgs_per_cu", ctypes.c_int32),
+        ("cache_policy", ctypes.c_int32),
+    ]
 SNAC_DESC_ALIGNED = 1
 SNAC_FLAG_STRIDE = 16
 
@@ -124,6 +140,9 @@ _SIGS = {
     "snac_get_device_context": (_I, [_VP, ctypes.POINTER(snac_dev_ctx)]),
     "snac_describe": (_I, [_VP, _I, ctypes.POINTER(_VP), ctypes.POINTER(_VP), _SZ, ctypes.POINTER(_SZ), _I,
                            ctypes.POINTER(snac_coll_desc)]),
+    "snac_set_tuning_rules": (_I, [ctypes.POINTER(snac_tuning_rule), _I]),
+    "snac_get_tuning_rules": (_I, [ctypes.POINTER(snac_tuning_rule), _I, ctypes.POINTER(_I)]),
+    "snac_tuning_lookup": (_I, [ctypes.c_int32, _I, _I, _SZ, ctypes.POINTER(snac_tuning)]),
     "snac_get_tuning": (_I, [ctypes.POINTER(snac_tuning)]),
     "snac_set_tuning": (_I, [ctypes.POINTER(snac_tuning)]),
 }
@@ -325,3 +344,33 @@ def snac_set_tuning(**kw) -> None:
     cur.update(kw)
     t = snac_tuning(**{k: int(v) for k, v in cur.items()})
     _check(lib().snac_set_tuning(ctypes.byref(t)), "snac_set_tuning")
+
+
+_RULE_FIELDS = [n for n, _ in snac_tuning_rule._fields_]
+
+
+def snac_set_tuning_rules(rules: Sequence[dict] | None) -> None:
+    """Install a rule table (dicts with the snac_tuning_rule field names);
+    None or [] restores the built-in table."""
+    rules = list(rules or [])
+    arr = (snac_tuning_rule * max(1, len(rules)))()
+    for i, r in enumerate(rules):
+        for k, v in r.items():
+            if k not in _RULE_FIELDS:
+                raise KeyError(f"unknown rule field {k}")
+            setattr(arr[i], k, int(v))
+    _check(lib().snac_set_tuning_rules(arr if rules else None, len(rules)), "snac_set_tuning_rules")
+
+
+def snac_get_tuning_rules() -> list[dict]:
+    n = _I()
+    _check(lib().snac_get_tuning_rules(None, 0, ctypes.byref(n)), "snac_get_tuning_rules")
+    arr = (snac_tuning_rule * max(1, n.value))()
+    _check(lib().snac_get_tuning_rules(arr, n.value, ctypes.byref(n)), "snac_get_tuning_rules")
+    return [{k: getattr(arr[i], k) for k in _RULE_FIELDS} for i in range(n.value)]
+
+
+def snac_tuning_lookup(coll: int, nranks: int, esize: int, nbytes: int) -> dict:
+    t = snac_tuning()
+    _check(lib().snac_tuning_lookup(coll, nranks, esize, nbytes, ctypes.byref(t)), "snac_tuning_lookup")
+    return {name: getattr(t, name) for name, _ in snac_tuning._fields_ if name != "reserved"}

@@ -4,6 +4,8 @@
 
 #include <algorithm>
 #include <cstdarg>
+#include <iterator>
+#include <vector>
 #include <cstdio>
 #include <cstring>
 #include <new>
@@ -67,7 +69,54 @@ constexpr uint32_t kMinSplitTile = 65536u;  // ... but no smaller tiles than thi
 constexpr size_t kDefaultStaging = 64u * 1024u * 1024u;
 constexpr int kDefaultSpinLog2 = 22;
 
-LaunchCfg launch_cfg() { return LaunchCfg{g_tuning.wgs_per_cu, g_tuning.cache_policy}; }
+// ---- tuning rules
+
+// Built-in rules, measured on MI355X: reduces of 4 or more sources run one
+// workgroup per CU (more concurrent write streams lower HBM efficiency),
+// smaller reduces and copies two; streaming (non-temporal) accesses
+// throughout; the pipeline picks its own grid (4 per CU when the ring
+// holds the message, else 2).
+const snac_tuning_rule kBuiltinRules[] = {
+    {SNAC_RULE_ANY_REDUCE, 4, SNAC_MAX_RANKS, 0, 0, UINT64_MAX, 1, 1},
+    {SNAC_RULE_ANY_REDUCE, 1, 3, 0, 0, UINT64_MAX, 2, 1},
+    {SNAC_RULE_ANY_COPY, 1, SNAC_MAX_RANKS, 0, 0, UINT64_MAX, 2, 1},
+};
+
+std::vector<snac_tuning_rule> g_rules(std::begin(kBuiltinRules), std::end(kBuiltinRules));
+
+bool rule_matches(const snac_tuning_rule& r, int32_t coll, int nsrc, int esize, uint64_t bytes) {
+  bool c = false;
+  if (r.coll == SNAC_RULE_ANY) c = true;
+  else if (r.coll == SNAC_RULE_ANY_REDUCE) c = coll != SNAC_RULE_PIPELINE && coll_is_reduce(coll);
+  else if (r.coll == SNAC_RULE_ANY_COPY) c = coll != SNAC_RULE_PIPELINE && !coll_is_reduce(coll);
+  else c = r.coll == coll;
+  return c && nsrc >= r.min_ranks && nsrc <= r.max_ranks && (r.esize == 0 || r.esize == esize) &&
+         bytes >= r.min_bytes && bytes <= r.max_bytes;
+}
+
+// Launch parameters of a call: the first matching rule, then the explicit
+// process-wide values on top.
+LaunchCfg launch_cfg(int32_t coll, int nsrc, int esize, uint64_t bytes) {
+  LaunchCfg c{0, 0};
+  for (const snac_tuning_rule& r : g_rules) {
+    if (rule_matches(r, coll, nsrc, esize, bytes)) {
+      c = LaunchCfg{r.wgs_per_cu, r.cache_policy};
+      break;
+    }
+  }
+  if (g_tuning.wgs_per_cu) c.wgs_per_cu = g_tuning.wgs_per_cu;
+  if (g_tuning.cache_policy) c.cache_policy = g_tuning.cache_policy;
+  return c;
+}
+
+bool rule_ok(const snac_tuning_rule& r) {
+  const bool coll_ok = r.coll == SNAC_RULE_ANY || r.coll == SNAC_RULE_ANY_REDUCE || r.coll == SNAC_RULE_ANY_COPY ||
+                       (r.coll >= 0 && r.coll <= 6) || r.coll == SNAC_RULE_ATOM_COPY ||
+                       r.coll == SNAC_RULE_ATOM_REDUCE || r.coll == SNAC_RULE_PIPELINE;
+  return coll_ok && r.min_ranks >= 1 && r.min_ranks <= r.max_ranks && r.max_ranks <= SNAC_MAX_RANKS &&
+         (r.esize == 0 || r.esize == 1 || r.esize == 2 || r.esize == 4) && r.min_bytes <= r.max_bytes &&
+         r.wgs_per_cu >= 0 && r.wgs_per_cu <= 32 && r.cache_policy >= 0 && r.cache_policy <= 4;
+}
 
 int esize_of(snac_dtype t) {
   switch (t) {
@@ -92,6 +141,7 @@ struct Plan {
   CollDesc d;
   bool aligned;
   uint64_t tiles;
+  uint64_t rule_bytes;  // per-rank input bytes the tuning rules match on
 };
 
 // Host copy of the layout: total tiles and the aligned flag.
@@ -191,7 +241,8 @@ snac_status run(Plan& p, hipStream_t stream) {
     return ok();
   }
   if (p.tiles == 0) return ok();
-  hipError_t e = launch_collective(p.d, p.aligned, p.tiles, launch_cfg(), stream);
+  hipError_t e = launch_collective(p.d, p.aligned, p.tiles, launch_cfg(p.d.coll, p.d.nsrc, p.d.esize, p.rule_bytes),
+                                   stream);
   if (e != hipSuccess) return hip_fail(e, "collective launch");
   return ok();
 }
@@ -247,6 +298,7 @@ snac_status fixed_collective(int32_t coll, snac_ctx* ctx, const void* const* src
   if (st != SNAC_OK) return st;
   Plan p = base_plan(coll, n, n, e);
   p.d.bytes = bytes;
+  p.rule_bytes = bytes;
   for (int i = 0; i < n; ++i) {
     p.d.src[i] = src[i];
     p.d.dst[i] = dst[i];
@@ -297,6 +349,7 @@ snac_status v_collective(int32_t coll, snac_ctx* ctx, const void* const* src, vo
   for (int i = 0; i < n; ++i) {
     p.d.src[i] = src[i];
     p.d.dst[i] = dst[i];
+    p.rule_bytes = std::max<uint64_t>(p.rule_bytes, in_b[i]);
   }
   for (int i = 0; i < nc; ++i) p.d.counts[i] = counts[i];
   if (coll == kAllGatherV) p.d.split_multicast = split_copy(dst, n);
@@ -458,6 +511,7 @@ snac_status snac_copy(void* dst, const void* src, size_t bytes, snac_stream stre
   if (overlaps(a, b)) return fail(SNAC_E_ARG, "src and dst overlap");
   Plan p = base_plan(kAtomCopy, 1, 1, 1);
   p.d.bytes = bytes;
+  p.rule_bytes = bytes;
   p.d.src[0] = src;
   p.d.dst[0] = dst;
   return run(p, (hipStream_t)stream);
@@ -480,6 +534,7 @@ snac_status snac_reduce_n(void* const* dst, int ndst, const void* const* src, in
   if (st != SNAC_OK) return st;
   Plan p = base_plan(kAtomReduce, nsrc, ndst, e);
   p.d.bytes = bytes;
+  p.rule_bytes = bytes;
   for (int i = 0; i < nsrc; ++i) p.d.src[i] = src[i];
   for (int i = 0; i < ndst; ++i) p.d.dst[i] = dst[i];
   p.d.split_multicast = needs_split(dst, ndst);
@@ -569,8 +624,40 @@ snac_status snac_pipeline_scale_reduce(snac_ctx* ctx, const void* const* x, void
   a.lookahead = (uint32_t)g_tuning.pipeline_lookahead;
   a.spin_limit_log2 = (uint32_t)(g_tuning.spin_limit_log2 ? g_tuning.spin_limit_log2 : kDefaultSpinLog2);
   a.drop_notify = g_tuning.debug_drop_notify;
-  hipError_t err = launch_pipeline(a, dtype == SNAC_BF16, launch_cfg(), (hipStream_t)stream, nullptr);
+  hipError_t err = launch_pipeline(a, dtype == SNAC_BF16, launch_cfg(SNAC_RULE_PIPELINE, n, e, count * (uint64_t)e),
+                                   (hipStream_t)stream, nullptr);
   if (err != hipSuccess) return hip_fail(err, "pipeline launch");
+  return ok();
+}
+
+snac_status snac_set_tuning_rules(const snac_tuning_rule* rules, int n) {
+  if (n < 0 || n > SNAC_MAX_TUNING_RULES) return fail(SNAC_E_ARG, "rule count %d outside 0..%d", n, SNAC_MAX_TUNING_RULES);
+  if (n > 0 && !rules) return fail(SNAC_E_ARG, "rules is NULL");
+  for (int i = 0; i < n; ++i)
+    if (!rule_ok(rules[i])) return fail(SNAC_E_ARG, "rule %d is invalid", i);
+  if (n == 0)
+    g_rules.assign(std::begin(kBuiltinRules), std::end(kBuiltinRules));
+  else
+    g_rules.assign(rules, rules + n);
+  return ok();
+}
+
+snac_status snac_get_tuning_rules(snac_tuning_rule* out, int max, int* n) {
+  if (!n) return fail(SNAC_E_ARG, "n is NULL");
+  *n = (int)g_rules.size();
+  if (!out) return ok();
+  if (max < (int)g_rules.size()) return fail(SNAC_E_ARG, "max (%d) is smaller than the table (%d rules)", max, *n);
+  std::copy(g_rules.begin(), g_rules.end(), out);
+  return ok();
+}
+
+snac_status snac_tuning_lookup(int32_t coll, int nranks, int esize, size_t bytes, snac_tuning* out) {
+  if (!out) return fail(SNAC_E_ARG, "out is NULL");
+  if (nranks < 1 || nranks > SNAC_MAX_RANKS) return fail(SNAC_E_ARG, "nranks %d outside 1..%d", nranks, SNAC_MAX_RANKS);
+  const LaunchCfg c = launch_cfg(coll, nranks, esize, bytes);
+  *out = g_tuning;
+  out->wgs_per_cu = c.wgs_per_cu;
+  out->cache_policy = c.cache_policy;
   return ok();
 }
 

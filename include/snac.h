@@ -399,6 +399,66 @@ typedef struct snac_tuning {
 snac_status snac_get_tuning(snac_tuning* out);
 snac_status snac_set_tuning(const snac_tuning* in);
 
+/*
+ * Tuning rules: launch parameters keyed by collective, source count,
+ * element size and per-rank size, so that each regime runs with the launch
+ * shape measured best for it (Purlin 0.6.4 "Key Idea": extensive tuning for
+ * peak performance; Purlin 0.6.5 "Device-side": tuning policies).
+ *
+ * A call takes the first rule that matches it; a non-zero wgs_per_cu or
+ * cache_policy in the process-wide snac_tuning overrides the rule.  Rule
+ * fields that are 0 keep the kernel's own default.  The built-in table
+ * (restored by snac_set_tuning_rules(NULL, 0)) encodes the defaults measured
+ * on MI355X; copy_reduce_snac_amd/autotune.py measures and installs a table
+ * for the GPU at hand.
+ *
+ * Matching:
+ *   coll                a snac_coll value, SNAC_RULE_ATOM_COPY (snac_copy),
+ *                       SNAC_RULE_ATOM_REDUCE (snac_reduce_n),
+ *                       SNAC_RULE_PIPELINE (snac_pipeline_scale_reduce),
+ *                       SNAC_RULE_ANY_REDUCE (every reduce: AllReduce,
+ *                       ReduceScatter(V), reduce_n), SNAC_RULE_ANY_COPY
+ *                       (every copy collective and snac_copy), SNAC_RULE_ANY
+ *   min_ranks..max_ranks  source buffers of the call (N; nsrc for reduce_n;
+ *                       1 for snac_copy), inclusive
+ *   esize               element size in bytes, 0 = any
+ *   min_bytes..max_bytes  per-rank input bytes, inclusive (V collectives:
+ *                       the largest per-rank input; the pipeline: count *
+ *                       element size)
+ */
+#define SNAC_RULE_ANY (-1)
+#define SNAC_RULE_ANY_REDUCE (-2)
+#define SNAC_RULE_ANY_COPY (-3)
+#define SNAC_RULE_ATOM_COPY 100
+#define SNAC_RULE_ATOM_REDUCE 101
+#define SNAC_RULE_PIPELINE 200
+#define SNAC_MAX_TUNING_RULES 256
+
+typedef struct snac_tuning_rule {
+  int32_t coll;
+  int32_t min_ranks;
+  int32_t max_ranks;
+  int32_t esize;
+  uint64_t min_bytes;
+  uint64_t max_bytes;
+  int32_t wgs_per_cu;   /* 1..32, or 0 for the kernel's default */
+  int32_t cache_policy; /* as in snac_tuning (1..4), or 0 for the default */
+} snac_tuning_rule;
+
+/* Replace the rule table (rules copied; at most SNAC_MAX_TUNING_RULES).
+ * n == 0 restores the built-in table.  Errors: SNAC_E_ARG (bad field,
+ * min > max, too many rules); the table is unchanged on error. */
+snac_status snac_set_tuning_rules(const snac_tuning_rule* rules, int n);
+
+/* Copy the current table to out[0..max); *n receives its length.  With
+ * out == NULL only *n is set. */
+snac_status snac_get_tuning_rules(snac_tuning_rule* out, int max, int* n);
+
+/* The launch parameters a call would use (host-only, runs no GPU code):
+ * the process-wide tuning with wgs_per_cu and cache_policy resolved
+ * through the rules as described above. */
+snac_status snac_tuning_lookup(int32_t coll, int nranks, int esize, size_t bytes, snac_tuning* out);
+
 #ifdef __cplusplus
 }
 #endif

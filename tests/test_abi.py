@@ -227,3 +227,57 @@ def test_devtest_fixture_exports_its_launchers():
     lib = ctypes.CDLL(os.path.join(ROOT, "tests", "devapi", "libsnac_devtest.so"))
     for n in ("devtest_copy_slices", "devtest_reduce_slices", "devtest_collective", "devtest_fused_scale_allreduce"):
         assert hasattr(lib, n)
+
+
+# ------------------------------------------------------------ tuning rules
+def test_builtin_tuning_rules_and_lookup():
+    snac.snac_set_tuning_rules(None)
+    rules = snac.snac_get_tuning_rules()
+    assert len(rules) >= 3
+    MiB = 1 << 20
+    # measured defaults: big reduces one WG per CU, small reduces and copies two, streaming
+    assert snac.snac_tuning_lookup(snac.SNAC_COLL_ALL_REDUCE, 8, 2, 256 * MiB)["wgs_per_cu"] == 1
+    assert snac.snac_tuning_lookup(snac.SNAC_COLL_REDUCE_SCATTER_V, 4, 4, 1)["wgs_per_cu"] == 1
+    assert snac.snac_tuning_lookup(snac.SNAC_RULE_ATOM_REDUCE, 2, 4, 1)["wgs_per_cu"] == 2
+    assert snac.snac_tuning_lookup(snac.SNAC_COLL_ALL_GATHER, 8, 1, 1)["wgs_per_cu"] == 2
+    assert snac.snac_tuning_lookup(snac.SNAC_RULE_ATOM_COPY, 1, 1, 1)["cache_policy"] == 1
+    # the pipeline picks its own grid
+    assert snac.snac_tuning_lookup(snac.SNAC_RULE_PIPELINE, 8, 2, MiB)["wgs_per_cu"] == 0
+
+
+def test_tuning_rules_first_match_and_override():
+    MiB = 1 << 20
+    try:
+        snac.snac_set_tuning_rules([
+            {"coll": snac.SNAC_COLL_ALL_REDUCE, "min_ranks": 8, "max_ranks": 8, "esize": 2, "min_bytes": 0,
+             "max_bytes": MiB, "wgs_per_cu": 4, "cache_policy": 4},
+            {"coll": snac.SNAC_RULE_ANY_REDUCE, "min_ranks": 1, "max_ranks": 16, "esize": 0, "min_bytes": 0,
+             "max_bytes": 2 ** 64 - 1, "wgs_per_cu": 3, "cache_policy": 2},
+        ])
+        assert len(snac.snac_get_tuning_rules()) == 2
+        t = snac.snac_tuning_lookup(snac.SNAC_COLL_ALL_REDUCE, 8, 2, MiB)
+        assert (t["wgs_per_cu"], t["cache_policy"]) == (4, 4)
+        t = snac.snac_tuning_lookup(snac.SNAC_COLL_ALL_REDUCE, 8, 2, MiB + 1)  # past the first rule's range
+        assert (t["wgs_per_cu"], t["cache_policy"]) == (3, 2)
+        t = snac.snac_tuning_lookup(snac.SNAC_COLL_ALL_REDUCE, 8, 4, 16)  # f32: first rule wants esize 2
+        assert (t["wgs_per_cu"], t["cache_policy"]) == (3, 2)
+        t = snac.snac_tuning_lookup(snac.SNAC_COLL_ALL_TO_ALL, 8, 4, 16)  # no rule: kernel defaults
+        assert (t["wgs_per_cu"], t["cache_policy"]) == (0, 0)
+        snac.snac_set_tuning(wgs_per_cu=5)  # explicit process-wide value wins
+        assert snac.snac_tuning_lookup(snac.SNAC_COLL_ALL_REDUCE, 8, 2, 64)["wgs_per_cu"] == 5
+    finally:
+        snac.snac_set_tuning(wgs_per_cu=0)
+        snac.snac_set_tuning_rules(None)
+    assert len(snac.snac_get_tuning_rules()) >= 3
+
+
+@pytest.mark.parametrize("bad", [
+    {"coll": 7}, {"coll": -4}, {"min_ranks": 0}, {"min_ranks": 5, "max_ranks": 4}, {"max_ranks": 17},
+    {"esize": 3}, {"min_bytes": 10, "max_bytes": 9}, {"wgs_per_cu": 33}, {"cache_policy": 5},
+])
+def test_invalid_tuning_rules_rejected(bad):
+    good = {"coll": -1, "min_ranks": 1, "max_ranks": 16, "esize": 0, "min_bytes": 0, "max_bytes": 100,
+            "wgs_per_cu": 1, "cache_policy": 1}
+    before = snac.snac_get_tuning_rules()
+    _expect(snac.SNAC_E_ARG, snac.snac_set_tuning_rules, [good, {**good, **bad}])
+    assert snac.snac_get_tuning_rules() == before  # unchanged on error
