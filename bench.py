@@ -18,8 +18,9 @@ collectives (ReduceScatter then AllGather, AllToAll / AllToAllV, AllGatherV,
 ReduceScatterV, the SNAC pipeline, and a plain copy) measured the same way.
 
 Other modes:
-    --only NAME     run one workload (allreduce, copy, rs_ag, a2a, a2av, agv,
-                    rsv, pipeline_bf16, pipeline_f32, pipeline_latency) --
+    --only NAME     run one workload (allreduce, allreduce_atomic, copy, rs_ag,
+                    a2a, a2av, agv, rsv, pipeline_bf16, pipeline_f32,
+                    pipeline_latency) --
                     for profiler runs
     --sweep         AllReduce bf16 N=8 over 1 KiB .. 1 GiB per rank (JSON
                     lines to stdout; small sizes batched in a HIP graph)
@@ -164,6 +165,26 @@ def run_allreduce(env: Env, steps: int, warmup: int, per_rank: int = 256 * MiB, 
     if cpu:
         cpu_res = cpu_baseline_allreduce(host, dst, per_rank)
     return out, cpu_res
+
+
+def run_allreduce_atomic(env: Env, steps: int, warmup: int, per_rank: int = 256 * MiB):
+    """The non-deterministic (float-atomic) AllReduce mode on the headline
+    workload, for comparison with the deterministic kernel."""
+    from copy_reduce_snac_amd import workloads as wl
+
+    snac = env.snac
+    m = per_rank // 2
+    src = [env.upload(gen_bf16(m, wl.CFG_AR_BF16_N8, r)) for r in range(N)]
+    dst = [env.empty(per_rank) for _ in range(N)]
+    # accumulator: a staging ring per rank big enough for the binary32 sums
+    ctx = snac.snac_init(N, 2 * per_rank // N, env.stream)
+    try:
+        t = env.time_calls(lambda: snac.snac_all_reduce_ex(ctx, src, dst, per_rank, "bf16", "atomic", env.stream),
+                           steps, warmup)
+    finally:
+        snac.snac_finalize(ctx, env.stream)
+    return result(f"allreduce_sum bf16 N={N} {per_rank // MiB} MiB/rank, atomic (non-deterministic) mode", t,
+                  2 * N * per_rank, per_rank)
 
 
 def cpu_baseline_allreduce(host, dst, per_rank):
@@ -376,6 +397,8 @@ def main() -> int:
         name = args.only
         if name == "allreduce":
             r, _ = run_allreduce(env, args.steps, args.warmup, cpu=False)
+        elif name == "allreduce_atomic":
+            r = run_allreduce_atomic(env, args.steps, args.warmup)
         elif name == "copy":
             r = run_copy(env, args.steps, args.warmup)
         elif name == "rs_ag":
@@ -403,6 +426,8 @@ def main() -> int:
         for dt in ("bf16", "f32"):
             extra.append(run_pipeline(env, args.steps, args.warmup, dt))
         extra.append(run_pipeline_latency(env))
+        env.torch.cuda.empty_cache()
+        extra.append(run_allreduce_atomic(env, 3, 1))
     t = head["ms_per_call"] / 1e3
     achieved = head["hbm_GBps"]
     traffic = recorded_traffic()

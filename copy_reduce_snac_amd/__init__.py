@@ -129,6 +129,7 @@ _SIGS = {
     "snac_copy": (_I, [_VP, _VP, _SZ, _VP]),
     "snac_reduce_n": (_I, [ctypes.POINTER(_VP), _I, ctypes.POINTER(_VP), _I, _SZ, _I, _VP]),
     "snac_all_reduce": (_I, [_VP, ctypes.POINTER(_VP), ctypes.POINTER(_VP), _SZ, _I, _VP]),
+    "snac_all_reduce_ex": (_I, [_VP, ctypes.POINTER(_VP), ctypes.POINTER(_VP), _SZ, _I, _I, _VP]),
     "snac_reduce_scatter": (_I, [_VP, ctypes.POINTER(_VP), ctypes.POINTER(_VP), _SZ, _I, _VP]),
     "snac_all_gather": (_I, [_VP, ctypes.POINTER(_VP), ctypes.POINTER(_VP), _SZ, _I, _VP]),
     "snac_all_to_all": (_I, [_VP, ctypes.POINTER(_VP), ctypes.POINTER(_VP), _SZ, _I, _VP]),
@@ -273,6 +274,16 @@ def _vary(name: str, ctx: int, srcs: Sequence, dsts: Sequence, counts: Iterable[
 
 def snac_all_reduce(ctx, srcs, dsts, nbytes, dtype, stream=None):
     _fixed("snac_all_reduce", ctx, srcs, dsts, nbytes, dtype, stream)
+
+
+SNAC_REDUCE_DETERMINISTIC, SNAC_REDUCE_ATOMIC = 0, 1
+_MODES = {"deterministic": SNAC_REDUCE_DETERMINISTIC, "atomic": SNAC_REDUCE_ATOMIC}
+
+
+def snac_all_reduce_ex(ctx, srcs, dsts, nbytes, dtype, mode, stream=None):
+    m = _MODES[mode] if isinstance(mode, str) else int(mode)
+    _check(lib().snac_all_reduce_ex(ctx, _ptrs(srcs), _ptrs(dsts), nbytes, _dtype(dtype), m, _stream(stream)),
+           "snac_all_reduce_ex")
 
 
 def snac_reduce_scatter(ctx, srcs, dsts, nbytes, dtype, stream=None):

@@ -546,6 +546,35 @@ snac_status snac_all_reduce(snac_ctx* ctx, const void* const* src, void* const* 
   return fixed_collective(kAllReduce, ctx, src, dst, bytes, dtype, stream);
 }
 
+snac_status snac_all_reduce_ex(snac_ctx* ctx, const void* const* src, void* const* dst, size_t bytes,
+                               snac_dtype dtype, snac_reduce_mode mode, snac_stream stream) {
+  if (mode == SNAC_REDUCE_DETERMINISTIC) return fixed_collective(kAllReduce, ctx, src, dst, bytes, dtype, stream);
+  if (mode != SNAC_REDUCE_ATOMIC) return fail(SNAC_E_ARG, "unknown reduction mode %d", (int)mode);
+  // validate exactly as the deterministic call, without launching
+  snac_coll_desc d;
+  g_describe = &d;
+  snac_status st = fixed_collective(kAllReduce, ctx, src, dst, bytes, dtype, stream);
+  g_describe = nullptr;
+  if (st != SNAC_OK) return st;
+  if (bytes == 0) return ok();
+  const uint64_t e = (uint64_t)d.esize;
+  const uint64_t elems = bytes / e;
+  bool vec = true;
+  for (int i = 0; i < d.nsrc; ++i)
+    if (((uintptr_t)d.src[i] | (uintptr_t)d.dst[i]) & 15u) vec = false;
+  // accumulator: the staging rings, whole tiles at a time
+  const uint64_t tile_e = atomic_chunk_elems(d.esize);
+  const uint64_t cap = (uint64_t)ctx->nranks * ctx->staging_bytes / sizeof(float) / tile_e * tile_e;
+  if (cap == 0) return fail(SNAC_E_STATE, "staging too small for the atomic accumulator");
+  float* acc = reinterpret_cast<float*>(ctx->staging);
+  for (uint64_t first = 0; first < elems; first += cap) {
+    const uint64_t n = std::min(cap, elems - first);
+    hipError_t he = launch_atomic_allreduce(d, acc, first, n, vec && (first * e) % 16 == 0, (hipStream_t)stream);
+    if (he != hipSuccess) return hip_fail(he, "atomic all-reduce launch");
+  }
+  return ok();
+}
+
 snac_status snac_reduce_scatter(snac_ctx* ctx, const void* const* src, void* const* dst, size_t bytes,
                                 snac_dtype dtype, snac_stream stream) {
   return fixed_collective(kReduceScatter, ctx, src, dst, bytes, dtype, stream);

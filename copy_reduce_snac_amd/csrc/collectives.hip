@@ -127,6 +127,122 @@ hipError_t launch_collective(const CollDesc& d, bool aligned, uint64_t tiles, co
   return hipGetLastError();
 }
 
+// -------------------------------------------- non-deterministic AllReduce
+//
+// Each (tile, source rank) item adds its 16 KiB of the source into a
+// binary32 accumulator with hardware float atomics (global_atomic_add_f32),
+// as Iris's all_reduce_atomic adds every rank's tile into the destination;
+// the N items of a tile run on different workgroups, so the order of the
+// adds -- and the last bits of the sum -- depend on timing.  A second
+// kernel rounds the accumulator once into every destination.
+
+constexpr int kAtomicThreads = 256;
+constexpr int kAtomicUnits = 4;  // 16-byte units per lane per item
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kAtomicThreads) void atomic_accumulate_kernel(const CollDesc d, float* acc,
+                                                                           uint64_t first, uint64_t elems,
+                                                                           uint64_t items) {
+  constexpr uint32_t E = T::kSize;
+  constexpr uint32_t L = 16 / E;  // elements per 16-byte unit
+  constexpr uint64_t TILE_E = (uint64_t)kAtomicThreads * kAtomicUnits * L;
+  const uint64_t n = (uint64_t)d.nsrc;
+  for (uint64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const uint64_t t = it / n;
+    const int k = (int)(it - t * n);
+    const char* src = static_cast<const char*>(d.src[k]) + first * E;
+#pragma unroll
+    for (int u = 0; u < kAtomicUnits; ++u) {
+      const uint64_t e0 = t * TILE_E + ((uint64_t)u * kAtomicThreads + threadIdx.x) * L;
+      if (VEC && e0 + L <= elems) {
+        UnitAcc<T> v;
+        v.set(ld16<kCacheStream>(src + e0 * E));
+#pragma unroll
+        for (uint32_t j = 0; j < L; ++j)
+          __hip_atomic_fetch_add(acc + e0 + j, v.a[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        for (uint32_t j = 0; j < L && e0 + j < elems; ++j)
+          __hip_atomic_fetch_add(acc + e0 + j, load_elem<T>(src + (e0 + j) * E), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+}
+
+// dst[d][first + e] = R(acc[e]) for every destination.
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kAtomicThreads) void atomic_finish_kernel(const CollDesc d, const float* acc,
+                                                                       uint64_t first, uint64_t elems) {
+  constexpr uint32_t E = T::kSize;
+  constexpr uint32_t L = 16 / E;
+  const uint64_t stride = (uint64_t)gridDim.x * kAtomicThreads * L;
+  for (uint64_t e0 = ((uint64_t)blockIdx.x * kAtomicThreads + threadIdx.x) * L; e0 < elems; e0 += stride) {
+    if (VEC && e0 + L <= elems) {
+      UnitAcc<T> v;
+#pragma unroll
+      for (uint32_t j = 0; j < L; ++j) v.a[j] = acc[e0 + j];
+      const u32x4 w = v.out();
+      for (int k = 0; k < d.ndst; ++k) st16<kCacheStream>(static_cast<char*>(d.dst[k]) + (first + e0) * E, w);
+    } else {
+      for (uint32_t j = 0; j < L && e0 + j < elems; ++j)
+        for (int k = 0; k < d.ndst; ++k) store_elem<T>(static_cast<char*>(d.dst[k]) + (first + e0 + j) * E, acc[e0 + j]);
+    }
+  }
+}
+
+uint64_t atomic_chunk_elems(int esize) {
+  const uint64_t tile_e = (uint64_t)kAtomicThreads * kAtomicUnits * (16u / (uint32_t)esize);
+  return tile_e;  // chunks are whole tiles
+}
+
+hipError_t launch_atomic_allreduce(const CollDesc& d, float* acc, uint64_t first, uint64_t elems, bool vec,
+                                   hipStream_t stream) {
+  if (elems == 0) return hipSuccess;
+  const uint64_t tile_e = atomic_chunk_elems(d.esize);
+  const uint64_t items = (elems + tile_e - 1) / tile_e * (uint64_t)d.nsrc;
+  const int cus = device_cu_count();
+  uint64_t grid = (uint64_t)(cus > 0 ? cus : 1) * 4;
+  if (grid > items) grid = items;
+  hipError_t e = fill_u64(reinterpret_cast<uint64_t*>(acc), (elems + 1) / 2, 0, stream);
+  if (e != hipSuccess) return e;
+  const bool bf = d.esize == 2;
+  if (bf) {
+    if (vec)
+      hipLaunchKernelGGL((atomic_accumulate_kernel<BF16, true>), dim3((uint32_t)grid), dim3(kAtomicThreads), 0, stream, d,
+                         acc, first, elems, items);
+    else
+      hipLaunchKernelGGL((atomic_accumulate_kernel<BF16, false>), dim3((uint32_t)grid), dim3(kAtomicThreads), 0, stream, d,
+                         acc, first, elems, items);
+  } else {
+    if (vec)
+      hipLaunchKernelGGL((atomic_accumulate_kernel<F32, true>), dim3((uint32_t)grid), dim3(kAtomicThreads), 0, stream, d,
+                         acc, first, elems, items);
+    else
+      hipLaunchKernelGGL((atomic_accumulate_kernel<F32, false>), dim3((uint32_t)grid), dim3(kAtomicThreads), 0, stream, d,
+                         acc, first, elems, items);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const uint64_t units = (elems + (16u / d.esize) - 1) / (16u / d.esize);
+  uint64_t fgrid = (units + kAtomicThreads - 1) / kAtomicThreads;
+  if (fgrid > (uint64_t)(cus > 0 ? cus : 1) * 4) fgrid = (uint64_t)(cus > 0 ? cus : 1) * 4;
+  if (bf) {
+    if (vec)
+      hipLaunchKernelGGL((atomic_finish_kernel<BF16, true>), dim3((uint32_t)fgrid), dim3(kAtomicThreads), 0, stream, d, acc,
+                         first, elems);
+    else
+      hipLaunchKernelGGL((atomic_finish_kernel<BF16, false>), dim3((uint32_t)fgrid), dim3(kAtomicThreads), 0, stream, d, acc,
+                         first, elems);
+  } else {
+    if (vec)
+      hipLaunchKernelGGL((atomic_finish_kernel<F32, true>), dim3((uint32_t)fgrid), dim3(kAtomicThreads), 0, stream, d, acc,
+                         first, elems);
+    else
+      hipLaunchKernelGGL((atomic_finish_kernel<F32, false>), dim3((uint32_t)fgrid), dim3(kAtomicThreads), 0, stream, d, acc,
+                         first, elems);
+  }
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ fill
 
 __global__ void fill_u64_kernel(uint64_t* p, uint64_t n, uint64_t v) {

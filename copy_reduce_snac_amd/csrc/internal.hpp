@@ -25,6 +25,15 @@ uint32_t coll_tile_bytes(const CollDesc& d, bool aligned);
 hipError_t launch_collective(const CollDesc& d, bool aligned, uint64_t tiles, const LaunchCfg& cfg,
                              hipStream_t stream);
 
+// Non-deterministic AllReduce of elements [first, first + elems) of every
+// source: zero acc[0..elems), add every source into it with float atomics,
+// round it into every destination.  vec: every source and destination
+// address of the range 16-byte aligned.  Chunks are whole tiles of
+// atomic_chunk_elems(esize) elements (except the last).
+hipError_t launch_atomic_allreduce(const CollDesc& d, float* acc, uint64_t first, uint64_t elems, bool vec,
+                                   hipStream_t stream);
+uint64_t atomic_chunk_elems(int esize);
+
 // Device-side SNAC pipeline (y = 0.5 x + r staged, then N-to-1 reduce).
 constexpr int kMaxQueues = 8;
 

@@ -239,6 +239,36 @@ snac_status snac_all_reduce(snac_ctx* ctx, const void* const* src, void* const* 
                             snac_dtype dtype, snac_stream stream);
 
 /*
+ * Reduction modes (Purlin 0.6.5 and 0.6.4 "Reduction determinism": a
+ * deterministic mode gives bitwise repeatable results; the default there is
+ * non-deterministic, which lets the hardware reduce in any order).
+ *
+ *   SNAC_REDUCE_DETERMINISTIC  binary32 in rank order 0..N-1, one rounding:
+ *                              what snac_all_reduce does.
+ *   SNAC_REDUCE_ATOMIC         every rank's tile is added into a binary32
+ *                              accumulator with hardware float atomics
+ *                              (Iris all_reduce_atomic), in whatever order the
+ *                              workgroups reach it, from +0.0; one rounding
+ *                              into every destination.  The result may differ
+ *                              between runs in the last bits: |result - exact
+ *                              sum| <= N * 2^-24 * sum|x_k| before the final
+ *                              rounding.  On one GPU it is slower than the
+ *                              deterministic mode (N float atomics per
+ *                              element); it exists for comparison.
+ */
+typedef enum snac_reduce_mode { SNAC_REDUCE_DETERMINISTIC = 0, SNAC_REDUCE_ATOMIC = 1 } snac_reduce_mode;
+
+/*
+ * snac_all_reduce_ex -- snac_all_reduce with a reduction mode.  Arguments,
+ * errors and in-place rules as for snac_all_reduce.  SNAC_REDUCE_ATOMIC uses
+ * the context's staging rings (N * staging_bytes_per_rank bytes) as its
+ * accumulator, in chunks of up to that size / 4 elements; it must not run
+ * concurrently with snac_pipeline_scale_reduce on the same context.
+ */
+snac_status snac_all_reduce_ex(snac_ctx* ctx, const void* const* src, void* const* dst, size_t bytes,
+                               snac_dtype dtype, snac_reduce_mode mode, snac_stream stream);
+
+/*
  * snac_reduce_scatter -- dst[r] (bytes/N) receives the reduction of chunk r
  * of every src, dim 0 split into N equal contiguous chunks (NKI
  * reduce_scatter_hbm_kernel).  `bytes` is the per-rank input size and must

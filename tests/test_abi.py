@@ -281,3 +281,8 @@ def test_invalid_tuning_rules_rejected(bad):
     before = snac.snac_get_tuning_rules()
     _expect(snac.SNAC_E_ARG, snac.snac_set_tuning_rules, [good, {**good, **bad}])
     assert snac.snac_get_tuning_rules() == before  # unchanged on error
+
+
+def test_reduce_mode_argument_errors_without_gpu():
+    _expect(snac.SNAC_E_ARG, snac.snac_all_reduce_ex, None, [0x1000], [0x2000], 16, "f32", "atomic")
+    _expect(snac.SNAC_E_ARG, snac.snac_all_reduce_ex, None, [0x1000], [0x2000], 16, "f32", 7)
