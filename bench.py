@@ -123,6 +123,27 @@ class Env:
         return start.elapsed_time(end) / 1e3 / steps
 
 
+    def time_calls_cold(self, fn, steps: int, warmup: int) -> float:
+        """Seconds per call with the inputs evicted from the caches first:
+        a 1 GiB scratch write (untimed) before each event-timed call."""
+        torch = self.torch
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=self.dev)
+        for _ in range(warmup):
+            fn()
+        total = 0.0
+        for _ in range(steps):
+            scratch.fill_(1)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(self.stream)
+            fn()
+            e1.record(self.stream)
+            torch.cuda.synchronize()
+            total += e0.elapsed_time(e1) / 1e3
+        del scratch
+        return total / steps
+
+
 def gen_bf16(m: int, cfg: int, rank: int) -> np.ndarray:
     from copy_reduce_snac_amd import workloads as wl
 
@@ -240,8 +261,9 @@ def run_rs_ag(env: Env, steps: int, warmup: int):
     ag_out = [env.empty(per_rank) for _ in range(N)]
     t_rs = env.time_calls(lambda: snac.snac_reduce_scatter(env.ctx, src, rs_out, per_rank, "bf16", env.stream),
                           steps, warmup)
-    t_ag = env.time_calls(lambda: snac.snac_all_gather(env.ctx, rs_out, ag_out, per_rank // N, "bf16", env.stream),
-                          steps, warmup)
+    ag = lambda: snac.snac_all_gather(env.ctx, rs_out, ag_out, per_rank // N, "bf16", env.stream)
+    t_ag = env.time_calls(ag, steps, warmup)
+    t_ag_cold = env.time_calls_cold(ag, steps, warmup)
     ar_out = [env.empty(per_rank) for _ in range(N)]
     snac.snac_all_reduce(env.ctx, src, ar_out, per_rank, "bf16", env.stream)
     env.torch.cuda.synchronize()
@@ -250,6 +272,8 @@ def run_rs_ag(env: Env, steps: int, warmup: int):
         result(f"reduce_scatter bf16 N={N} ({rows}x{cols})/rank", t_rs, N * per_rank + per_rank, per_rank),
         result(f"all_gather bf16 N={N} ({rows // N}x{cols})/rank in", t_ag, per_rank + N * per_rank, per_rank,
                ag_of_rs_equals_allreduce=same),
+        result(f"all_gather bf16 N={N} ({rows // N}x{cols})/rank in, inputs evicted from the caches before each call",
+               t_ag_cold, per_rank + N * per_rank, per_rank),
     ]
 
 

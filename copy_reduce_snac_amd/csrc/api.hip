@@ -73,10 +73,16 @@ constexpr int kDefaultSpinLog2 = 22;
 
 // Built-in rules, measured on MI355X: reduces of 4 or more sources run one
 // workgroup per CU (more concurrent write streams lower HBM efficiency),
-// smaller reduces and copies two; streaming (non-temporal) accesses
-// throughout; the pipeline picks its own grid (4 per CU when the ring
-// holds the message, else 2).
+// smaller reduces and copies two; streaming (non-temporal) accesses,
+// except that AllGather(V) reads its inputs with cached loads -- N
+// destinations are written per input byte, so inputs small enough for the
+// Infinity Cache stay there across calls (6.3-6.7 TB/s against 4.9 with
+// streaming loads when they are reused; no difference when they are not).
+// The pipeline picks its own grid (4 per CU when the ring holds the
+// message, else 2).
 const snac_tuning_rule kBuiltinRules[] = {
+    {SNAC_COLL_ALL_GATHER, 1, SNAC_MAX_RANKS, 0, 0, UINT64_MAX, 2, 2},
+    {SNAC_COLL_ALL_GATHER_V, 1, SNAC_MAX_RANKS, 0, 0, UINT64_MAX, 2, 2},
     {SNAC_RULE_ANY_REDUCE, 4, SNAC_MAX_RANKS, 0, 0, UINT64_MAX, 1, 1},
     {SNAC_RULE_ANY_REDUCE, 1, 3, 0, 0, UINT64_MAX, 2, 1},
     {SNAC_RULE_ANY_COPY, 1, SNAC_MAX_RANKS, 0, 0, UINT64_MAX, 2, 1},
@@ -140,6 +146,7 @@ bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 struct Plan {
   CollDesc d;
   bool aligned;
+  bool small;  // small-tile kernels (message too small to fill the GPU at 16 KiB tiles)
   uint64_t tiles;
   uint64_t rule_bytes;  // per-rank input bytes the tuning rules match on
 };
@@ -160,14 +167,23 @@ void finish_plan(Plan& p) {
       if (((uintptr_t)p.d.dst[t] + jb.dst_off) & 15u) aligned = false;
   }
   p.aligned = aligned;
-  const uint64_t tile = coll_tile_bytes(p.d, aligned);
-  uint64_t tiles = 0;
-  for (int j = 0; j < nj; ++j) {
-    const Job jb = make_job(p.d, j);
-    const uint32_t head = aligned ? 0u : job_head_bytes(p.d, jb);
-    tiles += job_tiles(jb, head, tile);
+  auto count_tiles = [&](bool small) {
+    const uint64_t tile = coll_tile_bytes(p.d, small);
+    uint64_t tiles = 0;
+    for (int j = 0; j < nj; ++j) {
+      const Job jb = make_job(p.d, j);
+      const uint32_t head = aligned ? 0u : job_head_bytes(p.d, jb);
+      tiles += job_tiles(jb, head, tile);
+    }
+    return tiles;
+  };
+  p.small = false;
+  p.tiles = count_tiles(false);
+  const int cus = device_cu_count();
+  if (p.tiles > 0 && cus > 0 && p.tiles < (uint64_t)cus) {
+    p.small = true;
+    p.tiles = count_tiles(true);
   }
-  p.tiles = tiles;
 }
 
 // Copy multicasts split into one job per destination when asked to.
@@ -241,8 +257,8 @@ snac_status run(Plan& p, hipStream_t stream) {
     return ok();
   }
   if (p.tiles == 0) return ok();
-  hipError_t e = launch_collective(p.d, p.aligned, p.tiles, launch_cfg(p.d.coll, p.d.nsrc, p.d.esize, p.rule_bytes),
-                                   stream);
+  hipError_t e = launch_collective(p.d, p.aligned, p.small, p.tiles,
+                                   launch_cfg(p.d.coll, p.d.nsrc, p.d.esize, p.rule_bytes), stream);
   if (e != hipSuccess) return hip_fail(e, "collective launch");
   return ok();
 }

@@ -13,46 +13,59 @@ namespace snac {
 constexpr int kCopyThreads = 256;
 constexpr int kReduceThreads = 128;
 
-// N-to-1 reduce of element type T over N sources, the whole grid.
-template <int N, typename T, int CP, bool ALIGNED>
+// N-to-1 reduce of element type T over N sources, the whole grid.  SMALL:
+// the small-tile form (one 16-byte unit per lane, all sources in flight)
+// for messages with fewer 16 KiB tiles than the GPU has CUs.
+template <int N, typename T, int CP, bool ALIGNED, bool SMALL = false>
 __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(const CollDesc d) {
-  run_reduce<N, T, kReduceThreads, CP, ALIGNED>(d, blockIdx.x, gridDim.x);
+  constexpr uint32_t TILE = SMALL ? kReduceThreads * 16u : kTileBytes;
+  run_reduce<N, T, kReduceThreads, CP, ALIGNED, TILE>(d, blockIdx.x, gridDim.x);
 }
 
-// Byte copy of the collective's jobs, the whole grid.
-template <int CP, bool ALIGNED>
-__global__ __launch_bounds__(kCopyThreads) void copy_kernel(const CollDesc d) {
-  run_copy<kCopyThreads, CP, ALIGNED>(d, blockIdx.x, gridDim.x);
+// Byte copy of the collective's jobs, the whole grid.  TH = 256 for
+// one-to-one copies; multicast copies (AllGather, AllGatherV: one read, N
+// writes per unit) use single-wave workgroups, which on MI355X sustain
+// about 6 % more write bandwidth than 256-thread ones.
+constexpr int kMulticastThreads = 64;
+
+template <int CP, bool ALIGNED, int TH, bool SMALL = false>
+__global__ __launch_bounds__(TH) void copy_kernel(const CollDesc d) {
+  constexpr uint32_t TILE = SMALL ? TH * 16u : kTileBytes;
+  run_copy<TH, CP, ALIGNED, TILE>(d, blockIdx.x, gridDim.x);
+}
+
+SNAC_HD bool is_multicast_copy(const CollDesc& d) {
+  return (d.coll == kAllGather || d.coll == kAllGatherV) && !d.split_multicast;
 }
 
 // ------------------------------------------------------------- launchers
 
 using KernelFn = void (*)(const CollDesc);
 
-template <int N, typename T, int CP, bool A>
+template <int N, typename T, int CP, bool A, bool SMALL>
 KernelFn kernel_ptr() {
-  return &reduce_kernel<N, T, CP, A>;
+  return &reduce_kernel<N, T, CP, A, SMALL>;
 }
 
-template <typename T, int CP, bool A>
+template <typename T, int CP, bool A, bool SMALL = false>
 KernelFn reduce_kernel_n(int n) {
   switch (n) {
-    case 1: return kernel_ptr<1, T, CP, A>();
-    case 2: return kernel_ptr<2, T, CP, A>();
-    case 3: return kernel_ptr<3, T, CP, A>();
-    case 4: return kernel_ptr<4, T, CP, A>();
-    case 5: return kernel_ptr<5, T, CP, A>();
-    case 6: return kernel_ptr<6, T, CP, A>();
-    case 7: return kernel_ptr<7, T, CP, A>();
-    case 8: return kernel_ptr<8, T, CP, A>();
-    case 9: return kernel_ptr<9, T, CP, A>();
-    case 10: return kernel_ptr<10, T, CP, A>();
-    case 11: return kernel_ptr<11, T, CP, A>();
-    case 12: return kernel_ptr<12, T, CP, A>();
-    case 13: return kernel_ptr<13, T, CP, A>();
-    case 14: return kernel_ptr<14, T, CP, A>();
-    case 15: return kernel_ptr<15, T, CP, A>();
-    case 16: return kernel_ptr<16, T, CP, A>();
+    case 1: return kernel_ptr<1, T, CP, A, SMALL>();
+    case 2: return kernel_ptr<2, T, CP, A, SMALL>();
+    case 3: return kernel_ptr<3, T, CP, A, SMALL>();
+    case 4: return kernel_ptr<4, T, CP, A, SMALL>();
+    case 5: return kernel_ptr<5, T, CP, A, SMALL>();
+    case 6: return kernel_ptr<6, T, CP, A, SMALL>();
+    case 7: return kernel_ptr<7, T, CP, A, SMALL>();
+    case 8: return kernel_ptr<8, T, CP, A, SMALL>();
+    case 9: return kernel_ptr<9, T, CP, A, SMALL>();
+    case 10: return kernel_ptr<10, T, CP, A, SMALL>();
+    case 11: return kernel_ptr<11, T, CP, A, SMALL>();
+    case 12: return kernel_ptr<12, T, CP, A, SMALL>();
+    case 13: return kernel_ptr<13, T, CP, A, SMALL>();
+    case 14: return kernel_ptr<14, T, CP, A, SMALL>();
+    case 15: return kernel_ptr<15, T, CP, A, SMALL>();
+    case 16: return kernel_ptr<16, T, CP, A, SMALL>();
     default: return nullptr;
   }
 }
@@ -68,19 +81,27 @@ KernelFn reduce_kernel_cp(int n, int cp, bool aligned) {
   }
 }
 
+template <int TH>
 static KernelFn copy_kernel_cp(int cp, bool aligned) {
-  if (!aligned) return cp == kCached ? &copy_kernel<kCached, false> : &copy_kernel<kCacheStream, false>;
+  if (!aligned) {
+    if (cp == kCached) return &copy_kernel<kCached, false, TH>;
+    if (cp == kCacheStreamStores) return &copy_kernel<kCacheStreamStores, false, TH>;
+    return &copy_kernel<kCacheStream, false, TH>;
+  }
   switch (cp) {
-    case kCacheStream: return &copy_kernel<kCacheStream, true>;
-    case kCacheStreamStores: return &copy_kernel<kCacheStreamStores, true>;
-    case kCacheStreamLoads: return &copy_kernel<kCacheStreamLoads, true>;
-    default: return &copy_kernel<kCached, true>;
+    case kCacheStream: return &copy_kernel<kCacheStream, true, TH>;
+    case kCacheStreamStores: return &copy_kernel<kCacheStreamStores, true, TH>;
+    case kCacheStreamLoads: return &copy_kernel<kCacheStreamLoads, true, TH>;
+    default: return &copy_kernel<kCached, true, TH>;
   }
 }
 
-uint32_t coll_tile_bytes(const CollDesc& d, bool aligned) {
-  (void)aligned;
-  return kTileBytes;
+static int coll_threads(const CollDesc& d) {
+  return coll_is_reduce(d.coll) ? kReduceThreads : (is_multicast_copy(d) ? kMulticastThreads : kCopyThreads);
+}
+
+uint32_t coll_tile_bytes(const CollDesc& d, bool small) {
+  return small ? (uint32_t)coll_threads(d) * 16u : kTileBytes;
 }
 
 int device_cu_count() {
@@ -97,28 +118,49 @@ int device_cu_count() {
   return cached_cus;
 }
 
-hipError_t launch_collective(const CollDesc& d, bool aligned, uint64_t tiles, const LaunchCfg& cfg,
+// Small-tile kernels: streaming accesses (the cache policy does not matter
+// for a message this small), aligned or generic.
+static KernelFn small_kernel(const CollDesc& d, bool aligned) {
+  if (coll_is_reduce(d.coll)) {
+    if (d.esize == 4)
+      return aligned ? reduce_kernel_n<F32, kCacheStream, true, true>(d.nsrc)
+                     : reduce_kernel_n<F32, kCacheStream, false, true>(d.nsrc);
+    return aligned ? reduce_kernel_n<BF16, kCacheStream, true, true>(d.nsrc)
+                   : reduce_kernel_n<BF16, kCacheStream, false, true>(d.nsrc);
+  }
+  if (is_multicast_copy(d))
+    return aligned ? &copy_kernel<kCacheStream, true, kMulticastThreads, true>
+                   : &copy_kernel<kCacheStream, false, kMulticastThreads, true>;
+  return aligned ? &copy_kernel<kCacheStream, true, kCopyThreads, true>
+                 : &copy_kernel<kCacheStream, false, kCopyThreads, true>;
+}
+
+hipError_t launch_collective(const CollDesc& d, bool aligned, bool small, uint64_t tiles, const LaunchCfg& cfg,
                              hipStream_t stream) {
   if (tiles == 0) return hipSuccess;
   KernelFn fn = nullptr;
   // tuning value 0 = library default (streaming loads and stores), 4 = cached
   const int cp = cfg.cache_policy == 0 ? kCacheStream : (cfg.cache_policy == 4 ? kCached : cfg.cache_policy);
   const bool reduce = coll_is_reduce(d.coll);
-  if (reduce) {
-    if (num_jobs(d) > kMaxRanks) return hipErrorInvalidValue;
+  if (reduce && num_jobs(d) > kMaxRanks) return hipErrorInvalidValue;
+  if (small) {
+    fn = small_kernel(d, aligned);
+  } else if (reduce) {
     fn = d.esize == 4 ? reduce_kernel_cp<F32>(d.nsrc, cp, aligned) : reduce_kernel_cp<BF16>(d.nsrc, cp, aligned);
   } else {
-    fn = copy_kernel_cp(cp, aligned);
+    fn = is_multicast_copy(d) ? copy_kernel_cp<kMulticastThreads>(cp, aligned) : copy_kernel_cp<kCopyThreads>(cp, aligned);
   }
   if (!fn) return hipErrorInvalidValue;
-  const int threads = reduce ? kReduceThreads : kCopyThreads;
+  const int threads = coll_threads(d);
   int per_cu = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), threads, 0);
   if (e != hipSuccess) return e;
   if (per_cu < 1) per_cu = 1;
   // Measured on MI355X: the 1:1 read/write streams run fastest with few
   // workgroups per CU (more concurrent write streams lower HBM efficiency).
-  const int want = cfg.wgs_per_cu > 0 ? cfg.wgs_per_cu : (reduce && d.nsrc >= 4 ? 1 : 2);
+  // A small message instead wants its tiles spread wide (two workgroups per
+  // CU: more would each rebuild the job table for a single tile).
+  const int want = cfg.wgs_per_cu > 0 ? cfg.wgs_per_cu : (small ? 2 : (reduce && d.nsrc >= 4 ? 1 : 2));
   if (want < per_cu) per_cu = want;
   const int cus = device_cu_count();
   uint64_t grid = (uint64_t)(cus > 0 ? cus : 1) * (uint64_t)per_cu;

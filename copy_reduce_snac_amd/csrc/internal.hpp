@@ -16,13 +16,15 @@ struct LaunchCfg {
 };
 
 // Tile size (bytes of each source per workgroup iteration) of the kernel
-// that serves this descriptor; the host needs it to size the grid.
-uint32_t coll_tile_bytes(const CollDesc& d, bool aligned);
+// that serves this descriptor; the host needs it to count tiles.  small:
+// the small-tile kernels (one 16-byte unit per lane) used when a message
+// has fewer 16 KiB tiles than the GPU has CUs.
+uint32_t coll_tile_bytes(const CollDesc& d, bool small);
 
 // Launch the copy or reduce kernel for a collective descriptor.  `tiles` is
-// the total tile count of the layout (computed on the host with the same
-// layout functions the kernel uses).
-hipError_t launch_collective(const CollDesc& d, bool aligned, uint64_t tiles, const LaunchCfg& cfg,
+// the total tile count of the layout at coll_tile_bytes(d, small) (computed
+// on the host with the same layout functions the kernel uses).
+hipError_t launch_collective(const CollDesc& d, bool aligned, bool small, uint64_t tiles, const LaunchCfg& cfg,
                              hipStream_t stream);
 
 // Non-deterministic AllReduce of elements [first, first + elems) of every

@@ -493,10 +493,11 @@ __device__ inline bool group_barrier(const snac_dev_ctx& c, uint32_t blocks) {
 
 constexpr uint32_t kTileBytes = 16384;
 
-template <int TH>
+template <int TH, uint32_t TILE = kTileBytes>
 constexpr int tile_units() {
   static_assert(TH % 64 == 0 && TH >= 64 && TH <= 1024, "workgroup size must be a multiple of 64, at most 1024");
-  return (int)(kTileBytes / (TH * 16u));
+  static_assert(TILE % (TH * 16u) == 0 && TILE >= TH * 16u, "a tile is a whole number of units per lane");
+  return (int)(TILE / (TH * 16u));
 }
 
 struct JobL {
@@ -517,6 +518,31 @@ __device__ uint32_t build_table(const CollDesc& d, uint32_t tile_bytes, JobL* jo
   constexpr int K = (MAXJ + TH - 1) / TH;
   nj = num_jobs(d);
   const int t = threadIdx.x;
+  if (nj <= 64) {
+    // one wave: lane j owns job j; an inclusive scan over the wave with
+    // shuffles, then a single barrier (no LDS scan rounds)
+    if (t < 64) {
+      uint32_t mine = 0;
+      if (t < nj) {
+        const Job jb = make_job(d, t);
+        const uint32_t head = ALIGNED ? 0u : job_head_bytes(d, jb);
+        mine = (uint32_t)job_tiles(jb, head, tile_bytes);
+        jobs[t] = JobL{jb.src_off, jb.dst_off, jb.bytes, jb.src_rank, jb.dst_rank, head, 0u};
+      }
+      uint32_t incl = mine;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t v = __shfl_up(incl, off, 64);
+        if (t >= off) incl += v;
+      }
+      if (t < nj) jobs[t].tile0 = incl - mine;
+      if (t == 63) scan[0] = incl;
+    }
+    __syncthreads();
+    const uint32_t total = scan[0];
+    __syncthreads();  // scan[0] may be reused by the next table build
+    return total;
+  }
   uint32_t mine[K];
   uint32_t sum = 0;
 #pragma unroll
@@ -625,10 +651,21 @@ struct JobCursor {
     next_tile0 = j + 1 < nj ? uniform(jobs[j + 1].tile0) : 0xffffffffu;
   }
 
+  // first job: binary search for the last job whose first tile is <= tile
+  // (tile0 ascends; a linear walk cost up to 63 dependent LDS reads)
   __device__ __forceinline__ void init(const JobL* t, int n, uint32_t tile) {
     jobs = t;
     nj = n;
-    j = 0;
+    int lo = 0, hi = nj - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (jobs[mid].tile0 <= tile)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    j = lo;
+    // zero-tile jobs share their tile0 with the next job: step past them
     while (j + 1 < nj && jobs[j + 1].tile0 <= tile) ++j;
     load_job();
   }
@@ -731,6 +768,21 @@ __device__ __forceinline__ void reduce_tile(const CollDesc& d, const TileRef& t,
   for (int u = 0; u < U; ++u) r[u] = acc[u].out();
 }
 
+// Small tiles (one unit per lane): every source's load is issued before
+// the first add, so a tile costs one memory round trip -- what matters when
+// a message has fewer tiles than the GPU has CUs.
+template <int N, typename T, int TH, int CP, bool ALIGNED, bool FULL>
+__device__ __forceinline__ void reduce_tile_allin(const CollDesc& d, const TileRef& t, u32x4 (&r)[1]) {
+  u32x4 v[N][1];
+#pragma unroll
+  for (int k = 0; k < N; ++k) reduce_load<TH, 1, CP, ALIGNED, FULL>(d, t, k, v[k]);
+  UnitAcc<T> acc;
+  acc.set(v[0][0]);
+#pragma unroll
+  for (int k = 1; k < N; ++k) acc.add(v[k][0]);
+  r[0] = acc.out();
+}
+
 // -------------------------------------------------------------- copy tiles
 
 __device__ inline void copy_edges(const CollDesc& d, const JobL& J, uint32_t head, uint64_t body) {
@@ -772,14 +824,16 @@ __device__ __forceinline__ void copy_load(const CollDesc& d, const TileRef& t, u
 // ----------------------------------------------------------- tile loops
 //
 // run_reduce / run_copy: this workgroup's share (tiles block, block +
-// blocks, ...) of a reduce or copy collective.  blockDim.x must equal TH.
+// blocks, ...) of a reduce or copy collective.  blockDim.x must equal TH;
+// TILE (bytes of each source per tile) defaults to kTileBytes, and
+// TILE = TH * 16 gives the small-tile form for messages too small to fill
+// the GPU.
 // Every thread of the workgroup calls them; they return once the share is
 // stored (not yet visible to other workgroups: see group_barrier).
 
-template <int N, typename T, int TH, int CP, bool ALIGNED>
+template <int N, typename T, int TH, int CP, bool ALIGNED, uint32_t TILE = kTileBytes>
 __device__ void run_reduce(const CollDesc& d, uint32_t block, uint32_t blocks) {
-  constexpr int U = tile_units<TH>();
-  constexpr uint32_t TILE = kTileBytes;
+  constexpr int U = tile_units<TH, TILE>();
   // edge elements (head < 128 bytes, tail < 16) and jobs are looped over
   __shared__ JobL jobs[kMaxRanks];
   __shared__ uint32_t scan[TH];
@@ -793,10 +847,17 @@ __device__ void run_reduce(const CollDesc& d, uint32_t block, uint32_t blocks) {
   for (; tile < total; tile += blocks) {
     const TileRef t = jc.at(tile);
     u32x4 r[U];
-    if (ALIGNED || t.rem == TILE)
-      reduce_tile<N, T, TH, U, CP, ALIGNED, true>(d, t, r);
-    else
-      reduce_tile<N, T, TH, U, CP, ALIGNED, false>(d, t, r);
+    if constexpr (U == 1) {
+      if (ALIGNED || t.rem == TILE)
+        reduce_tile_allin<N, T, TH, CP, ALIGNED, true>(d, t, r);
+      else
+        reduce_tile_allin<N, T, TH, CP, ALIGNED, false>(d, t, r);
+    } else {
+      if (ALIGNED || t.rem == TILE)
+        reduce_tile<N, T, TH, U, CP, ALIGNED, true>(d, t, r);
+      else
+        reduce_tile<N, T, TH, U, CP, ALIGNED, false>(d, t, r);
+    }
     if constexpr (!ALIGNED) {
       if (t.lt == 0) reduce_edges<T, N>(d, t.J, t.head, t.body);
     }
@@ -804,10 +865,9 @@ __device__ void run_reduce(const CollDesc& d, uint32_t block, uint32_t blocks) {
   }
 }
 
-template <int TH, int CP, bool ALIGNED>
+template <int TH, int CP, bool ALIGNED, uint32_t TILE = kTileBytes>
 __device__ void run_copy(const CollDesc& d, uint32_t block, uint32_t blocks) {
-  constexpr int U = tile_units<TH>();
-  constexpr uint32_t TILE = kTileBytes;
+  constexpr int U = tile_units<TH, TILE>();
   __shared__ JobL jobs[kMaxJobs];
   __shared__ uint32_t scan[TH];
   int nj;

@@ -240,6 +240,9 @@ def test_builtin_tuning_rules_and_lookup():
     assert snac.snac_tuning_lookup(snac.SNAC_COLL_REDUCE_SCATTER_V, 4, 4, 1)["wgs_per_cu"] == 1
     assert snac.snac_tuning_lookup(snac.SNAC_RULE_ATOM_REDUCE, 2, 4, 1)["wgs_per_cu"] == 2
     assert snac.snac_tuning_lookup(snac.SNAC_COLL_ALL_GATHER, 8, 1, 1)["wgs_per_cu"] == 2
+    # AllGather(V) reads inputs with cached loads (streaming stores)
+    assert snac.snac_tuning_lookup(snac.SNAC_COLL_ALL_GATHER_V, 8, 2, 1)["cache_policy"] == 2
+    assert snac.snac_tuning_lookup(snac.SNAC_COLL_ALL_TO_ALL, 8, 4, 1)["cache_policy"] == 1
     assert snac.snac_tuning_lookup(snac.SNAC_RULE_ATOM_COPY, 1, 1, 1)["cache_policy"] == 1
     # the pipeline picks its own grid
     assert snac.snac_tuning_lookup(snac.SNAC_RULE_PIPELINE, 8, 2, MiB)["wgs_per_cu"] == 0

@@ -343,3 +343,55 @@ def test_repeat_runs_bit_identical(ctxs):
     sync()
     for a, b in zip(d1, d2):
         assert np.array_equal(a.download(), b.download())
+
+
+# -------------------------------------------- 16 KiB-tile (large-message) paths
+# Messages with fewer 16 KiB tiles than the GPU has CUs run the small-tile
+# kernels, so the cases above mostly exercise those; these sizes (over 4 MiB
+# per rank) keep the 16 KiB-tile kernels, misaligned (generic) and ragged.
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_large_tiles_misaligned_allreduce_and_rs(ctxs, dtype):
+    n = 8
+    e = 2 if dtype == "bf16" else 4
+    m = 8 * (600_000 + 13)  # > 4 MiB per rank, divisible by N, ragged
+    srcs = gen(n, m, dtype, seed=41)
+    nb = srcs[0].nbytes
+    sb = [DevBuf(nb, offset=e * (k % 4), data=s) for k, s in enumerate(srcs)]
+    db = [DevBuf(nb, offset=e) for _ in srcs]
+    snac.snac_all_reduce(ctxs(n), [b.ptr for b in sb], [b.ptr for b in db], nb, dtype)
+    run_and_check(db, oracle.all_reduce(srcs, dtype), dtype, f"AR large misaligned {dtype}")
+    rb = [DevBuf(nb // n, offset=3 * e) for _ in srcs]
+    snac.snac_reduce_scatter(ctxs(n), [b.ptr for b in sb], [b.ptr for b in rb], nb, dtype)
+    run_and_check(rb, oracle.reduce_scatter(srcs, dtype), dtype, f"RS large misaligned {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["u32", "byte"])
+def test_large_tiles_v_collectives(ctxs, dtype):
+    n = 8
+    m = 4_500_000 if dtype == "byte" else 1_200_000
+    srcs = gen(n, m, dtype, seed=43)
+    c = wl.v_counts(n, m, n, cfg=wl.CFG_TEST, seed=43)
+    want = oracle.all_to_all_v(srcs, c)
+    e = 4 if dtype == "u32" else 1
+    sb = [DevBuf(s.nbytes, offset=e * (k % 3), data=s) for k, s in enumerate(srcs)]
+    db = [DevBuf(np.asarray(w).nbytes, offset=e) for w in want]
+    snac.snac_all_to_all_v(ctxs(n), [b.ptr for b in sb], [b.ptr for b in db], c.reshape(-1).tolist(), dtype)
+    run_and_check(db, want, dtype, f"A2AV large {dtype}")
+    row = c[0].tolist()
+    gsrc = [gen(1, int(row[k]), dtype, seed=50 + k)[0] for k in range(n)]
+    want = oracle.all_gather_v(gsrc, row)
+    gb = [DevBuf(s.nbytes, data=s) for s in gsrc]
+    db = [DevBuf(np.asarray(w).nbytes, offset=2 * e) for w in want]
+    snac.snac_all_gather_v(ctxs(n), [b.ptr for b in gb], [b.ptr for b in db], row, dtype)
+    run_and_check(db, want, dtype, f"AGV large {dtype}")
+
+
+@pytest.mark.parametrize("per_rank", [256 * 16384 - 16, 256 * 16384, 256 * 16384 + 16])
+def test_small_and_large_tiles_meet(ctxs, per_rank):
+    """Sizes on both sides of the switch between the two tile sizes."""
+    n = 8
+    srcs = gen(n, per_rank // 2, "bf16", seed=per_rank % 97)
+    sb = [DevBuf(per_rank, data=s) for s in srcs]
+    db = [DevBuf(per_rank) for _ in srcs]
+    snac.snac_all_reduce(ctxs(n), [b.ptr for b in sb], [b.ptr for b in db], per_rank, "bf16")
+    run_and_check(db, oracle.all_reduce(srcs, "bf16"), "bf16", f"AR {per_rank} B/rank")
