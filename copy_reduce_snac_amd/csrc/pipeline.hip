@@ -110,6 +110,9 @@ __device__ void stage_item(const PipeArgs& a, uint32_t t, uint32_t gslot, uint32
   const float rf = (float)r;
   const uint32_t nvec = nbytes & ~15u;
   constexpr int U = 4;
+  // staging stores write through the L2 (see kWriteThrough), so the release
+  // fence below has little left to write back
+  const __amdgpu_buffer_rsrc_t stg_r = buffer_rsrc(stg, nvec);
   for (uint32_t base = 0; base < nvec; base += kThreads * 16u * U) {
     u32x4 v[U];
 #pragma unroll
@@ -120,7 +123,7 @@ __device__ void stage_item(const PipeArgs& a, uint32_t t, uint32_t gslot, uint32
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t o = base + (threadIdx.x + (uint32_t)u * kThreads) * 16u;
-      if (o < nvec) st16<kCached>(stg + o, scale_unit<T>(v[u], rf));
+      if (o < nvec) bst16<kWriteThrough>(stg_r, o, scale_unit<T>(v[u], rf));
     }
   }
   const uint32_t tail = (nbytes - nvec) / E;
@@ -181,7 +184,7 @@ __device__ void consume_item(const PipeArgs& a, uint32_t t, uint32_t gslot, uint
       const uint32_t o = base + (threadIdx.x + (uint32_t)u * kThreads) * 16u;
       if (o < nvec) {
 #pragma unroll
-        for (int k = 0; k < N; ++k) v[u][k] = ld16<kCached>(stg + k * rank_stride + o);
+        for (int k = 0; k < N; ++k) v[u][k] = bld16<kWriteThrough>(buffer_rsrc(stg + k * rank_stride, nvec), o);
       }
     }
 #pragma unroll

