@@ -158,9 +158,10 @@ hipError_t launch_collective(const CollDesc& d, bool aligned, bool small, uint64
   if (per_cu < 1) per_cu = 1;
   // Measured on MI355X: the 1:1 read/write streams run fastest with few
   // workgroups per CU (more concurrent write streams lower HBM efficiency).
-  // A small message instead wants its tiles spread wide (two workgroups per
-  // CU: more would each rebuild the job table for a single tile).
-  const int want = cfg.wgs_per_cu > 0 ? cfg.wgs_per_cu : (small ? 2 : (reduce && d.nsrc >= 4 ? 1 : 2));
+  // A small message instead wants its tiles spread wide: a small-tile
+  // reduce (one job) up to four workgroups per CU, so each holds about one
+  // tile; copies, whose workgroups each rebuild a larger job table, two.
+  const int want = cfg.wgs_per_cu > 0 ? cfg.wgs_per_cu : (small ? (reduce ? 4 : 2) : (reduce && d.nsrc >= 4 ? 1 : 2));
   if (want < per_cu) per_cu = want;
   const int cus = device_cu_count();
   uint64_t grid = (uint64_t)(cus > 0 ? cus : 1) * (uint64_t)per_cu;
