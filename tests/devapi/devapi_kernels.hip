@@ -88,6 +88,48 @@ __global__ __launch_bounds__(TH) void fused_kernel(const snac_coll_desc desc, co
   if (threadIdx.x == 0) ok_out[blockIdx.x] = ok ? 1u : 0u;
 }
 
+// ---- the public SNAC primitives, stage / notify / consume by hand
+//
+// Workgroups p < n are producers: round r copies block r of x_p into rank
+// p's staging slot r % S (after waiting for the consumer to free it) and
+// notifies ready[p][slot] = base + r + 1.  The last workgroup is the
+// consumer: it consumes all n ready flags of the slot, reduces the n staged
+// blocks in rank order into out[r], and notifies free[slot].  User flags:
+// ready[p][slot] at p * S + slot, free[slot] at n * S + slot.
+
+__global__ __launch_bounds__(TH) void flags_kernel(const snac_dev_ctx ctx, snac_coll_desc xs, float* stage, float* out,
+                                                   int n, uint32_t S, uint32_t R, uint32_t B, uint64_t base,
+                                                   uint32_t* ok_out) {
+  const snac::WaitCtl w = snac::wait_ctl(ctx);
+  constexpr uint64_t F = SNAC_FLAG_STRIDE;
+  bool ok = true;
+  if ((int)blockIdx.x < n) {
+    const int p = blockIdx.x;
+    for (uint32_t r = 0; r < R && ok; ++r) {
+      const uint32_t slot = r % S;
+      if (r >= S) ok = snac::consume(ctx.flags + ((uint64_t)n * S + slot) * F, 1, F, base + r - S + 1, w);
+      if (!ok) break;
+      float* dst = stage + ((uint64_t)p * S + slot) * B;
+      const float* src = static_cast<const float*>(xs.src[p]) + (uint64_t)r * B;
+      for (uint32_t i = threadIdx.x; i < B; i += TH) dst[i] = src[i];
+      snac::notify(ctx.flags + ((uint64_t)p * S + slot) * F, base + r + 1);
+    }
+  } else {
+    for (uint32_t r = 0; r < R && ok; ++r) {
+      const uint32_t slot = r % S;
+      ok = snac::consume(ctx.flags + (uint64_t)slot * F, n, (uint64_t)S * F, base + r + 1, w);
+      if (!ok) break;
+      for (uint32_t i = threadIdx.x; i < B; i += TH) {
+        float acc = stage[(uint64_t)slot * B + i];
+        for (int p = 1; p < n; ++p) acc = acc + stage[((uint64_t)p * S + slot) * B + i];
+        out[(uint64_t)r * B + i] = acc;
+      }
+      snac::notify(ctx.flags + ((uint64_t)n * S + slot) * F, base + r + 1);
+    }
+  }
+  if (threadIdx.x == 0) ok_out[blockIdx.x] = ok ? 1u : 0u;
+}
+
 // N dispatch tables (N in {1, 2, 3, 4, 8, 16})
 #define SNAC_DISPATCH_N(MACRO) MACRO(1) MACRO(2) MACRO(3) MACRO(4) MACRO(8) MACRO(16)
 
@@ -190,6 +232,18 @@ int devtest_fused_scale_allreduce(const snac_coll_desc* desc, const snac_dev_ctx
     default: return hipErrorInvalidValue;
   }
 #undef SNAC_CASE
+  return hipGetLastError();
+}
+
+// n producers + 1 consumer over S slots for R rounds of B floats; stage
+// holds n * S * B floats, out R * B, ok_out n + 1 words; flags from
+// base + 1 upward (base must exceed every value the flags already hold).
+int devtest_flags(const snac_dev_ctx* ctx, const snac_coll_desc* xs, float* stage, float* out, int n, uint32_t S,
+                  uint32_t R, uint32_t B, uint64_t base, uint32_t* ok_out, hipStream_t s) {
+  if (!ctx || !xs || n < 1 || n > SNAC_MAX_RANKS || S < 1 || ((uint64_t)n + 1) * S > ctx->nflags)
+    return hipErrorInvalidValue;
+  if (!fits((const void*)&flags_kernel, n + 1)) return -1;
+  hipLaunchKernelGGL(flags_kernel, dim3(n + 1), dim3(TH), 0, s, *ctx, *xs, stage, out, n, S, R, B, base, ok_out);
   return hipGetLastError();
 }
 

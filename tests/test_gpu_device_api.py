@@ -34,6 +34,8 @@ def dev():
         "devtest_reduce_slices": [_DP, _I, _U64, _I, _I, _VP],
         "devtest_collective": [_DP, _CP, _I, _I, _I, _I, _I, _VP, _VP],
         "devtest_fused_scale_allreduce": [_DP, _CP, _DP, _U64, _VP, _I, _VP, _VP],
+        "devtest_flags": [_CP, _DP, _VP, _VP, _I, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, _U64, _VP,
+                          _VP],
     }
     for name, args in sigs.items():
         f = getattr(lib, name)
@@ -265,5 +267,39 @@ def test_fused_scale_allreduce(dev, dtype, n):
                 assert_same(b.download(np_dtype(dtype)), want, dtype, f"fused N={n} out[{r}] rep {rep}")
             assert check.guards_ok()
             assert_same(check.download(np_dtype(dtype)), want, dtype, f"fused N={n} read-back rep {rep}")
+    finally:
+        snac.snac_finalize(ctx)
+
+
+# ------------------------------------------ SNAC primitives used by hand
+@pytest.mark.parametrize("n,S", [(2, 2), (8, 2), (8, 3)])
+def test_stage_notify_consume_by_hand(dev, n, S):
+    """n producer workgroups stage blocks and notify; one consumer consumes
+    every rank's flag, reduces the staged blocks and frees the slot; slots
+    are reused (R > S) and the sequence numbers keep rising across calls."""
+    import torch
+
+    R, B = 7, 5000
+    xs = [wl.uniform_f32(R * B, wl.CFG_TEST, r, seed=n * 10 + S) for r in range(n)]
+    ctx = snac.snac_init(n, 0)
+    try:
+        xb = [DevBuf(x.nbytes, data=x) for x in xs]
+        xsd = snac.snac_coll_desc()
+        for r, b in enumerate(xb):
+            xsd.src[r] = b.ptr
+        stage = torch.zeros(n * S * B, dtype=torch.float32, device="cuda")
+        dctx = snac.snac_get_device_context(ctx)
+        want = np.stack([oracle.reduce_n([x[r * B:(r + 1) * B] for x in xs], "f32") for r in range(R)])
+        base = 0
+        for call in range(2):
+            out = torch.full((R * B,), -1.0, dtype=torch.float32, device="cuda")
+            ok = ok_buffer(n + 1)
+            launch(dev.devtest_flags(ctypes.byref(dctx), ctypes.byref(xsd), stage.data_ptr(), out.data_ptr(), n, S, R,
+                                     B, base, ok.data_ptr(), None))
+            torch.cuda.synchronize()
+            snac.snac_check(ctx)
+            assert int(ok.sum().item()) == n + 1
+            assert_same(out.cpu().numpy().reshape(R, B), want, "f32", f"n={n} S={S} call {call}")
+            base += R
     finally:
         snac.snac_finalize(ctx)
