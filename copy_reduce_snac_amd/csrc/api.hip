@@ -3,7 +3,9 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cstdarg>
+#include <cstdlib>
 #include <iterator>
 #include <vector>
 #include <cstdio>
@@ -58,7 +60,52 @@ snac_status hip_fail(hipError_t e, const char* what) {
   return fail(SNAC_E_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-snac_tuning g_tuning = {0, 0, 0, 0, 0, 0, 0, {0}};
+// Process-wide tuning, initialised from the environment when the library
+// loads: SNAC_WGS_PER_CU, SNAC_CACHE_POLICY, SNAC_PIPELINE_TILE_BYTES,
+// SNAC_PIPELINE_LOOKAHEAD, SNAC_SPIN_LIMIT_LOG2, SNAC_COPY_MULTICAST (decimal
+// integers; a value snac_set_tuning would reject, or that does not parse,
+// is ignored).
+bool tuning_valid(const snac_tuning& t) {
+  return t.wgs_per_cu >= 0 && t.wgs_per_cu <= 32 && t.cache_policy >= 0 && t.cache_policy <= 4 &&
+         t.pipeline_tile_bytes >= 0 && t.pipeline_tile_bytes % 4096 == 0 && t.pipeline_lookahead >= 0 &&
+         t.spin_limit_log2 >= 0 && t.spin_limit_log2 <= 40 && t.debug_drop_notify >= 0 &&
+         t.debug_drop_notify <= SNAC_MAX_RANKS && t.copy_multicast >= 0 && t.copy_multicast <= 2;
+}
+
+int env_int(const char* name, bool* ok) {
+  const char* v = std::getenv(name);
+  *ok = false;
+  if (!v || !*v) return 0;
+  char* end = nullptr;
+  const long x = std::strtol(v, &end, 10);
+  if (*end != '\0' || x < INT32_MIN || x > INT32_MAX) return 0;
+  *ok = true;
+  return (int)x;
+}
+
+snac_tuning tuning_from_env() {
+  snac_tuning t{0, 0, 0, 0, 0, 0, 0, {0}};
+  struct {
+    const char* name;
+    int32_t* field;
+  } vars[] = {{"SNAC_WGS_PER_CU", &t.wgs_per_cu},
+              {"SNAC_CACHE_POLICY", &t.cache_policy},
+              {"SNAC_PIPELINE_TILE_BYTES", &t.pipeline_tile_bytes},
+              {"SNAC_PIPELINE_LOOKAHEAD", &t.pipeline_lookahead},
+              {"SNAC_SPIN_LIMIT_LOG2", &t.spin_limit_log2},
+              {"SNAC_COPY_MULTICAST", &t.copy_multicast}};
+  for (auto& v : vars) {
+    bool ok = false;
+    const int x = env_int(v.name, &ok);
+    if (!ok) continue;
+    const int32_t before = *v.field;
+    *v.field = x;
+    if (!tuning_valid(t)) *v.field = before;
+  }
+  return t;
+}
+
+snac_tuning g_tuning = tuning_from_env();
 
 constexpr uint32_t kMaxPipeTile = 1024u * 1024u;
 constexpr uint32_t kMinPipeTile = 4096u;

@@ -403,7 +403,11 @@ snac_status snac_plan(snac_coll coll, int nranks, snac_dtype dtype, size_t bytes
 
 /*
  * Process-wide launch parameters (Purlin 0.6.4 "Key Idea" mentions tuning
- * for peak performance).  Zero fields select the defaults.
+ * for peak performance).  Zero fields select the defaults.  When the library
+ * loads, the fields start from the environment variables SNAC_WGS_PER_CU,
+ * SNAC_CACHE_POLICY, SNAC_PIPELINE_TILE_BYTES, SNAC_PIPELINE_LOOKAHEAD,
+ * SNAC_SPIN_LIMIT_LOG2 and SNAC_COPY_MULTICAST (decimal integers; values
+ * snac_set_tuning would reject are ignored).
  */
 typedef struct snac_tuning {
   int32_t wgs_per_cu;      /* workgroups per compute unit in the persistent grid

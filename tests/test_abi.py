@@ -290,3 +290,17 @@ def test_invalid_tuning_rules_rejected(bad):
 def test_reduce_mode_argument_errors_without_gpu():
     _expect(snac.SNAC_E_ARG, snac.snac_all_reduce_ex, None, [0x1000], [0x2000], 16, "f32", "atomic")
     _expect(snac.SNAC_E_ARG, snac.snac_all_reduce_ex, None, [0x1000], [0x2000], 16, "f32", 7)
+
+
+def test_tuning_from_environment():
+    """SNAC_* variables seed the process-wide tuning; invalid ones are ignored."""
+    import subprocess
+    import sys
+
+    code = ("import sys; sys.path.insert(0, %r); import copy_reduce_snac_amd as s; t = s.snac_get_tuning(); "
+            "print(t['wgs_per_cu'], t['cache_policy'], t['pipeline_tile_bytes'], t['spin_limit_log2'], "
+            "t['copy_multicast'])" % ROOT)
+    env = dict(os.environ, SNAC_WGS_PER_CU="3", SNAC_CACHE_POLICY="4", SNAC_PIPELINE_TILE_BYTES="8192",
+               SNAC_SPIN_LIMIT_LOG2="99", SNAC_COPY_MULTICAST="x1")
+    out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, check=True).stdout
+    assert out.split() == ["3", "4", "8192", "0", "0"]
