@@ -56,7 +56,7 @@ class snac_tuning(ctypes.Structure):
         ("spin_limit_log2", ctypes.c_int32),
         ("debug_drop_notify", ctypes.c_int32),
         ("copy_multicast", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 1),
+        ("debug_producer_delay", ctypes.c_int32),
     ]
 
 
@@ -347,7 +347,7 @@ def snac_plan(coll: int, nranks: int, dtype, nbytes: int = 0, counts: Iterable[i
 def snac_get_tuning() -> dict:
     t = snac_tuning()
     _check(lib().snac_get_tuning(ctypes.byref(t)), "snac_get_tuning")
-    return {name: getattr(t, name) for name, _ in snac_tuning._fields_ if name != "reserved"}
+    return {name: getattr(t, name) for name, _ in snac_tuning._fields_}
 
 
 def snac_set_tuning(**kw) -> None:
@@ -384,4 +384,4 @@ def snac_get_tuning_rules() -> list[dict]:
 def snac_tuning_lookup(coll: int, nranks: int, esize: int, nbytes: int) -> dict:
     t = snac_tuning()
     _check(lib().snac_tuning_lookup(coll, nranks, esize, nbytes, ctypes.byref(t)), "snac_tuning_lookup")
-    return {name: getattr(t, name) for name, _ in snac_tuning._fields_ if name != "reserved"}
+    return {name: getattr(t, name) for name, _ in snac_tuning._fields_}

@@ -69,7 +69,8 @@ bool tuning_valid(const snac_tuning& t) {
   return t.wgs_per_cu >= 0 && t.wgs_per_cu <= 32 && t.cache_policy >= 0 && t.cache_policy <= 4 &&
          t.pipeline_tile_bytes >= 0 && t.pipeline_tile_bytes % 4096 == 0 && t.pipeline_lookahead >= 0 &&
          t.spin_limit_log2 >= 0 && t.spin_limit_log2 <= 40 && t.debug_drop_notify >= 0 &&
-         t.debug_drop_notify <= SNAC_MAX_RANKS && t.copy_multicast >= 0 && t.copy_multicast <= 2;
+         t.debug_drop_notify <= SNAC_MAX_RANKS && t.copy_multicast >= 0 && t.copy_multicast <= 2 &&
+         t.debug_producer_delay >= 0 && t.debug_producer_delay <= 100000;
 }
 
 int env_int(const char* name, bool* ok) {
@@ -84,7 +85,7 @@ int env_int(const char* name, bool* ok) {
 }
 
 snac_tuning tuning_from_env() {
-  snac_tuning t{0, 0, 0, 0, 0, 0, 0, {0}};
+  snac_tuning t{0, 0, 0, 0, 0, 0, 0, 0};
   struct {
     const char* name;
     int32_t* field;
@@ -463,6 +464,8 @@ snac_status snac_set_tuning(const snac_tuning* in) {
   if (in->debug_drop_notify < 0 || in->debug_drop_notify > SNAC_MAX_RANKS)
     return fail(SNAC_E_ARG, "debug_drop_notify out of range");
   if (in->copy_multicast < 0 || in->copy_multicast > 2) return fail(SNAC_E_ARG, "copy_multicast out of range [0, 2]");
+  if (in->debug_producer_delay < 0 || in->debug_producer_delay > 100000)
+    return fail(SNAC_E_ARG, "debug_producer_delay out of range [0, 100000]");
   g_tuning = *in;
   return ok();
 }
@@ -719,6 +722,7 @@ snac_status snac_pipeline_scale_reduce(snac_ctx* ctx, const void* const* x, void
   a.lookahead = (uint32_t)g_tuning.pipeline_lookahead;
   a.spin_limit_log2 = (uint32_t)(g_tuning.spin_limit_log2 ? g_tuning.spin_limit_log2 : kDefaultSpinLog2);
   a.drop_notify = g_tuning.debug_drop_notify;
+  a.producer_delay_us = (uint32_t)g_tuning.debug_producer_delay;
   hipError_t err = launch_pipeline(a, dtype == SNAC_BF16, launch_cfg(SNAC_RULE_PIPELINE, n, e, count * (uint64_t)e),
                                    (hipStream_t)stream, nullptr);
   if (err != hipSuccess) return hip_fail(err, "pipeline launch");

@@ -56,6 +56,7 @@ struct PipeArgs {
   uint32_t grid;
   uint32_t spin_limit_log2;
   int32_t drop_notify;  // r+1: rank r never notifies (test hook)
+  uint32_t producer_delay_us;  // > 0: some producer items sleep first (test hook)
   // Derived on the host so that every loop and branch condition in the
   // kernel is a scalar (kernel-argument) value: a condition the compiler
   // cannot prove uniform lets it restructure a loop that holds barriers.

@@ -62,6 +62,10 @@ __device__ __forceinline__ WaitCtl pipe_wait(const PipeArgs& a) {
   return WaitCtl{&a.ctrl[kCtrlStatus], a.abort_word, a.spin_limit_log2};
 }
 
+// The constant-rate wall clock (s_memrealtime), 100 MHz on MI300-family
+// parts; only the test-hook delay below uses it.
+constexpr uint64_t kWallTicksPerUs = 100;
+
 // y = 0.5 * x + r on one 16-byte unit, rounded to T.
 template <typename T>
 __device__ __forceinline__ u32x4 scale_unit(u32x4 x, float r) {
@@ -102,6 +106,13 @@ __device__ void stage_item(const PipeArgs& a, uint32_t t, uint32_t gslot, uint32
     const uint32_t ok = uniform(*s_ok);
     __syncthreads();
     if (ok == 0) return;
+  }
+  if (a.producer_delay_us) {  // test hook: skew a quarter of the producers
+    const uint32_t h = (t * 0x9E3779B1u) ^ (r * 0x85EBCA6Bu);
+    if ((h >> 29) < 2) {
+      const uint64_t until = wall_clock64() + (uint64_t)a.producer_delay_us * kWallTicksPerUs;
+      while (wall_clock64() < until) __builtin_amdgcn_s_sleep(8);
+    }
   }
   const uint64_t e0 = (uint64_t)t * a.tile_elems;
   const uint32_t nbytes = tile_count(a, t) * E;

@@ -427,7 +427,10 @@ typedef struct snac_tuning {
                                   0 library default, 1 one job per source
                                   writing all N destinations (one read),
                                   2 one job per (source, destination) */
-  int32_t reserved[1];
+  int32_t debug_producer_delay; /* test hook: when > 0, a quarter of the pipeline's
+                                    producer items (chosen by a hash of tile and
+                                    rank) first sleep about this many microseconds,
+                                    to skew producers against consumers */
 } snac_tuning;
 
 snac_status snac_get_tuning(snac_tuning* out);
