@@ -108,11 +108,11 @@ snac_tuning tuning_from_env() {
 
 snac_tuning g_tuning = tuning_from_env();
 
-constexpr uint32_t kMaxPipeTile = 1024u * 1024u;
+constexpr uint32_t kMaxPipeTile = 2048u * 1024u;
 constexpr uint32_t kMinPipeTile = 4096u;
 constexpr uint32_t kMinAutoSlots = 64u;
 constexpr uint32_t kMaxFlagSlots = 4096u;
-constexpr uint64_t kTargetTiles = 128u;  // tiles per message the pipeline aims for
+constexpr uint64_t kTargetTiles = 64u;  // tiles per message the pipeline aims for
 constexpr uint32_t kMinSplitTile = 65536u;  // ... but no smaller tiles than this
 constexpr size_t kDefaultStaging = 64u * 1024u * 1024u;
 constexpr int kDefaultSpinLog2 = 22;
@@ -128,10 +128,11 @@ constexpr int kDefaultSpinLog2 = 22;
 // streaming loads when they are reused; no difference when they are not).
 // The pipeline runs one workgroup per CU up to 8 MiB per rank (fewer
 // waiting workgroups: at 1 MiB 24.6 us against 31.3, at 4 MiB 60 against
-// 94) and above that picks its own grid (4 per CU when the ring holds the
-// message, else 2; 4 is 20-30 % faster at 4096x8192).
+// 94) and two above that (with 64 tiles per message: bf16 4096x8192 0.34 ms
+// against 0.39 at four per CU with 128 tiles).
 const snac_tuning_rule kBuiltinRules[] = {
     {SNAC_RULE_PIPELINE, 1, SNAC_MAX_RANKS, 0, 0, 8u << 20, 1, 0},
+    {SNAC_RULE_PIPELINE, 1, SNAC_MAX_RANKS, 0, (8u << 20) + 1, UINT64_MAX, 2, 0},
     {SNAC_COLL_ALL_GATHER, 1, SNAC_MAX_RANKS, 0, 0, UINT64_MAX, 2, 2},
     {SNAC_COLL_ALL_GATHER_V, 1, SNAC_MAX_RANKS, 0, 0, UINT64_MAX, 2, 2},
     {SNAC_RULE_ANY_REDUCE, 4, SNAC_MAX_RANKS, 0, 0, UINT64_MAX, 1, 1},
@@ -476,7 +477,7 @@ snac_status snac_init(int nranks, size_t staging_bytes_per_rank, snac_stream str
   if (nranks < 1 || nranks > SNAC_MAX_RANKS) return fail(SNAC_E_ARG, "nranks %d outside 1..%d", nranks, SNAC_MAX_RANKS);
   const size_t staging = staging_bytes_per_rank ? staging_bytes_per_rank : kDefaultStaging;
   // pipeline tile: the tuning value, else the largest power of two up to
-  // 1 MiB that still leaves at least 64 slots in the ring
+  // 2 MiB that still leaves at least 64 slots in the ring
   uint32_t tile = (uint32_t)g_tuning.pipeline_tile_bytes;
   if (!tile) {
     tile = kMaxPipeTile;
@@ -707,8 +708,10 @@ snac_status snac_pipeline_scale_reduce(snac_ctx* ctx, const void* const* x, void
   a.abort_word = ctx->abort_dev;
   // Tile of this call: the context's, halved (doubling the slots of the same
   // ring) while the message would have fewer than kTargetTiles tiles, down
-  // to 64 KiB; on MI355X about 128 tiles per message balanced producers and
-  // consumers best, and smaller tiles only add per-item overhead.
+  // to 64 KiB.  On MI355X about 64 tiles per message (1 MiB per rank for
+  // bf16 4096x8192, 2 MiB for f32) with two workgroups per CU ran best --
+  // bigger items mean fewer release and acquire fences, which serialise
+  // GPU-wide -- and smaller tiles only add per-item overhead.
   uint32_t tile = ctx->tile_bytes, slots = ctx->slots;
   if (!g_tuning.pipeline_tile_bytes) {
     while (tile / 2 >= kMinSplitTile && (uint64_t)slots * 2 <= ctx->flag_slots &&

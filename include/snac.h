@@ -140,16 +140,18 @@ const char* snac_last_error(void);
  *
  *   nranks                  1 .. SNAC_MAX_RANKS
  *   staging_bytes_per_rank  size of each rank's staging ring, used by the
- *                           device-side SNAC pipeline.  0 selects the
+ *                           device-side SNAC pipeline and as the accumulator
+ *                           of the atomic AllReduce mode.  0 selects the
  *                           default (64 MiB).  It is split into slots of the
  *                           pipeline tile size: the tuning value if set,
- *                           else the largest power of two up to 1 MiB that
+ *                           else the largest power of two up to 2 MiB that
  *                           leaves at least 64 slots (minimum 4 KiB).  Without
  *                           a tuning value a call halves the tile (doubling
  *                           the slots) while its message would have fewer
- *                           than 128 tiles, down to 64 KiB.  The size must be a multiple of
- *                           the tile and give at least 2 slots.  A ring that
- *                           holds a whole message runs fastest.
+ *                           than 64 tiles, down to 64 KiB.  The size must be
+ *                           a multiple of the tile and give at least 2
+ *                           slots.  A ring that holds a whole message runs
+ *                           fastest.
  *   stream                  signals are cleared on this stream.
  *   out                     receives the context; on error *out is NULL.
  *

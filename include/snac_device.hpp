@@ -369,14 +369,20 @@ __device__ __forceinline__ WaitCtl wait_ctl(const snac_dev_ctx& c) {
   return WaitCtl{c.status, c.abort_word, c.spin_limit_log2};
 }
 
-// One lane waits until *flag >= target with relaxed agent-scope loads and
-// s_sleep back-off.  Returns false, with the status word set, after
-// 2^spin_limit_log2 polls (SNAC_E_TIMEOUT), when the abort word is set
-// (SNAC_E_ABORTED), or at once when an error is already latched -- so every
-// wait ends.  The caller adds the acquire fence where it needs one.
+// One lane waits until *flag >= target with relaxed agent-scope loads: 16
+// polls 64 clocks apart (each poll is a memory round trip, so this covers
+// the first several microseconds, where small messages finish), then
+// exponential s_sleep back-off to 512 clocks between polls (with hundreds of
+// workgroups waiting, tight polling took enough of the memory system to
+// slow the producers they waited for -- up to 3x on MI355X).
+// Returns false, with the status word set, after 2^spin_limit_log2 polls
+// (SNAC_E_TIMEOUT), when the abort word is set (SNAC_E_ABORTED), or at once
+// when an error is already latched -- so every wait ends.  The caller adds
+// the acquire fence where it needs one.
 __device__ inline bool wait_geq(const uint64_t* flag, uint64_t target, const WaitCtl& w) {
   const uint64_t limit = 1ull << w.spin_limit_log2;
   uint64_t spins = 0;
+  uint32_t naps = 1;  // s_sleep(1) rounds between polls
   while (ld_relaxed(flag) < target) {
     if ((spins & 15u) == 15u) {
       if (ld_relaxed(w.status) != 0) return false;
@@ -390,7 +396,8 @@ __device__ inline bool wait_geq(const uint64_t* flag, uint64_t target, const Wai
       latch_status(w.status, kStatusTimeout);
       return false;
     }
-    __builtin_amdgcn_s_sleep(1);
+    for (uint32_t i = 0; i < naps; ++i) __builtin_amdgcn_s_sleep(1);
+    if (spins >= 16 && naps < 8) naps <<= 1;
   }
   return true;
 }

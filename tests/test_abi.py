@@ -246,7 +246,7 @@ def test_builtin_tuning_rules_and_lookup():
     assert snac.snac_tuning_lookup(snac.SNAC_RULE_ATOM_COPY, 1, 1, 1)["cache_policy"] == 1
     # the pipeline: one WG per CU for small messages, its own grid above 8 MiB
     assert snac.snac_tuning_lookup(snac.SNAC_RULE_PIPELINE, 8, 2, MiB)["wgs_per_cu"] == 1
-    assert snac.snac_tuning_lookup(snac.SNAC_RULE_PIPELINE, 8, 2, 64 * MiB)["wgs_per_cu"] == 0
+    assert snac.snac_tuning_lookup(snac.SNAC_RULE_PIPELINE, 8, 2, 64 * MiB)["wgs_per_cu"] == 2
 
 
 def test_tuning_rules_first_match_and_override():
