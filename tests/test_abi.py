@@ -237,7 +237,8 @@ def test_builtin_tuning_rules_and_lookup():
     MiB = 1 << 20
     # measured defaults: big reduces one WG per CU, small reduces and copies two, streaming
     assert snac.snac_tuning_lookup(snac.SNAC_COLL_ALL_REDUCE, 8, 2, 256 * MiB)["wgs_per_cu"] == 1
-    assert snac.snac_tuning_lookup(snac.SNAC_COLL_REDUCE_SCATTER_V, 4, 4, 1)["wgs_per_cu"] == 1
+    assert snac.snac_tuning_lookup(snac.SNAC_COLL_REDUCE_SCATTER, 4, 4, 1)["wgs_per_cu"] == 1
+    assert snac.snac_tuning_lookup(snac.SNAC_COLL_REDUCE_SCATTER_V, 8, 4, 1)["wgs_per_cu"] == 2
     assert snac.snac_tuning_lookup(snac.SNAC_RULE_ATOM_REDUCE, 2, 4, 1)["wgs_per_cu"] == 2
     assert snac.snac_tuning_lookup(snac.SNAC_COLL_ALL_GATHER, 8, 1, 1)["wgs_per_cu"] == 2
     # AllGather(V) reads inputs with cached loads (streaming stores)
