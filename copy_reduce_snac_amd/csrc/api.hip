@@ -137,10 +137,12 @@ const snac_tuning_rule kBuiltinRules[] = {
     {SNAC_COLL_ALL_GATHER_V, 1, SNAC_MAX_RANKS, 0, 0, UINT64_MAX, 2, 2},
     // ReduceScatterV's uneven jobs: 2 per CU measured 4 % faster (0.219 ms
     // against 0.228 for f32 N=8, 128 MiB per rank); ReduceScatter itself
-    // and AllReduce are fastest at one
+    // and AllReduce are fastest at one from three sources up (N=3 AllReduce
+    // bf16 256 MiB: 6.01 TB/s at one, 5.75 at two); two sources at two
+    // (6.00 against 5.94)
     {SNAC_COLL_REDUCE_SCATTER_V, 4, SNAC_MAX_RANKS, 0, 0, UINT64_MAX, 2, 1},
-    {SNAC_RULE_ANY_REDUCE, 4, SNAC_MAX_RANKS, 0, 0, UINT64_MAX, 1, 1},
-    {SNAC_RULE_ANY_REDUCE, 1, 3, 0, 0, UINT64_MAX, 2, 1},
+    {SNAC_RULE_ANY_REDUCE, 3, SNAC_MAX_RANKS, 0, 0, UINT64_MAX, 1, 1},
+    {SNAC_RULE_ANY_REDUCE, 1, 2, 0, 0, UINT64_MAX, 2, 1},
     {SNAC_RULE_ANY_COPY, 1, SNAC_MAX_RANKS, 0, 0, UINT64_MAX, 2, 1},
 };
 
