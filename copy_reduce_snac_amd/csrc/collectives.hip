@@ -192,6 +192,18 @@ hipError_t launch_collective(const CollDesc& d, bool aligned, bool small, uint64
 constexpr int kAtomicThreads = 256;
 constexpr int kAtomicUnits = 4;  // 16-byte units per lane per item
 
+// The accumulator is kept lane-major within each group of 64 units: element
+// j of unit l of a group (L elements per unit) sits at word j * 64 + l, so
+// the j-th atomic of a wave covers 64 consecutive words -- two 128-byte
+// lines -- instead of 64 words 32 or 16 bytes apart.  Only the two kernels
+// below see this layout.
+template <uint32_t L>
+__device__ __forceinline__ uint64_t acc_index(uint64_t e) {
+  const uint64_t g = e / (64u * L);
+  const uint32_t r = (uint32_t)(e - g * 64u * L);
+  return g * 64u * L + (uint64_t)(r % L) * 64u + r / L;
+}
+
 template <typename T, bool VEC>
 __global__ __launch_bounds__(kAtomicThreads) void atomic_accumulate_kernel(const CollDesc d, float* acc,
                                                                            uint64_t first, uint64_t elems,
@@ -210,12 +222,13 @@ __global__ __launch_bounds__(kAtomicThreads) void atomic_accumulate_kernel(const
       if (VEC && e0 + L <= elems) {
         UnitAcc<T> v;
         v.set(ld16<kCacheStream>(src + e0 * E));
+        float* a = acc + acc_index<L>(e0);
 #pragma unroll
         for (uint32_t j = 0; j < L; ++j)
-          __hip_atomic_fetch_add(acc + e0 + j, v.a[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_fetch_add(a + j * 64u, v.a[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       } else {
         for (uint32_t j = 0; j < L && e0 + j < elems; ++j)
-          __hip_atomic_fetch_add(acc + e0 + j, load_elem<T>(src + (e0 + j) * E), __ATOMIC_RELAXED,
+          __hip_atomic_fetch_add(acc + acc_index<L>(e0 + j), load_elem<T>(src + (e0 + j) * E), __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
       }
     }
@@ -232,13 +245,16 @@ __global__ __launch_bounds__(kAtomicThreads) void atomic_finish_kernel(const Col
   for (uint64_t e0 = ((uint64_t)blockIdx.x * kAtomicThreads + threadIdx.x) * L; e0 < elems; e0 += stride) {
     if (VEC && e0 + L <= elems) {
       UnitAcc<T> v;
+      const float* a = acc + acc_index<L>(e0);
 #pragma unroll
-      for (uint32_t j = 0; j < L; ++j) v.a[j] = acc[e0 + j];
+      for (uint32_t j = 0; j < L; ++j) v.a[j] = a[j * 64u];
       const u32x4 w = v.out();
       for (int k = 0; k < d.ndst; ++k) st16<kCacheStream>(static_cast<char*>(d.dst[k]) + (first + e0) * E, w);
     } else {
-      for (uint32_t j = 0; j < L && e0 + j < elems; ++j)
-        for (int k = 0; k < d.ndst; ++k) store_elem<T>(static_cast<char*>(d.dst[k]) + (first + e0 + j) * E, acc[e0 + j]);
+      for (uint32_t j = 0; j < L && e0 + j < elems; ++j) {
+        const float x = acc[acc_index<L>(e0 + j)];
+        for (int k = 0; k < d.ndst; ++k) store_elem<T>(static_cast<char*>(d.dst[k]) + (first + e0 + j) * E, x);
+      }
     }
   }
 }
@@ -256,7 +272,11 @@ hipError_t launch_atomic_allreduce(const CollDesc& d, float* acc, uint64_t first
   const int cus = device_cu_count();
   uint64_t grid = (uint64_t)(cus > 0 ? cus : 1) * 4;
   if (grid > items) grid = items;
-  hipError_t e = fill_u64(reinterpret_cast<uint64_t*>(acc), (elems + 1) / 2, 0, stream);
+  // the accumulator's words of a partial last group lie past elems: clear
+  // whole groups (the chunk capacity is whole tiles, so they fit)
+  const uint64_t group_e = 64u * (16u / (uint64_t)d.esize);
+  const uint64_t acc_words = (elems + group_e - 1) / group_e * group_e;
+  hipError_t e = fill_u64(reinterpret_cast<uint64_t*>(acc), acc_words / 2, 0, stream);
   if (e != hipSuccess) return e;
   const bool bf = d.esize == 2;
   if (bf) {
