@@ -133,17 +133,23 @@ constexpr int kDefaultSpinLog2 = 22;
 const snac_tuning_rule kBuiltinRules[] = {
     {SNAC_RULE_PIPELINE, 1, SNAC_MAX_RANKS, 0, 0, 8u << 20, 1, 0},
     {SNAC_RULE_PIPELINE, 1, SNAC_MAX_RANKS, 0, (8u << 20) + 1, UINT64_MAX, 2, 0},
-    {SNAC_COLL_ALL_GATHER, 1, SNAC_MAX_RANKS, 0, 0, UINT64_MAX, 2, 2},
-    {SNAC_COLL_ALL_GATHER_V, 1, SNAC_MAX_RANKS, 0, 0, UINT64_MAX, 2, 2},
+    // multicast copies: cached loads, streaming stores.  AllGather bf16 N=8,
+    // 16 MiB per rank in: 180 us against 210 with streaming loads when a
+    // producer kernel had just written the inputs, 228 against 235 right
+    // after the ReduceScatter that wrote them
+    {SNAC_COLL_ALL_GATHER, 1, SNAC_MAX_RANKS, 0, 0, UINT64_MAX, 0, 2},
+    {SNAC_COLL_ALL_GATHER_V, 1, SNAC_MAX_RANKS, 0, 0, UINT64_MAX, 0, 2},
     // ReduceScatterV's uneven jobs: 2 per CU measured 4 % faster (0.219 ms
-    // against 0.228 for f32 N=8, 128 MiB per rank); ReduceScatter itself
-    // and AllReduce are fastest at one from three sources up (N=3 AllReduce
-    // bf16 256 MiB: 6.01 TB/s at one, 5.75 at two); two sources at two
-    // (6.00 against 5.94)
+    // against 0.228 for f32 N=8, 128 MiB per rank) than the kernel default
     {SNAC_COLL_REDUCE_SCATTER_V, 4, SNAC_MAX_RANKS, 0, 0, UINT64_MAX, 2, 1},
-    {SNAC_RULE_ANY_REDUCE, 3, SNAC_MAX_RANKS, 0, 0, UINT64_MAX, 1, 1},
-    {SNAC_RULE_ANY_REDUCE, 1, 2, 0, 0, UINT64_MAX, 2, 1},
-    {SNAC_RULE_ANY_COPY, 1, SNAC_MAX_RANKS, 0, 0, UINT64_MAX, 2, 1},
+    // everything else: the kernel's workgroups per CU, which depend on the
+    // message's tile size and source count, and streaming accesses.  Cached
+    // loads measured up to 30 % faster at 4-32 MiB per rank, but only when
+    // the same inputs were read again call after call; with inputs freshly
+    // written by a producer kernel they gained nothing, and at 64 MiB they
+    // lost 17-30 %
+    {SNAC_RULE_ANY_REDUCE, 1, SNAC_MAX_RANKS, 0, 0, UINT64_MAX, 0, 1},
+    {SNAC_RULE_ANY_COPY, 1, SNAC_MAX_RANKS, 0, 0, UINT64_MAX, 0, 1},
 };
 
 std::vector<snac_tuning_rule> g_rules(std::begin(kBuiltinRules), std::end(kBuiltinRules));

@@ -145,6 +145,21 @@ static KernelFn small_kernel(const CollDesc& d, bool aligned) {
                  : &copy_kernel<kCacheStream, false, kCopyThreads, true>;
 }
 
+// Workgroups per CU when neither a rule nor the process-wide tuning names
+// one.  Measured on MI355X: the 1:1 read/write streams of 16 KiB tiles run
+// fastest with few workgroups per CU (more concurrent write streams lower
+// HBM efficiency): one for reduces of three or more sources, two otherwise.
+// A small message instead wants its tiles spread wide, about one per
+// workgroup: four per CU for reduces and multicast copies (AllReduce
+// bf16 N=8 at 2 MiB per rank 10 % faster than at one per CU, AllGather at
+// 256 KiB per rank in 28 % faster than at two), two for other copies,
+// whose workgroups each rebuild a larger job table.
+static int default_wgs_per_cu(const CollDesc& d, bool small) {
+  const bool reduce = coll_is_reduce(d.coll);
+  if (small) return reduce || is_multicast_copy(d) ? 4 : 2;
+  return reduce && d.nsrc >= 3 ? 1 : 2;
+}
+
 hipError_t launch_collective(const CollDesc& d, bool aligned, bool small, uint64_t tiles, const LaunchCfg& cfg,
                              hipStream_t stream) {
   if (tiles == 0) return hipSuccess;
@@ -166,12 +181,7 @@ hipError_t launch_collective(const CollDesc& d, bool aligned, bool small, uint64
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), threads, 0);
   if (e != hipSuccess) return e;
   if (per_cu < 1) per_cu = 1;
-  // Measured on MI355X: the 1:1 read/write streams run fastest with few
-  // workgroups per CU (more concurrent write streams lower HBM efficiency).
-  // A small message instead wants its tiles spread wide: a small-tile
-  // reduce (one job) up to four workgroups per CU, so each holds about one
-  // tile; copies, whose workgroups each rebuild a larger job table, two.
-  const int want = cfg.wgs_per_cu > 0 ? cfg.wgs_per_cu : (small ? (reduce ? 4 : 2) : (reduce && d.nsrc >= 3 ? 1 : 2));
+  const int want = cfg.wgs_per_cu > 0 ? cfg.wgs_per_cu : default_wgs_per_cu(d, small);
   if (want < per_cu) per_cu = want;
   const int cus = device_cu_count();
   uint64_t grid = (uint64_t)(cus > 0 ? cus : 1) * (uint64_t)per_cu;

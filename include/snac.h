@@ -413,7 +413,10 @@ snac_status snac_plan(snac_coll coll, int nranks, snac_dtype dtype, size_t bytes
  */
 typedef struct snac_tuning {
   int32_t wgs_per_cu;      /* workgroups per compute unit in the persistent grid
-                              (0: 1 for reduces of >= 4 sources, else 2) */
+                              (0: the kernel default -- for messages of at
+                              least one 16 KiB tile per CU, 1 for reduces of
+                              >= 3 sources, else 2; for smaller messages,
+                              4 for reduces and AllGather(V), else 2) */
   int32_t cache_policy;    /* 0 library default (= 1), 1 streaming (non-temporal)
                               loads and stores, 2 streaming stores only,
                               3 streaming loads only, 4 cached loads and stores */
