@@ -124,15 +124,17 @@ class Env:
 
 
     def time_calls_cold(self, fn, steps: int, warmup: int) -> float:
-        """Seconds per call with the inputs evicted from the caches first:
-        a 1 GiB scratch write (untimed) before each event-timed call."""
+        """Seconds per call with the inputs evicted from the caches first: a
+        1 GiB scratch buffer is read (untimed) before each event-timed call.
+        A read, not a write: a write would leave the Infinity Cache full of
+        dirty lines whose write-back the timed call would then pay for."""
         torch = self.torch
-        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=self.dev)
+        scratch = torch.ones(1 << 27, dtype=torch.int64, device=self.dev)
         for _ in range(warmup):
             fn()
         total = 0.0
         for _ in range(steps):
-            scratch.fill_(1)
+            scratch.sum()
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(self.stream)
