@@ -139,10 +139,9 @@ const snac_tuning_rule kBuiltinRules[] = {
     // after the ReduceScatter that wrote them
     {SNAC_COLL_ALL_GATHER, 1, SNAC_MAX_RANKS, 0, 0, UINT64_MAX, 0, 2},
     {SNAC_COLL_ALL_GATHER_V, 1, SNAC_MAX_RANKS, 0, 0, UINT64_MAX, 0, 2},
-    // ReduceScatterV's uneven jobs: 2 per CU measured 4 % faster (0.219 ms
-    // against 0.228 for f32 N=8, 128 MiB per rank) than the kernel default
-    {SNAC_COLL_REDUCE_SCATTER_V, 4, SNAC_MAX_RANKS, 0, 0, UINT64_MAX, 2, 1},
-    // everything else: the kernel's workgroups per CU, which depend on the
+    // everything else (ReduceScatterV included: 205 us at the kernel's one
+    // workgroup per CU against 215 at two, f32 N=8, 128 MiB per rank with
+    // Dirichlet counts): the kernel's workgroups per CU, which depend on the
     // message's tile size and source count, and streaming accesses.  Cached
     // loads measured up to 30 % faster at 4-32 MiB per rank, but only when
     // the same inputs were read again call after call; with inputs freshly
