@@ -209,7 +209,8 @@ bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 struct Plan {
   CollDesc d;
   bool aligned;
-  bool small;  // small-tile kernels (message too small to fill the GPU at 16 KiB tiles)
+  int shape;   // kShape*: 16 KiB tiles, small tiles (message too small to fill the GPU
+               // at 16 KiB tiles), or the 4 KiB streaming shape of big one-to-one copies
   uint64_t tiles;
   uint64_t rule_bytes;  // per-rank input bytes the tuning rules match on
 };
@@ -230,8 +231,8 @@ void finish_plan(Plan& p) {
       if (((uintptr_t)p.d.dst[t] + jb.dst_off) & 15u) aligned = false;
   }
   p.aligned = aligned;
-  auto count_tiles = [&](bool small) {
-    const uint64_t tile = coll_tile_bytes(p.d, small);
+  auto count_tiles = [&](int shape) {
+    const uint64_t tile = coll_tile_bytes(p.d, shape);
     uint64_t tiles = 0;
     for (int j = 0; j < nj; ++j) {
       const Job jb = make_job(p.d, j);
@@ -240,12 +241,17 @@ void finish_plan(Plan& p) {
     }
     return tiles;
   };
-  p.small = false;
-  p.tiles = count_tiles(false);
+  p.shape = kShapeTile;
+  p.tiles = count_tiles(kShapeTile);
   const int cus = device_cu_count();
   if (p.tiles > 0 && cus > 0 && p.tiles < (uint64_t)cus) {
-    p.small = true;
-    p.tiles = count_tiles(true);
+    p.shape = kShapeSmall;
+    p.tiles = count_tiles(kShapeSmall);
+  } else if (p.tiles > 0) {
+    uint64_t job_bytes = 0;
+    for (int j = 0; j < nj; ++j) job_bytes += make_job(p.d, j).bytes;
+    p.shape = large_shape(p.d, job_bytes);
+    if (p.shape != kShapeTile) p.tiles = count_tiles(p.shape);
   }
 }
 
@@ -320,7 +326,7 @@ snac_status run(Plan& p, hipStream_t stream) {
     return ok();
   }
   if (p.tiles == 0) return ok();
-  hipError_t e = launch_collective(p.d, p.aligned, p.small, p.tiles,
+  hipError_t e = launch_collective(p.d, p.aligned, p.shape, p.tiles,
                                    launch_cfg(p.d.coll, p.d.nsrc, p.d.esize, p.rule_bytes), stream);
   if (e != hipSuccess) return hip_fail(e, "collective launch");
   return ok();

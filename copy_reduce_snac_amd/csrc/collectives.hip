@@ -3,7 +3,8 @@
 // snac_device.hpp over the job table of the collective's layout
 // (snac_layout.hpp).  Reduces and one-to-one copies use 256-thread
 // workgroups (4 units of 16 bytes per lane per 16 KiB tile); the small-tile
-// reduce uses 128 threads, multicast copies single waves.
+// reduce uses 128 threads, multicast copies single waves, and one-to-one
+// copies that move at least 1 GiB single waves on 4 KiB tiles.
 #include <hip/hip_runtime.h>
 
 #include "internal.hpp"
@@ -37,11 +38,23 @@ __global__ __launch_bounds__(SMALL ? kSmallReduceThreads : kReduceThreads) void 
 // about 6 % more write bandwidth than 256-thread ones.
 constexpr int kMulticastThreads = 64;
 
-template <int CP, bool ALIGNED, int TH, bool SMALL = false>
+template <int CP, bool ALIGNED, int TH, uint32_t TILE = kTileBytes>
 __global__ __launch_bounds__(TH) void copy_kernel(const CollDesc d) {
-  constexpr uint32_t TILE = SMALL ? TH * 16u : kTileBytes;
   run_copy<TH, CP, ALIGNED, TILE>(d, blockIdx.x, gridDim.x);
 }
+
+// One-to-one copies that move at least kStreamCopyBytes (read plus
+// written): single-wave workgroups on 4 KiB tiles, five per CU when every
+// job is 16-byte aligned, four otherwise.  Measured on three MI355X boxes
+// against 256-thread workgroups on 16 KiB tiles at two per CU: copy 1 GiB
+// 6.29-6.34 against 5.95-6.02 TB/s, AllToAll u32 N=8 128 MiB per rank
+// 5.96-5.97 against 5.58-5.69, AllToAllV with misaligned Dirichlet counts
+// 5.74 against 5.61-5.63.  Below about 512 MiB moved the 16 KiB tiles are
+// faster (copy 64 MiB: 6.05 against 5.75; AllToAll 16 MiB per rank: 5.85
+// against 5.64).
+constexpr int kStreamThreads = 64;
+constexpr uint32_t kStreamTile = 4096;
+constexpr uint64_t kStreamCopyBytes = 1ull << 30;
 
 SNAC_HD bool is_multicast_copy(const CollDesc& d) {
   return (d.coll == kAllGather || d.coll == kAllGatherV) && !d.split_multicast;
@@ -90,28 +103,35 @@ KernelFn reduce_kernel_cp(int n, int cp, bool aligned) {
   }
 }
 
-template <int TH>
+template <int TH, uint32_t TILE = kTileBytes>
 static KernelFn copy_kernel_cp(int cp, bool aligned) {
   if (!aligned) {
-    if (cp == kCached) return &copy_kernel<kCached, false, TH>;
-    if (cp == kCacheStreamStores) return &copy_kernel<kCacheStreamStores, false, TH>;
-    return &copy_kernel<kCacheStream, false, TH>;
+    if (cp == kCached) return &copy_kernel<kCached, false, TH, TILE>;
+    if (cp == kCacheStreamStores) return &copy_kernel<kCacheStreamStores, false, TH, TILE>;
+    return &copy_kernel<kCacheStream, false, TH, TILE>;
   }
   switch (cp) {
-    case kCacheStream: return &copy_kernel<kCacheStream, true, TH>;
-    case kCacheStreamStores: return &copy_kernel<kCacheStreamStores, true, TH>;
-    case kCacheStreamLoads: return &copy_kernel<kCacheStreamLoads, true, TH>;
-    default: return &copy_kernel<kCached, true, TH>;
+    case kCacheStream: return &copy_kernel<kCacheStream, true, TH, TILE>;
+    case kCacheStreamStores: return &copy_kernel<kCacheStreamStores, true, TH, TILE>;
+    case kCacheStreamLoads: return &copy_kernel<kCacheStreamLoads, true, TH, TILE>;
+    default: return &copy_kernel<kCached, true, TH, TILE>;
   }
 }
 
-static int coll_threads(const CollDesc& d, bool small) {
-  if (coll_is_reduce(d.coll)) return small ? kSmallReduceThreads : kReduceThreads;
+static int coll_threads(const CollDesc& d, int shape) {
+  if (coll_is_reduce(d.coll)) return shape == kShapeSmall ? kSmallReduceThreads : kReduceThreads;
+  if (shape == kShapeStream) return kStreamThreads;
   return is_multicast_copy(d) ? kMulticastThreads : kCopyThreads;
 }
 
-uint32_t coll_tile_bytes(const CollDesc& d, bool small) {
-  return small ? (uint32_t)coll_threads(d, true) * 16u : kTileBytes;
+uint32_t coll_tile_bytes(const CollDesc& d, int shape) {
+  if (shape == kShapeSmall) return (uint32_t)coll_threads(d, shape) * 16u;
+  return shape == kShapeStream ? kStreamTile : kTileBytes;
+}
+
+int large_shape(const CollDesc& d, uint64_t job_bytes) {
+  if (coll_is_reduce(d.coll) || is_multicast_copy(d)) return kShapeTile;
+  return 2 * job_bytes >= kStreamCopyBytes ? kShapeStream : kShapeTile;
 }
 
 int device_cu_count() {
@@ -139,10 +159,10 @@ static KernelFn small_kernel(const CollDesc& d, bool aligned) {
                    : reduce_kernel_n<BF16, kCacheStream, false, true>(d.nsrc);
   }
   if (is_multicast_copy(d))
-    return aligned ? &copy_kernel<kCacheStream, true, kMulticastThreads, true>
-                   : &copy_kernel<kCacheStream, false, kMulticastThreads, true>;
-  return aligned ? &copy_kernel<kCacheStream, true, kCopyThreads, true>
-                 : &copy_kernel<kCacheStream, false, kCopyThreads, true>;
+    return aligned ? &copy_kernel<kCacheStream, true, kMulticastThreads, kMulticastThreads * 16u>
+                   : &copy_kernel<kCacheStream, false, kMulticastThreads, kMulticastThreads * 16u>;
+  return aligned ? &copy_kernel<kCacheStream, true, kCopyThreads, kCopyThreads * 16u>
+                 : &copy_kernel<kCacheStream, false, kCopyThreads, kCopyThreads * 16u>;
 }
 
 // Workgroups per CU when neither a rule nor the process-wide tuning names
@@ -154,13 +174,14 @@ static KernelFn small_kernel(const CollDesc& d, bool aligned) {
 // bf16 N=8 at 2 MiB per rank 10 % faster than at one per CU, AllGather at
 // 256 KiB per rank in 28 % faster than at two), two for other copies,
 // whose workgroups each rebuild a larger job table.
-static int default_wgs_per_cu(const CollDesc& d, bool small) {
+static int default_wgs_per_cu(const CollDesc& d, int shape, bool aligned) {
   const bool reduce = coll_is_reduce(d.coll);
-  if (small) return reduce || is_multicast_copy(d) ? 4 : 2;
+  if (shape == kShapeSmall) return reduce || is_multicast_copy(d) ? 4 : 2;
+  if (shape == kShapeStream) return aligned ? 5 : 4;
   return reduce && d.nsrc >= 3 ? 1 : 2;
 }
 
-hipError_t launch_collective(const CollDesc& d, bool aligned, bool small, uint64_t tiles, const LaunchCfg& cfg,
+hipError_t launch_collective(const CollDesc& d, bool aligned, int shape, uint64_t tiles, const LaunchCfg& cfg,
                              hipStream_t stream) {
   if (tiles == 0) return hipSuccess;
   KernelFn fn = nullptr;
@@ -168,20 +189,24 @@ hipError_t launch_collective(const CollDesc& d, bool aligned, bool small, uint64
   const int cp = cfg.cache_policy == 0 ? kCacheStream : (cfg.cache_policy == 4 ? kCached : cfg.cache_policy);
   const bool reduce = coll_is_reduce(d.coll);
   if (reduce && num_jobs(d) > kMaxRanks) return hipErrorInvalidValue;
-  if (small) {
+  if (shape == kShapeSmall) {
     fn = small_kernel(d, aligned);
   } else if (reduce) {
+    if (shape != kShapeTile) return hipErrorInvalidValue;
     fn = d.esize == 4 ? reduce_kernel_cp<F32>(d.nsrc, cp, aligned) : reduce_kernel_cp<BF16>(d.nsrc, cp, aligned);
+  } else if (shape == kShapeStream) {
+    if (is_multicast_copy(d)) return hipErrorInvalidValue;
+    fn = copy_kernel_cp<kStreamThreads, kStreamTile>(cp, aligned);
   } else {
     fn = is_multicast_copy(d) ? copy_kernel_cp<kMulticastThreads>(cp, aligned) : copy_kernel_cp<kCopyThreads>(cp, aligned);
   }
   if (!fn) return hipErrorInvalidValue;
-  const int threads = coll_threads(d, small);
+  const int threads = coll_threads(d, shape);
   int per_cu = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), threads, 0);
   if (e != hipSuccess) return e;
   if (per_cu < 1) per_cu = 1;
-  const int want = cfg.wgs_per_cu > 0 ? cfg.wgs_per_cu : default_wgs_per_cu(d, small);
+  const int want = cfg.wgs_per_cu > 0 ? cfg.wgs_per_cu : default_wgs_per_cu(d, shape, aligned);
   if (want < per_cu) per_cu = want;
   const int cus = device_cu_count();
   uint64_t grid = (uint64_t)(cus > 0 ? cus : 1) * (uint64_t)per_cu;

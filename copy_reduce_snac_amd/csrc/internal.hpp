@@ -15,16 +15,27 @@ struct LaunchCfg {
   int cache_policy;  // kCache*
 };
 
+// Tile shapes of the host-launched collective kernels:
+//   kShapeTile    16 KiB tiles (the default)
+//   kShapeSmall   one 16-byte unit per lane, for a message with fewer
+//                 16 KiB tiles than the GPU has CUs
+//   kShapeStream  one-to-one copies that move at least 1 GiB: single-wave
+//                 workgroups on 4 KiB tiles
+enum Shape : int { kShapeTile = 0, kShapeSmall = 1, kShapeStream = 2 };
+
 // Tile size (bytes of each source per workgroup iteration) of the kernel
-// that serves this descriptor; the host needs it to count tiles.  small:
-// the small-tile kernels (one 16-byte unit per lane) used when a message
-// has fewer 16 KiB tiles than the GPU has CUs.
-uint32_t coll_tile_bytes(const CollDesc& d, bool small);
+// that serves this descriptor in this shape; the host needs it to count
+// tiles.
+uint32_t coll_tile_bytes(const CollDesc& d, int shape);
+
+// The shape of a message that fills the GPU with 16 KiB tiles, given the
+// bytes its jobs copy or reduce (each job's bytes once).
+int large_shape(const CollDesc& d, uint64_t job_bytes);
 
 // Launch the copy or reduce kernel for a collective descriptor.  `tiles` is
-// the total tile count of the layout at coll_tile_bytes(d, small) (computed
+// the total tile count of the layout at coll_tile_bytes(d, shape) (computed
 // on the host with the same layout functions the kernel uses).
-hipError_t launch_collective(const CollDesc& d, bool aligned, bool small, uint64_t tiles, const LaunchCfg& cfg,
+hipError_t launch_collective(const CollDesc& d, bool aligned, int shape, uint64_t tiles, const LaunchCfg& cfg,
                              hipStream_t stream);
 
 // Non-deterministic AllReduce of elements [first, first + elems) of every
