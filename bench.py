@@ -246,6 +246,39 @@ def cpu_baseline_allreduce(host, dst, per_rank, budget_s: float = 10.0):
                   f"(NumPy, single thread, {spent:.1f} s); GPU output equal on the first pass: {ok}",
         "host_cpu": platform.processor() or platform.machine(),
         "host_threads_available": len(os.sched_getaffinity(0)),
+        "parallel": cpu_baseline_allreduce_threads(host, m),
+    }
+
+
+def cpu_baseline_allreduce_threads(host, m: int, budget_s: float = 3.0):
+    """The same oracle call on P threads at once, each over its own slices of
+    the element range (NumPy releases the GIL inside its loops), whole passes
+    over the workload until about `budget_s` seconds of wall time."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    slice_elems = 4 * MiB
+    bounds = [(lo, min(m, lo + slice_elems)) for lo in range(0, m, slice_elems)]
+
+    def work(k):
+        for lo, hi in bounds[k::threads]:
+            oracle.reduce_n([h[lo:hi] for h in host], "bf16")
+
+    passes = 0
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=threads) as pool:
+        while passes == 0 or time.perf_counter() - t0 < budget_s:
+            list(pool.map(work, range(threads)))
+            passes += 1
+    wall = time.perf_counter() - t0
+    return {
+        "value": round(2 * N * m * 2 * passes / wall / 1e9, 3),
+        "unit": "GB/s",
+        "cores": threads,
+        "sample": f"{passes} whole passes over the {2 * m // MiB} MiB-per-rank workload in 8 MiB slices shared "
+                  f"round-robin by {threads} threads ({wall:.1f} s wall)",
     }
 
 
