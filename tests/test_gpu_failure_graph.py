@@ -139,3 +139,72 @@ def test_graph_replay(torch):
                 assert np.array_equal(got, want_a2a[d]), f"replay {it} A2AV dst[{d}]"
     finally:
         snac.snac_finalize(ctx)
+
+
+def test_graph_replay_every_other_entry_point(torch):
+    """ReduceScatter, AllGather, AllGatherV, ReduceScatterV, copy, reduce_n
+    and the atomic AllReduce captured in one graph on a side stream, replayed
+    with new inputs copied in between; every replay checked against the
+    oracle.  The atomic mode gets small-integer inputs, whose sums are exact
+    in any order of the adds."""
+    from oracle.bf16 import f32_to_bf16
+
+    ctx = snac.snac_init(N, 0)
+    try:
+        m = N * 25_001
+        i = np.arange(m)
+        sets = [inputs(m, s) for s in (21, 22, 23)]
+        ints = [[f32_to_bf16(((k + s) * (i % 7)).astype(np.float32)) for k in range(N)] for s in (1, 2, 3)]
+        src = [torch.empty(m * 2, dtype=torch.uint8, device="cuda") for _ in range(N)]
+        isrc = [torch.empty(m * 2, dtype=torch.uint8, device="cuda") for _ in range(N)]
+        rs = [torch.empty(m * 2 // N, dtype=torch.uint8, device="cuda") for _ in range(N)]
+        ag = [torch.empty(m * 2, dtype=torch.uint8, device="cuda") for _ in range(N)]
+        c_rsv = wl.v_counts(N, m, 1, cfg=wl.CFG_TEST, seed=3)[0]
+        rsv = [torch.empty(max(1, int(c)) * 2, dtype=torch.uint8, device="cuda") for c in c_rsv]
+        c_agv = wl.v_counts(N, 30_000, 1, cfg=wl.CFG_TEST, seed=4)[0]
+        words = [wl.raw_u32(int(c), wl.CFG_TEST, r, seed=9) for r, c in enumerate(c_agv)]
+        agv_src = [up(torch, w) if w.size else torch.empty(4, dtype=torch.uint8, device="cuda") for w in words]
+        agv = [torch.empty(int(c_agv.sum()) * 4, dtype=torch.uint8, device="cuda") for _ in range(N)]
+        cp = torch.empty(m * 2, dtype=torch.uint8, device="cuda")
+        rn = [torch.empty(m * 2, dtype=torch.uint8, device="cuda") for _ in range(2)]
+        at = [torch.empty(m * 2, dtype=torch.uint8, device="cuda") for _ in range(N)]
+        s = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                cur = torch.cuda.current_stream()
+                snac.snac_reduce_scatter(ctx, src, rs, m * 2, "bf16", cur)
+                snac.snac_all_gather(ctx, rs, ag, m * 2 // N, "bf16", cur)
+                snac.snac_all_gather_v(ctx, agv_src, agv, [int(c) for c in c_agv], "u32", cur)
+                snac.snac_reduce_scatter_v(ctx, src, rsv, [int(c) for c in c_rsv], "bf16", cur)
+                snac.snac_copy(cp, src[0], m * 2, cur)
+                snac.snac_reduce_n(rn, src[:3], m, "bf16", cur)
+                snac.snac_all_reduce_ex(ctx, isrc, at, m * 2, "bf16", "atomic", cur)
+        want_agv = oracle.all_gather_v(words, [int(c) for c in c_agv])
+        for it, (host, ihost) in enumerate(zip(sets + sets[:1], ints + ints[:1])):
+            for t, h in zip(src, host):
+                t.copy_(up(torch, h))  # eager work between replays
+            for t, h in zip(isrc, ihost):
+                t.copy_(up(torch, h))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            snac.snac_check(ctx)
+            want_rs = oracle.reduce_scatter(host, "bf16")
+            want_ag = oracle.all_gather(want_rs)
+            want_rsv = oracle.reduce_scatter_v(host, [int(c) for c in c_rsv], "bf16")
+            want_rn = oracle.reduce_n(host[:3], "bf16")
+            want_at = oracle.all_reduce(ihost, "bf16")
+            for r in range(N):
+                assert_same(rs[r].cpu().numpy().view(np.uint16), want_rs[r], "bf16", f"replay {it} RS dst[{r}]")
+                assert_same(ag[r].cpu().numpy().view(np.uint16), want_ag[r], "bf16", f"replay {it} AG dst[{r}]")
+                if c_rsv[r]:
+                    got = rsv[r][: int(c_rsv[r]) * 2].cpu().numpy().view(np.uint16)
+                    assert_same(got, want_rsv[r], "bf16", f"replay {it} RSV dst[{r}]")
+                assert np.array_equal(agv[r].cpu().numpy().view(np.uint32), want_agv[r]), f"replay {it} AGV dst[{r}]"
+                assert_same(at[r].cpu().numpy().view(np.uint16), want_at[r], "bf16", f"replay {it} atomic dst[{r}]")
+            assert np.array_equal(cp.cpu().numpy(), host[0].view(np.uint8)), f"replay {it} copy"
+            for k in range(2):
+                assert_same(rn[k].cpu().numpy().view(np.uint16), want_rn, "bf16", f"replay {it} reduce_n dst[{k}]")
+    finally:
+        snac.snac_finalize(ctx)
