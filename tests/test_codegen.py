@@ -7,6 +7,9 @@
   that the lanes of one wave reach a barrier on different iterations,
   which deadlocks the workgroup.
 * No packed fp32 arithmetic (the build disables that target feature).
+* No writes through the scalar data cache: no scalar memory stores or
+  atomics and no scalar cache write-back or discard, in any kernel; data
+  leaves the kernels through vector stores only.
 """
 from __future__ import annotations
 
@@ -26,14 +29,25 @@ pytestmark = pytest.mark.skipif(hipcc is None, reason="hipcc not available")
 PACKED = ["v_pk_" + op + "_f32" for op in ("add", "mul", "fma")]
 
 
+SOURCES = {
+    "collectives.hip": os.path.join(CSRC, "collectives.hip"),
+    "pipeline.hip": os.path.join(CSRC, "pipeline.hip"),
+    "devapi_kernels.hip": os.path.join(ROOT, "tests", "devapi", "devapi_kernels.hip"),
+}
+_ASM: dict[str, str] = {}
+
+
 def _asm(src: str, tmp_path) -> str:
+    """gfx950 assembly of one source, compiled once per test session."""
     from copy_reduce_snac_amd.build import DEVICE_FLAGS
 
-    out = tmp_path / (src + ".s")
-    flags = [f for f in DEVICE_FLAGS if f not in ("-fPIC",)]
-    subprocess.run([hipcc, *flags, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", str(out)],
-                   check=True, capture_output=True)
-    return out.read_text()
+    if src not in _ASM:
+        out = tmp_path / (src + ".s")
+        flags = [f for f in DEVICE_FLAGS if f not in ("-fPIC",)]
+        subprocess.run([hipcc, *flags, "--cuda-device-only", "-S", SOURCES[src], "-o", str(out)],
+                       check=True, capture_output=True)
+        _ASM[src] = out.read_text()
+    return _ASM[src]
 
 
 def _kernels(asm: str) -> dict[str, list[str]]:
@@ -79,3 +93,14 @@ def test_no_packed_fp32(tmp_path, src):
     asm = _asm(src, tmp_path)
     for op in PACKED:
         assert op not in asm, f"{src}: {op} emitted"
+
+
+SCALAR_WRITES = re.compile(r"^\s*(s_store_|s_buffer_store_|s_scratch_store_|s_atomic_|s_buffer_atomic_|"
+                           r"s_dcache_wb|s_dcache_discard)", re.M)
+
+
+@pytest.mark.parametrize("src", sorted(SOURCES))
+def test_no_scalar_cache_writes(tmp_path, src):
+    asm = _asm(src, tmp_path)
+    bad = SCALAR_WRITES.findall(asm)
+    assert not bad, f"{src}: {sorted(set(bad))}"
