@@ -450,7 +450,7 @@ def main() -> int:
     ap.add_argument("--no-extra", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU (N logical ranks in one GPU's HBM); --gpus {args.gpus} "
+        print(f"bench.py: the library runs its N logical ranks in one GPU's HBM; --gpus {args.gpus} "
               "is not supported", file=sys.stderr)
         return 2
     env = Env()
