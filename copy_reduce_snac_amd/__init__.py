@@ -262,14 +262,42 @@ def snac_reduce_n(dsts: Sequence, srcs: Sequence, count: int, dtype, stream=None
 
 
 # ----------------------------------------------------------- collectives
+def _ctx_ranks(ctx: int) -> int:
+    return snac_ctx_nranks(ctx) if ctx else 0
+
+
+def _rank_ptrs(ctx: int, xs: Sequence, what: str) -> ctypes.Array:
+    """Pointer array of a per-rank argument.  The library reads exactly
+    snac_ctx_nranks(ctx) entries, so a list of another length is refused here
+    rather than read past its end."""
+    xs = list(xs)
+    n = _ctx_ranks(ctx)
+    if n and len(xs) != n:
+        raise ValueError(f"{what}: {len(xs)} buffers for a context of {n} ranks")
+    return _ptrs(xs)
+
+
+def _rank_sizes(ctx: int, counts: Iterable[int], per_pair: bool, what: str) -> ctypes.Array:
+    """Count array of a V collective: N entries, or N * N for AllToAllV."""
+    counts = [int(c) for c in counts]
+    n = _ctx_ranks(ctx)
+    want = n * n if per_pair else n
+    if n and len(counts) != want:
+        raise ValueError(f"{what}: {len(counts)} counts for a context of {n} ranks (need {want})")
+    return _sizes(counts)
+
+
 def _fixed(name: str, ctx: int, srcs: Sequence, dsts: Sequence, nbytes: int, dtype, stream) -> None:
     f = getattr(lib(), name)
-    _check(f(ctx, _ptrs(srcs), _ptrs(dsts), nbytes, _dtype(dtype), _stream(stream)), name)
+    _check(f(ctx, _rank_ptrs(ctx, srcs, name + " srcs"), _rank_ptrs(ctx, dsts, name + " dsts"), nbytes, _dtype(dtype),
+             _stream(stream)), name)
 
 
 def _vary(name: str, ctx: int, srcs: Sequence, dsts: Sequence, counts: Iterable[int], dtype, stream) -> None:
     f = getattr(lib(), name)
-    _check(f(ctx, _ptrs(srcs), _ptrs(dsts), _sizes(counts), _dtype(dtype), _stream(stream)), name)
+    cnt = _rank_sizes(ctx, counts, name == "snac_all_to_all_v", name + " counts")
+    _check(f(ctx, _rank_ptrs(ctx, srcs, name + " srcs"), _rank_ptrs(ctx, dsts, name + " dsts"), cnt, _dtype(dtype),
+             _stream(stream)), name)
 
 
 def snac_all_reduce(ctx, srcs, dsts, nbytes, dtype, stream=None):
@@ -282,7 +310,9 @@ _MODES = {"deterministic": SNAC_REDUCE_DETERMINISTIC, "atomic": SNAC_REDUCE_ATOM
 
 def snac_all_reduce_ex(ctx, srcs, dsts, nbytes, dtype, mode, stream=None):
     m = _MODES[mode] if isinstance(mode, str) else int(mode)
-    _check(lib().snac_all_reduce_ex(ctx, _ptrs(srcs), _ptrs(dsts), nbytes, _dtype(dtype), m, _stream(stream)),
+    _check(lib().snac_all_reduce_ex(ctx, _rank_ptrs(ctx, srcs, "snac_all_reduce_ex srcs"),
+                                    _rank_ptrs(ctx, dsts, "snac_all_reduce_ex dsts"), nbytes, _dtype(dtype), m,
+                                    _stream(stream)),
            "snac_all_reduce_ex")
 
 
@@ -311,7 +341,8 @@ def snac_all_to_all_v(ctx, srcs, dsts, counts, dtype, stream=None):
 
 
 def snac_pipeline_scale_reduce(ctx, xs, out, count, dtype, stream=None):
-    _check(lib().snac_pipeline_scale_reduce(ctx, _ptrs(xs), _ptr(out), count, _dtype(dtype), _stream(stream)),
+    _check(lib().snac_pipeline_scale_reduce(ctx, _rank_ptrs(ctx, xs, "snac_pipeline_scale_reduce xs"), _ptr(out), count,
+                                            _dtype(dtype), _stream(stream)),
            "snac_pipeline_scale_reduce")
 
 
@@ -327,8 +358,15 @@ def snac_describe(ctx: int, coll: int, srcs: Sequence, dsts: Sequence, nbytes: i
                   counts: Iterable[int] | None = None, dtype="byte") -> snac_coll_desc:
     """A validated, laid-out collective for snac::collective() in a user kernel."""
     out = snac_coll_desc()
-    cnt = _sizes(counts) if counts is not None else None
-    _check(lib().snac_describe(ctx, coll, _ptrs(srcs), _ptrs(dsts), nbytes, cnt, _dtype(dtype), ctypes.byref(out)),
+    cnt = None
+    if coll in (SNAC_COLL_ALL_GATHER_V, SNAC_COLL_REDUCE_SCATTER_V, SNAC_COLL_ALL_TO_ALL_V):
+        cnt = _rank_sizes(ctx, counts if counts is not None else [], coll == SNAC_COLL_ALL_TO_ALL_V,
+                          "snac_describe counts")
+    elif counts is not None:
+        cnt = _sizes(counts)
+    _check(lib().snac_describe(ctx, coll, _rank_ptrs(ctx, srcs, "snac_describe srcs"),
+                               _rank_ptrs(ctx, dsts, "snac_describe dsts"), nbytes, cnt, _dtype(dtype),
+                               ctypes.byref(out)),
            "snac_describe")
     return out
 

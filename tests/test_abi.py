@@ -307,3 +307,29 @@ def test_tuning_from_environment():
                SNAC_SPIN_LIMIT_LOG2="99", SNAC_COPY_MULTICAST="x1")
     out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, check=True).stdout
     assert out.split() == ["3", "4", "8192", "0", "0"]
+
+
+def test_binding_refuses_rank_lists_of_the_wrong_length(monkeypatch):
+    """The library reads exactly N pointers (and N or N*N counts) per call,
+    so the binding checks every per-rank list against the context's rank
+    count before calling it.  A stand-in rank count for a fake context keeps
+    this on the CPU: the refusals happen before any library call."""
+    monkeypatch.setattr(snac, "snac_ctx_nranks", lambda ctx: 4)
+    fake = 0x1000
+    four, three = [0x10000] * 4, [0x10000] * 3
+    calls = [
+        lambda: snac.snac_all_reduce(fake, three, four, 64, "f32"),
+        lambda: snac.snac_reduce_scatter(fake, four, three, 64, "f32"),
+        lambda: snac.snac_all_gather(fake, four, [0x10000] * 5, 64, "f32"),
+        lambda: snac.snac_all_to_all(fake, [], four, 64, "u32"),
+        lambda: snac.snac_all_reduce_ex(fake, four, three, 64, "bf16", "atomic"),
+        lambda: snac.snac_all_gather_v(fake, four, four, [1, 2, 3], "u32"),
+        lambda: snac.snac_reduce_scatter_v(fake, four, four, [1] * 5, "f32"),
+        lambda: snac.snac_all_to_all_v(fake, four, four, [1] * 4, "u32"),
+        lambda: snac.snac_pipeline_scale_reduce(fake, three, 0x10000, 16, "bf16"),
+        lambda: snac.snac_describe(fake, snac.SNAC_COLL_ALL_REDUCE, three, four, 64, None, "f32"),
+        lambda: snac.snac_describe(fake, snac.SNAC_COLL_ALL_TO_ALL_V, four, four, 0, [1] * 4, "u32"),
+    ]
+    for i, call in enumerate(calls):
+        with pytest.raises(ValueError):
+            call()
