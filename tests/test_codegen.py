@@ -34,20 +34,24 @@ SOURCES = {
     "pipeline.hip": os.path.join(CSRC, "pipeline.hip"),
     "devapi_kernels.hip": os.path.join(ROOT, "tests", "devapi", "devapi_kernels.hip"),
 }
-_ASM: dict[str, str] = {}
-
-
-def _asm(src: str, tmp_path) -> str:
-    """gfx950 assembly of one source, compiled once per test session."""
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory) -> dict[str, str]:
+    """gfx950 assembly of every source, the compiles run side by side."""
     from copy_reduce_snac_amd.build import DEVICE_FLAGS
 
-    if src not in _ASM:
-        out = tmp_path / (src + ".s")
-        flags = [f for f in DEVICE_FLAGS if f not in ("-fPIC",)]
-        subprocess.run([hipcc, *flags, "--cuda-device-only", "-S", SOURCES[src], "-o", str(out)],
-                       check=True, capture_output=True)
-        _ASM[src] = out.read_text()
-    return _ASM[src]
+    d = tmp_path_factory.mktemp("asm")
+    flags = [f for f in DEVICE_FLAGS if f not in ("-fPIC",)]
+    procs = {}
+    for name, path in SOURCES.items():
+        out = d / (name + ".s")
+        procs[name] = (out, subprocess.Popen([hipcc, *flags, "--cuda-device-only", "-S", path, "-o", str(out)],
+                                             stdout=subprocess.PIPE, stderr=subprocess.PIPE))
+    res = {}
+    for name, (out, p) in procs.items():
+        _, err = p.communicate()
+        assert p.returncode == 0, f"{name}: {err.decode()[-2000:]}"
+        res[name] = out.read_text()
+    return res
 
 
 def _kernels(asm: str) -> dict[str, list[str]]:
@@ -79,8 +83,8 @@ def _barrier_depths(lines: list[str]) -> list[int]:
     return found
 
 
-def test_pipeline_barriers_only_in_the_ticket_loop(tmp_path):
-    ks = {k: v for k, v in _kernels(_asm("pipeline.hip", tmp_path)).items() if "pipeline_kernel" in k}
+def test_pipeline_barriers_only_in_the_ticket_loop(asm):
+    ks = {k: v for k, v in _kernels(asm["pipeline.hip"]).items() if "pipeline_kernel" in k}
     assert len(ks) == 32
     for name, lines in ks.items():
         depths = _barrier_depths(lines)
@@ -88,11 +92,10 @@ def test_pipeline_barriers_only_in_the_ticket_loop(tmp_path):
         assert max(depths) <= 1, f"{name}: barrier inside a nested loop"
 
 
-@pytest.mark.parametrize("src", ["collectives.hip", "pipeline.hip"])
-def test_no_packed_fp32(tmp_path, src):
-    asm = _asm(src, tmp_path)
+@pytest.mark.parametrize("src", sorted(SOURCES))
+def test_no_packed_fp32(asm, src):
     for op in PACKED:
-        assert op not in asm, f"{src}: {op} emitted"
+        assert op not in asm[src], f"{src}: {op} emitted"
 
 
 SCALAR_WRITES = re.compile(r"^\s*(s_store_|s_buffer_store_|s_scratch_store_|s_atomic_|s_buffer_atomic_|"
@@ -100,7 +103,6 @@ SCALAR_WRITES = re.compile(r"^\s*(s_store_|s_buffer_store_|s_scratch_store_|s_at
 
 
 @pytest.mark.parametrize("src", sorted(SOURCES))
-def test_no_scalar_cache_writes(tmp_path, src):
-    asm = _asm(src, tmp_path)
-    bad = SCALAR_WRITES.findall(asm)
+def test_no_scalar_cache_writes(asm, src):
+    bad = SCALAR_WRITES.findall(asm[src])
     assert not bad, f"{src}: {sorted(set(bad))}"

@@ -370,15 +370,27 @@ def test_bf16_narrowing_exhaustive_vs_torch():
     """Every non-NaN binary32 pattern against torch's CPU bfloat16 cast (a
     library routine, used here only as an independent reference)."""
     torch = pytest.importorskip("torch")
-    step = 1 << 24
-    for lo in range(0, 1 << 32, step):
+    from concurrent.futures import ThreadPoolExecutor
+
+    step = 1 << 22
+
+    def chunk(lo):
         u = np.arange(lo, lo + step, dtype=np.uint64).astype(np.uint32)
         f = u.view(np.float32)
         ours = obf.f32_to_bf16(f)
         ref = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
         nan = np.isnan(f)
-        assert np.array_equal(ours[~nan], ref[~nan]), hex(lo)
-        assert np.all((ours[nan] & 0x7F80) == 0x7F80) and np.all((ours[nan] & 0x7F) != 0)
+        ok = bool(np.array_equal(ours[~nan], ref[~nan]))
+        ok_nan = bool(np.all((ours[nan] & 0x7F80) == 0x7F80) and np.all((ours[nan] & 0x7F) != 0))
+        return lo, ok, ok_nan
+
+    # the chunks are independent and NumPy and torch release the GIL inside
+    # their loops, so threads share the 2^32 patterns
+    workers = max(1, min(8, len(os.sched_getaffinity(0))))
+    with ThreadPoolExecutor(max_workers=workers) as pool:
+        for lo, ok, ok_nan in pool.map(chunk, range(0, 1 << 32, step)):
+            assert ok, hex(lo)
+            assert ok_nan, hex(lo)
 
 
 # ---------------------------------------------------------------- mutations
