@@ -155,7 +155,7 @@ def test_reduce_n_atom(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("n", [1, 2, 3, 8])
+@pytest.mark.parametrize("n", [1, 2, 3, 8, 16])
 def test_reduce_scatter(ctxs, n, dtype):
     for mc in [1, 5, 4096, 12_345]:
         srcs = gen(n, n * mc, dtype, seed=mc)
@@ -168,7 +168,7 @@ def test_reduce_scatter(ctxs, n, dtype):
 
 # ------------------------------------------------------------------- copy
 @pytest.mark.parametrize("dtype", ["byte", "u32", "bf16"])
-@pytest.mark.parametrize("n", [1, 2, 3, 8])
+@pytest.mark.parametrize("n", [1, 2, 3, 8, 16])
 def test_all_gather(ctxs, n, dtype):
     for m in [1, 3, 4096, 9_999]:
         srcs = gen(n, m, dtype, seed=m + n)
@@ -180,7 +180,7 @@ def test_all_gather(ctxs, n, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["byte", "u32", "f32"])
-@pytest.mark.parametrize("n", [1, 2, 3, 8])
+@pytest.mark.parametrize("n", [1, 2, 3, 8, 16])
 def test_all_to_all(ctxs, n, dtype):
     for mc in [1, 7, 4096, 5_001]:
         srcs = gen(n, n * mc, dtype, seed=mc)
@@ -207,7 +207,7 @@ def _v_counts(n, total, rows, seed):
 
 
 @pytest.mark.parametrize("dtype", ["u32", "f32", "bf16", "byte"])
-@pytest.mark.parametrize("n", [2, 3, 8])
+@pytest.mark.parametrize("n", [2, 3, 8, 16])
 def test_all_to_all_v(ctxs, n, dtype):
     for total, seed in [(10_000, 1), (100_003, 2), (7, 3)]:
         c = _v_counts(n, total, n, seed)
@@ -220,7 +220,7 @@ def test_all_to_all_v(ctxs, n, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["u32", "bf16", "byte"])
-@pytest.mark.parametrize("n", [2, 3, 8])
+@pytest.mark.parametrize("n", [2, 3, 8, 16])
 def test_all_gather_v(ctxs, n, dtype):
     for total, seed in [(10_000, 4), (99_999, 5), (5, 6)]:
         c = _v_counts(n, total, 1, seed)[0]
@@ -233,7 +233,7 @@ def test_all_gather_v(ctxs, n, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("n", [2, 3, 8])
+@pytest.mark.parametrize("n", [2, 3, 8, 16])
 def test_reduce_scatter_v(ctxs, n, dtype):
     for total, seed in [(10_000, 7), (100_001, 8), (9, 9)]:
         c = _v_counts(n, total, 1, seed)[0]
@@ -261,7 +261,7 @@ def test_v_equal_counts_match_fixed(ctxs):
 
 # -------------------------------------------------------- SNAC pipeline
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("n", [1, 2, 3, 8])
+@pytest.mark.parametrize("n", [1, 2, 3, 8, 16])
 def test_pipeline(n, dtype):
     ctx = snac.snac_init(n, 4 * 65536)  # 4 slots: the ring wraps many times
     try:
