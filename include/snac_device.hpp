@@ -915,7 +915,17 @@ __device__ void run_copy(const CollDesc& d, uint32_t block, uint32_t blocks) {
 // On a mismatch nothing is moved and SNAC_E_ARG latches.  The `blocks`
 // workgroups must be co-resident; the context's barrier serves one group at
 // a time.
-template <typename T = F32, int N = 1, int TH = 256, int CP = kCacheStream>
+//
+// SYNC = false leaves out that closing grid barrier: the call returns as
+// soon as this workgroup's share is stored, and the output is complete and
+// visible once the kernel has ended (to the next kernel on the stream), not
+// inside it.  It suits a kernel whose collective is its last step; the
+// workgroups need not be co-resident, and it returns false only on an
+// argument mismatch.  On MI355X the barrier costs about 33 us at the end of
+// a 256 MiB-per-rank bf16 N=8 AllReduce (0.785 against 0.752 ms): the
+// release fence of every workgroup about 24 us, the acquire fence and the
+// arrival counter the rest.
+template <typename T = F32, int N = 1, int TH = 256, int CP = kCacheStream, bool SYNC = true>
 __device__ bool collective(const CollDesc& desc, const snac_dev_ctx& ctx, uint32_t block, uint32_t blocks,
                            uint32_t coll_blocks) {
   const bool reduce = coll_is_reduce(desc.coll);
@@ -938,8 +948,12 @@ __device__ bool collective(const CollDesc& desc, const snac_dev_ctx& ctx, uint32
         run_copy<TH, CP, false>(desc, block, coll_blocks);
     }
   }
-  const bool met = group_barrier(ctx, blocks);
-  return good && met;
+  if constexpr (!SYNC) {
+    return good;
+  } else {
+    const bool met = group_barrier(ctx, blocks);
+    return good && met;
+  }
 }
 
 }  // namespace snac

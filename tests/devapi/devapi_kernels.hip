@@ -43,11 +43,11 @@ __global__ __launch_bounds__(TH) void reduce_slices_kernel(snac_coll_desc bufs, 
 
 // ---- a described collective run by workgroups [0, blocks) of a larger grid
 
-template <typename T, int N>
+template <typename T, int N, bool SYNC = true>
 __global__ __launch_bounds__(TH) void collective_kernel(const snac_coll_desc desc, const snac_dev_ctx ctx,
                                                         uint32_t blocks, uint32_t coll_blocks, uint32_t* ok_out) {
   if (blockIdx.x >= blocks) return;  // workgroups doing "other work"
-  const bool ok = snac::collective<T, N, TH>(desc, ctx, blockIdx.x, blocks, coll_blocks);
+  const bool ok = snac::collective<T, N, TH, snac::kCacheStream, SYNC>(desc, ctx, blockIdx.x, blocks, coll_blocks);
   if (threadIdx.x == 0) ok_out[blockIdx.x] = ok ? 1u : 0u;
 }
 
@@ -192,6 +192,29 @@ int devtest_collective(const snac_coll_desc* desc, const snac_dev_ctx* ctx, int 
     else                                                                                                   \
       hipLaunchKernelGGL((collective_kernel<snac::F32, NN>), dim3(grid), dim3(TH), 0, s, *desc, *ctx,      \
                          (uint32_t)blocks, (uint32_t)coll_blocks, ok_out);                                 \
+    break;
+  switch (nsrc) {
+    SNAC_DISPATCH_N(SNAC_CASE)
+    default: return hipErrorInvalidValue;
+  }
+#undef SNAC_CASE
+  return hipGetLastError();
+}
+
+// The same without the closing grid barrier (SYNC = false): all `blocks`
+// workgroups move data, need not be co-resident, and the output is checked
+// after the kernel.
+int devtest_collective_nosync(const snac_coll_desc* desc, const snac_dev_ctx* ctx, int bf16, int nsrc, int blocks,
+                              uint32_t* ok_out, hipStream_t s) {
+  if (!desc || !ctx || blocks <= 0) return hipErrorInvalidValue;
+#define SNAC_CASE(NN)                                                                                       \
+  case NN:                                                                                                  \
+    if (bf16)                                                                                               \
+      hipLaunchKernelGGL((collective_kernel<snac::BF16, NN, false>), dim3(blocks), dim3(TH), 0, s, *desc,   \
+                         *ctx, (uint32_t)blocks, (uint32_t)blocks, ok_out);                                 \
+    else                                                                                                    \
+      hipLaunchKernelGGL((collective_kernel<snac::F32, NN, false>), dim3(blocks), dim3(TH), 0, s, *desc,    \
+                         *ctx, (uint32_t)blocks, (uint32_t)blocks, ok_out);                                 \
     break;
   switch (nsrc) {
     SNAC_DISPATCH_N(SNAC_CASE)

@@ -33,6 +33,7 @@ def dev():
         "devtest_copy_slices": [_VP, _VP, _U64, _I, _VP],
         "devtest_reduce_slices": [_DP, _I, _U64, _I, _I, _VP],
         "devtest_collective": [_DP, _CP, _I, _I, _I, _I, _I, _VP, _VP],
+        "devtest_collective_nosync": [_DP, _CP, _I, _I, _I, _VP, _VP],
         "devtest_fused_scale_allreduce": [_DP, _CP, _DP, _U64, _VP, _I, _VP, _VP],
         "devtest_flags": [_CP, _DP, _VP, _VP, _I, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, _U64, _VP,
                           _VP],
@@ -180,6 +181,28 @@ def test_device_collective(dev, ctx8, coll, dtype, misalign):
     for r, (b, w) in enumerate(zip(db, want)):
         assert b.guards_ok(), f"canary around dst[{r}]"
         assert_same(b.download(np_dtype(dtype)), np.asarray(w), dtype, f"device collective {coll} dst[{r}]")
+
+
+@pytest.mark.parametrize("blocks", [37, 1500])
+@pytest.mark.parametrize("coll,dtype", COLLS)
+def test_device_collective_without_barrier(dev, ctx8, coll, dtype, blocks):
+    """SYNC = false: no closing grid barrier, so any grid size works (1500
+    workgroups exceed what fits at once); the output is complete after the
+    kernel."""
+    n = 8
+    m = 8 * 12_289
+    srcs, sb, db, want, nbytes, counts = _case(coll, n, dtype, m, blocks == 37, seed=coll * 10 + 7)
+    desc = snac.snac_describe(ctx8, coll, [b.ptr for b in sb], [b.ptr for b in db], nbytes, counts, dtype)
+    dctx = snac.snac_get_device_context(ctx8)
+    ok = ok_buffer(blocks)
+    launch(dev.devtest_collective_nosync(ctypes.byref(desc), ctypes.byref(dctx), int(dtype == "bf16"), n, blocks,
+                                         ok.data_ptr(), None))
+    sync()
+    snac.snac_check(ctx8)
+    assert int(ok.sum().item()) == blocks
+    for r, (b, w) in enumerate(zip(db, want)):
+        assert b.guards_ok(), f"canary around dst[{r}]"
+        assert_same(b.download(np_dtype(dtype)), np.asarray(w), dtype, f"no-barrier collective {coll} dst[{r}]")
 
 
 def test_device_collective_repeats_and_one_block(dev, ctx8):
