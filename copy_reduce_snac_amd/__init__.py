@@ -412,10 +412,11 @@ def snac_set_tuning_rules(rules: Sequence[dict] | None) -> None:
 
 
 def snac_get_tuning_rules() -> list[dict]:
+    # one call into room for the largest table: the table may be replaced
+    # from another thread between a size query and a copy
     n = _I()
-    _check(lib().snac_get_tuning_rules(None, 0, ctypes.byref(n)), "snac_get_tuning_rules")
-    arr = (snac_tuning_rule * max(1, n.value))()
-    _check(lib().snac_get_tuning_rules(arr, n.value, ctypes.byref(n)), "snac_get_tuning_rules")
+    arr = (snac_tuning_rule * SNAC_MAX_TUNING_RULES)()
+    _check(lib().snac_get_tuning_rules(arr, SNAC_MAX_TUNING_RULES, ctypes.byref(n)), "snac_get_tuning_rules")
     return [{k: getattr(arr[i], k) for k in _RULE_FIELDS} for i in range(n.value)]
 
 

@@ -10,7 +10,9 @@
 #include <vector>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
+#include <shared_mutex>
 #include <string>
 
 #include "internal.hpp"
@@ -108,6 +110,16 @@ snac_tuning tuning_from_env() {
 
 snac_tuning g_tuning = tuning_from_env();
 
+// Guards g_tuning and g_rules.  The set calls write; every call reads one
+// consistent copy, since collectives may run on other host threads with
+// their own contexts while the tuning changes.
+std::shared_mutex g_tuning_mu;
+
+snac_tuning tuning_now() {
+  std::shared_lock<std::shared_mutex> lk(g_tuning_mu);
+  return g_tuning;
+}
+
 constexpr uint32_t kMaxPipeTile = 2048u * 1024u;
 constexpr uint32_t kMinPipeTile = 4096u;
 constexpr uint32_t kMinAutoSlots = 64u;
@@ -164,8 +176,8 @@ bool rule_matches(const snac_tuning_rule& r, int32_t coll, int nsrc, int esize, 
 }
 
 // Launch parameters of a call: the first matching rule, then the explicit
-// process-wide values on top.
-LaunchCfg launch_cfg(int32_t coll, int nsrc, int esize, uint64_t bytes) {
+// process-wide values on top.  The caller holds g_tuning_mu.
+LaunchCfg launch_cfg_locked(int32_t coll, int nsrc, int esize, uint64_t bytes) {
   LaunchCfg c{0, 0};
   for (const snac_tuning_rule& r : g_rules) {
     if (rule_matches(r, coll, nsrc, esize, bytes)) {
@@ -176,6 +188,11 @@ LaunchCfg launch_cfg(int32_t coll, int nsrc, int esize, uint64_t bytes) {
   if (g_tuning.wgs_per_cu) c.wgs_per_cu = g_tuning.wgs_per_cu;
   if (g_tuning.cache_policy) c.cache_policy = g_tuning.cache_policy;
   return c;
+}
+
+LaunchCfg launch_cfg(int32_t coll, int nsrc, int esize, uint64_t bytes) {
+  std::shared_lock<std::shared_mutex> lk(g_tuning_mu);
+  return launch_cfg_locked(coll, nsrc, esize, bytes);
 }
 
 bool rule_ok(const snac_tuning_rule& r) {
@@ -267,7 +284,7 @@ int needs_split(void* const* dst, int ndst) {
 
 // A buffer may be NULL only when its extent (in_bytes/out_bytes) is zero.
 int split_copy(void* const* dst, int ndst) {
-  if (g_tuning.copy_multicast == 2) return 1;
+  if (tuning_now().copy_multicast == 2) return 1;
   return needs_split(dst, ndst);
 }
 
@@ -467,7 +484,7 @@ int snac_ctx_nranks(const snac_ctx* ctx) { return ctx ? ctx->nranks : 0; }
 
 snac_status snac_get_tuning(snac_tuning* out) {
   if (!out) return fail(SNAC_E_ARG, "out is NULL");
-  *out = g_tuning;
+  *out = tuning_now();
   return ok();
 }
 
@@ -484,7 +501,10 @@ snac_status snac_set_tuning(const snac_tuning* in) {
   if (in->copy_multicast < 0 || in->copy_multicast > 2) return fail(SNAC_E_ARG, "copy_multicast out of range [0, 2]");
   if (in->debug_producer_delay < 0 || in->debug_producer_delay > 100000)
     return fail(SNAC_E_ARG, "debug_producer_delay out of range [0, 100000]");
-  g_tuning = *in;
+  {
+    std::unique_lock<std::shared_mutex> lk(g_tuning_mu);
+    g_tuning = *in;
+  }
   return ok();
 }
 
@@ -495,7 +515,7 @@ snac_status snac_init(int nranks, size_t staging_bytes_per_rank, snac_stream str
   const size_t staging = staging_bytes_per_rank ? staging_bytes_per_rank : kDefaultStaging;
   // pipeline tile: the tuning value, else the largest power of two up to
   // 2 MiB that still leaves at least 64 slots in the ring
-  uint32_t tile = (uint32_t)g_tuning.pipeline_tile_bytes;
+  uint32_t tile = (uint32_t)tuning_now().pipeline_tile_bytes;
   if (!tile) {
     tile = kMaxPipeTile;
     while (tile > kMinPipeTile && staging / tile < kMinAutoSlots) tile >>= 1;
@@ -729,8 +749,9 @@ snac_status snac_pipeline_scale_reduce(snac_ctx* ctx, const void* const* x, void
   // bf16 4096x8192, 2 MiB for f32) with two workgroups per CU ran best --
   // bigger items mean fewer release and acquire fences, which serialise
   // GPU-wide -- and smaller tiles only add per-item overhead.
+  const snac_tuning tn = tuning_now();
   uint32_t tile = ctx->tile_bytes, slots = ctx->slots;
-  if (!g_tuning.pipeline_tile_bytes) {
+  if (!tn.pipeline_tile_bytes) {
     while (tile / 2 >= kMinSplitTile && (uint64_t)slots * 2 <= ctx->flag_slots &&
            (count * (uint64_t)e + tile - 1) / tile < kTargetTiles) {
       tile >>= 1;
@@ -739,10 +760,10 @@ snac_status snac_pipeline_scale_reduce(snac_ctx* ctx, const void* const* x, void
   }
   a.slots = slots;
   a.tile_bytes = tile;
-  a.lookahead = (uint32_t)g_tuning.pipeline_lookahead;
-  a.spin_limit_log2 = (uint32_t)(g_tuning.spin_limit_log2 ? g_tuning.spin_limit_log2 : kDefaultSpinLog2);
-  a.drop_notify = g_tuning.debug_drop_notify;
-  a.producer_delay_us = (uint32_t)g_tuning.debug_producer_delay;
+  a.lookahead = (uint32_t)tn.pipeline_lookahead;
+  a.spin_limit_log2 = (uint32_t)(tn.spin_limit_log2 ? tn.spin_limit_log2 : kDefaultSpinLog2);
+  a.drop_notify = tn.debug_drop_notify;
+  a.producer_delay_us = (uint32_t)tn.debug_producer_delay;
   hipError_t err = launch_pipeline(a, dtype == SNAC_BF16, launch_cfg(SNAC_RULE_PIPELINE, n, e, count * (uint64_t)e),
                                    (hipStream_t)stream, nullptr);
   if (err != hipSuccess) return hip_fail(err, "pipeline launch");
@@ -754,6 +775,7 @@ snac_status snac_set_tuning_rules(const snac_tuning_rule* rules, int n) {
   if (n > 0 && !rules) return fail(SNAC_E_ARG, "rules is NULL");
   for (int i = 0; i < n; ++i)
     if (!rule_ok(rules[i])) return fail(SNAC_E_ARG, "rule %d is invalid", i);
+  std::unique_lock<std::shared_mutex> lk(g_tuning_mu);
   if (n == 0)
     g_rules.assign(std::begin(kBuiltinRules), std::end(kBuiltinRules));
   else
@@ -763,6 +785,7 @@ snac_status snac_set_tuning_rules(const snac_tuning_rule* rules, int n) {
 
 snac_status snac_get_tuning_rules(snac_tuning_rule* out, int max, int* n) {
   if (!n) return fail(SNAC_E_ARG, "n is NULL");
+  std::shared_lock<std::shared_mutex> lk(g_tuning_mu);
   *n = (int)g_rules.size();
   if (!out) return ok();
   if (max < (int)g_rules.size()) return fail(SNAC_E_ARG, "max (%d) is smaller than the table (%d rules)", max, *n);
@@ -773,7 +796,8 @@ snac_status snac_get_tuning_rules(snac_tuning_rule* out, int max, int* n) {
 snac_status snac_tuning_lookup(int32_t coll, int nranks, int esize, size_t bytes, snac_tuning* out) {
   if (!out) return fail(SNAC_E_ARG, "out is NULL");
   if (nranks < 1 || nranks > SNAC_MAX_RANKS) return fail(SNAC_E_ARG, "nranks %d outside 1..%d", nranks, SNAC_MAX_RANKS);
-  const LaunchCfg c = launch_cfg(coll, nranks, esize, bytes);
+  std::shared_lock<std::shared_mutex> lk(g_tuning_mu);
+  const LaunchCfg c = launch_cfg_locked(coll, nranks, esize, bytes);
   *out = g_tuning;
   out->wgs_per_cu = c.wgs_per_cu;
   out->cache_policy = c.cache_policy;
@@ -784,7 +808,8 @@ snac_status snac_get_device_context(const snac_ctx* ctx, snac_dev_ctx* out) {
   if (!ctx || !out) return fail(SNAC_E_ARG, "NULL argument");
   std::memset(out, 0, sizeof *out);
   out->nranks = ctx->nranks;
-  out->spin_limit_log2 = (uint32_t)(g_tuning.spin_limit_log2 ? g_tuning.spin_limit_log2 : kDefaultSpinLog2);
+  const uint32_t spin = (uint32_t)tuning_now().spin_limit_log2;
+  out->spin_limit_log2 = spin ? spin : kDefaultSpinLog2;
   out->status = ctx->ctrl + kCtrlStatus;
   out->abort_word = ctx->abort_dev;
   out->barrier = ctx->ctrl + kCtrlBarrier;

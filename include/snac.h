@@ -22,11 +22,14 @@
  *     long, an abort) latch in the context's status word; snac_check() and
  *     snac_finalize() report them.
  *   - A context is used from one host thread and one stream at a time.
+ *     Different contexts may be used from different threads at once.  The
+ *     process-wide tuning (snac_set_tuning, the rule table) may be changed
+ *     from any thread; every call uses one consistent copy of it.
  *   - Reductions accumulate in binary32 in rank order 0..N-1 starting from
  *     the rank-0 value and round once to the output type (bf16:
  *     round-to-nearest-even).  Results are therefore bitwise repeatable, the
- *     deterministic mode of Purlin 0.6.5 ("Reduction determinism"); there is
- *     no non-deterministic mode.
+ *     deterministic mode of Purlin 0.6.5 ("Reduction determinism");
+ *     snac_all_reduce_ex also offers a non-deterministic (float-atomic) mode.
  *   - No C++ exception crosses this interface.
  */
 #ifndef SNAC_H

@@ -334,3 +334,49 @@ def test_binding_refuses_rank_lists_of_the_wrong_length(monkeypatch):
     for i, call in enumerate(calls):
         with pytest.raises(ValueError):
             call()
+
+
+def test_tuning_tables_survive_concurrent_use():
+    """The rule table and the process-wide tuning are read by every call and
+    may be replaced from another host thread meanwhile: a reader must always
+    see one whole table (ctypes releases the GIL around library calls, so
+    the threads really overlap)."""
+    import threading
+
+    MiB = 1 << 20
+    table_a = [{"coll": snac.SNAC_COLL_ALL_REDUCE, "min_ranks": 1, "max_ranks": 16, "esize": 0, "min_bytes": 0,
+                "max_bytes": 2 ** 64 - 1, "wgs_per_cu": 3, "cache_policy": 2}]
+    table_b = [{"coll": snac.SNAC_RULE_ANY, "min_ranks": 1, "max_ranks": 16, "esize": 0, "min_bytes": 0,
+                "max_bytes": MiB, "wgs_per_cu": 5, "cache_policy": 4}] * 40 + table_a
+    seen, errors = set(), []
+    stop = threading.Event()
+
+    def writer():
+        try:
+            for i in range(3000):
+                snac.snac_set_tuning_rules(table_a if i % 2 else table_b)
+        except Exception as e:  # pragma: no cover - reported below
+            errors.append(e)
+        finally:
+            stop.set()
+
+    def reader():
+        try:
+            while not stop.is_set():
+                t = snac.snac_tuning_lookup(snac.SNAC_COLL_ALL_REDUCE, 8, 2, 4 * MiB)
+                seen.add((t["wgs_per_cu"], t["cache_policy"]))
+                n = len(snac.snac_get_tuning_rules())
+                assert n in (1, 41), n
+        except Exception as e:
+            errors.append(e)
+
+    threads = [threading.Thread(target=writer)] + [threading.Thread(target=reader) for _ in range(3)]
+    try:
+        for t in threads:
+            t.start()
+        for t in threads:
+            t.join()
+    finally:
+        snac.snac_set_tuning_rules(None)
+    assert not errors, errors
+    assert seen <= {(3, 2)}, seen  # 4 MiB is past table B's first 40 rules: both tables give (3, 2)
