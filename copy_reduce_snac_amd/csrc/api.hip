@@ -254,7 +254,8 @@ void finish_plan(Plan& p) {
     for (int j = 0; j < nj; ++j) {
       const Job jb = make_job(p.d, j);
       const uint32_t head = aligned ? 0u : job_head_bytes(p.d, jb);
-      tiles += job_tiles(jb, head, tile);
+      const uint64_t body = (jb.bytes - head) & ~(uint64_t)15;
+      tiles += job_tiles(jb, head, job_lead(p.d, jb, head, body, tile), tile);
     }
     return tiles;
   };

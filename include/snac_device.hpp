@@ -520,6 +520,7 @@ struct JobL {
   int32_t dst_rank;
   uint32_t head;
   uint32_t tile0;
+  uint32_t lead;  // body bytes before the destination's tile grid (job_lead)
 };
 
 // Build the job table and its tile numbering in LDS.  Returns the total
@@ -538,8 +539,10 @@ __device__ uint32_t build_table(const CollDesc& d, uint32_t tile_bytes, JobL* jo
       if (t < nj) {
         const Job jb = make_job(d, t);
         const uint32_t head = ALIGNED ? 0u : job_head_bytes(d, jb);
-        mine = (uint32_t)job_tiles(jb, head, tile_bytes);
-        jobs[t] = JobL{jb.src_off, jb.dst_off, jb.bytes, jb.src_rank, jb.dst_rank, head, 0u};
+        const uint64_t body = (jb.bytes - head) & ~(uint64_t)15;
+        const uint32_t lead = (uint32_t)job_lead(d, jb, head, body, tile_bytes);
+        mine = (uint32_t)job_tiles(jb, head, lead, tile_bytes);
+        jobs[t] = JobL{jb.src_off, jb.dst_off, jb.bytes, jb.src_rank, jb.dst_rank, head, 0u, lead};
       }
       uint32_t incl = mine;
 #pragma unroll
@@ -564,8 +567,10 @@ __device__ uint32_t build_table(const CollDesc& d, uint32_t tile_bytes, JobL* jo
     if (j < nj) {
       const Job jb = make_job(d, j);
       const uint32_t head = ALIGNED ? 0u : job_head_bytes(d, jb);
-      mine[i] = (uint32_t)job_tiles(jb, head, tile_bytes);
-      jobs[j] = JobL{jb.src_off, jb.dst_off, jb.bytes, jb.src_rank, jb.dst_rank, head, 0u};
+      const uint64_t body = (jb.bytes - head) & ~(uint64_t)15;
+      const uint32_t lead = (uint32_t)job_lead(d, jb, head, body, tile_bytes);
+      mine[i] = (uint32_t)job_tiles(jb, head, lead, tile_bytes);
+      jobs[j] = JobL{jb.src_off, jb.dst_off, jb.bytes, jb.src_rank, jb.dst_rank, head, 0u, lead};
     }
     sum += mine[i];
   }
@@ -595,7 +600,13 @@ __device__ uint32_t build_table(const CollDesc& d, uint32_t tile_bytes, JobL* jo
 // turn.  NU > 0 unrolls the multicast for the common case ndst == NU.
 template <int TH, int U, int CP, bool ALIGNED>
 __device__ __forceinline__ void store_one(char* p, uint32_t lane, uint32_t rem, const u32x4 (&v)[U]) {
-  if constexpr (ALIGNED) {  // units at or past rem fall outside the resource
+  // Buffer stores whenever the destination is 16-byte aligned: always on
+  // the aligned path, and on the generic path for body tiles, whose
+  // destination the job head has brought to a 128-byte line (the other
+  // destinations of a multicast reduce may sit elsewhere).  Units at or
+  // past rem fall outside the resource.  On MI355X the buffer form made
+  // single-wave multicast copies about 8 % faster than 64-bit global stores.
+  if (ALIGNED || ((uint32_t)(uintptr_t)p & 15u) == 0) {
     const __amdgpu_buffer_rsrc_t r = buffer_rsrc(p, rem);
 #pragma unroll
     for (int u = 0; u < U; ++u) bst16<CP>(r, lane + (uint32_t)u * TH * 16u, v[u]);
@@ -660,6 +671,7 @@ struct JobCursor {
     J.dst_rank = (int32_t)uniform((uint32_t)jobs[j].dst_rank);
     J.head = ALIGNED ? 0u : uniform(jobs[j].head);
     J.tile0 = uniform(jobs[j].tile0);
+    J.lead = TILE >= kLeadMinTile ? uniform(jobs[j].lead) : 0u;
     next_tile0 = j + 1 < nj ? uniform(jobs[j + 1].tile0) : 0xffffffffu;
   }
 
@@ -692,10 +704,16 @@ struct JobCursor {
     r.lt = tile - J.tile0;
     r.head = J.head;
     r.body = ALIGNED ? J.bytes : ((J.bytes - r.head) & ~(uint64_t)15);
-    r.toff = (uint64_t)r.head + (uint64_t)r.lt * TILE;
-    const uint64_t end = (uint64_t)r.head + r.body;
-    const uint64_t left = end > r.toff ? end - r.toff : 0;
-    r.rem = left > TILE ? TILE : (uint32_t)left;
+    if constexpr (TILE >= kLeadMinTile) {  // job_lead is always 0 for smaller tiles
+      const TileSpan sp = tile_span(r.head, J.lead, r.body, r.lt, TILE);
+      r.toff = sp.off;
+      r.rem = sp.bytes;
+    } else {
+      r.toff = (uint64_t)r.head + (uint64_t)r.lt * TILE;
+      const uint64_t end = (uint64_t)r.head + r.body;
+      const uint64_t left = end > r.toff ? end - r.toff : 0;
+      r.rem = left > TILE ? TILE : (uint32_t)left;
+    }
     return r;
   }
 };

@@ -176,13 +176,55 @@ SNAC_HD uint32_t job_head_bytes(const CollDesc& d, const Job& j) {
   return (uint32_t)h;
 }
 
-// Tiles of a job: tile_bytes-sized pieces of its 16-byte body; the head and
+// Body bytes of a job before its destination reaches a tile_bytes
+// boundary.  When a job's destination does not start on that grid, its
+// first tile is cut short there and every later tile covers one whole
+// aligned block of the destination.  Tiles offset from the grid straddle an
+// extra block each, which two workgroups then write at different times: on
+// MI355X that made write-heavy copies with uneven offsets up to 30 % slower
+// (AllGatherV, 8 ranks, 128 MiB).  Bodies shorter than two tiles keep the
+// plain split.  The body starts 16-byte aligned in the destination, so the
+// lead is a multiple of 16.
+SNAC_HD uint64_t job_lead_grid(const CollDesc& d, const Job& j, uint32_t head, uint64_t body, uint64_t tile_bytes) {
+  if (body < 2 * tile_bytes) return 0;
+  const int dr = j.dst_rank < 0 ? 0 : j.dst_rank;
+  const uint64_t a = (uint64_t)(uintptr_t)d.dst[dr] + j.dst_off + head;
+  return (tile_bytes - a % tile_bytes) % tile_bytes;
+}
+
+// The lead the kernels use: tiles of 16 KiB and more follow the destination
+// grid; smaller ones (the 4 KiB tiles of big one-to-one copies, the small-
+// tile kernels) keep the plain split, since aligning the 4 KiB tiles made
+// AllToAllV with Dirichlet counts 1.5 % slower (0.378 against 0.373 ms).
+constexpr uint64_t kLeadMinTile = 16384;
+
+SNAC_HD uint64_t job_lead(const CollDesc& d, const Job& j, uint32_t head, uint64_t body, uint64_t tile_bytes) {
+  return tile_bytes >= kLeadMinTile ? job_lead_grid(d, j, head, body, tile_bytes) : 0;
+}
+
+// Tiles of a job: a first piece of `lead` body bytes when lead > 0, then
+// tile_bytes-sized pieces of the rest of its 16-byte body; the head and
 // tail bytes ride on tile 0.  A job with bytes but no body still gets one.
-SNAC_HD uint64_t job_tiles(const Job& j, uint32_t head, uint64_t tile_bytes) {
+SNAC_HD uint64_t job_tiles(const Job& j, uint32_t head, uint64_t lead, uint64_t tile_bytes) {
   if (j.bytes == 0) return 0;
   const uint64_t body = (j.bytes - head) & ~(uint64_t)15;
-  const uint64_t t = (body + tile_bytes - 1) / tile_bytes;
+  const uint64_t t = (lead ? 1 : 0) + (body - lead + tile_bytes - 1) / tile_bytes;
   return t ? t : 1;
+}
+
+// Tile lt of a job (numbered as job_tiles does): its offset in the job and
+// its body bytes (a multiple of 16; 0 for an edge-only tile).
+struct TileSpan {
+  uint64_t off;
+  uint32_t bytes;
+};
+
+SNAC_HD TileSpan tile_span(uint32_t head, uint64_t lead, uint64_t body, uint32_t lt, uint64_t tile_bytes) {
+  if (lead && lt == 0) return TileSpan{head, (uint32_t)lead};
+  const uint64_t off = (uint64_t)head + lead + (uint64_t)(lead ? lt - 1 : lt) * tile_bytes;
+  const uint64_t end = (uint64_t)head + body;
+  const uint64_t left = end > off ? end - off : 0;
+  return TileSpan{off, (uint32_t)(left > tile_bytes ? tile_bytes : left)};
 }
 
 }  // namespace snac

@@ -40,6 +40,7 @@ int main() {
   const int colls[] = {kAllReduce, kReduceScatter, kAllGather, kAllToAll, kAllGatherV, kReduceScatterV, kAllToAllV};
   const int esizes[] = {1, 2, 4};
   int cases = 0;
+  long leads = 0;  // jobs whose tiles were cut to the destination grid
   for (int iter = 0; iter < 4000; ++iter) {
     const int coll = colls[rng() % 7];
     const bool reduce = coll_is_reduce(coll);
@@ -91,8 +92,11 @@ int main() {
     const int nj = num_jobs(d);
     CHECK(nj >= 0 && nj <= kMaxJobs, "coll %d: %d jobs", coll, nj);
     if (reduce) CHECK(nj <= kMaxRanks, "reduce coll %d: %d jobs", coll, nj);
-    const uint64_t tile_bytes[] = {16384, 2048, 1024, 4096};
-    uint64_t tiles[4] = {0, 0, 0, 0};
+    // the kernels' tile sizes, and small ones so that these small jobs also
+    // get tiles cut to the destination grid (bodies of two tiles or more)
+    const uint64_t tile_bytes[] = {16384, 2048, 1024, 4096, 512, 256};
+    constexpr int kTileSizes = 6;
+    uint64_t tiles[kTileSizes] = {};
     for (int j = 0; j < nj; ++j) {
       const Job jb = make_job(d, j);
       CHECK(jb.bytes % (uint64_t)e == 0, "coll %d job %d: %llu bytes not whole elements", coll, j,
@@ -107,17 +111,50 @@ int main() {
         if (jb.dst_off + jb.bytes <= out_b[t])
           for (uint64_t b = 0; b < jb.bytes; ++b) cover[t][jb.dst_off + b]++;
       }
-      const uint32_t head = job_head_bytes(d, jb);
-      CHECK(head <= jb.bytes && head < kHeadAlign && head % (uint32_t)e == 0, "coll %d job %d: head %u", coll, j, head);
-      for (int q = 0; q < 4; ++q) {
-        const uint64_t t = job_tiles(jb, head, tile_bytes[q]);
+      const uint32_t head_g = job_head_bytes(d, jb);
+      CHECK(head_g <= jb.bytes && head_g < kHeadAlign && head_g % (uint32_t)e == 0, "coll %d job %d: head %u", coll,
+            j, head_g);
+      // the generic path's head, and the aligned path's (none) where the job
+      // qualifies for it: 16-byte aligned destination and length
+      const int dr0 = jb.dst_rank < 0 ? 0 : jb.dst_rank;
+      const bool al = ((uint64_t)(uintptr_t)d.dst[dr0] + jb.dst_off) % 16 == 0 && jb.bytes % 16 == 0;
+      for (int path = 0; path < (al ? 2 : 1); ++path)
+      for (int q = 0; q < kTileSizes; ++q) {
+        const uint32_t head = path == 0 ? head_g : 0u;
+        const uint64_t T = tile_bytes[q];
         const uint64_t body = jb.bytes ? (jb.bytes - head) & ~(uint64_t)15 : 0;
+        // the kernels align only 16 KiB tiles (job_lead); the grid rule
+        // itself is checked at every size here
+        CHECK(job_lead(d, jb, head, body, T) == (T >= kLeadMinTile ? job_lead_grid(d, jb, head, body, T) : 0),
+              "coll %d job %d: job_lead", coll, j);
+        const uint64_t lead = job_lead_grid(d, jb, head, body, T);
+        const uint64_t t = job_tiles(jb, head, lead, T);
         CHECK(jb.bytes == 0 ? t == 0 : t >= 1, "coll %d job %d: %llu tiles", coll, j, (unsigned long long)t);
-        CHECK(t * tile_bytes[q] >= body && (t == 0 || (t - 1) * tile_bytes[q] < body || body == 0),
-              "coll %d job %d: tiles do not fit the body", coll, j);
         CHECK(jb.bytes - head - body < 16, "coll %d job %d: tail of %llu bytes", coll, j,
               (unsigned long long)(jb.bytes - head - body));
-        tiles[q] += t;
+        CHECK(lead < T && lead % 16 == 0 && lead <= body, "coll %d job %d: lead %llu", coll, j,
+              (unsigned long long)lead);
+        if (lead) ++leads;
+        // the tiles, as the kernels number them, cover the body once and in
+        // order; every tile after the lead starts on the destination's grid
+        const int dr = jb.dst_rank < 0 ? 0 : jb.dst_rank;
+        const uint64_t dst0 = (uint64_t)(uintptr_t)d.dst[dr] + jb.dst_off;
+        uint64_t next = head;
+        for (uint64_t lt = 0; lt < t; ++lt) {
+          const TileSpan sp = tile_span(head, lead, body, (uint32_t)lt, T);
+          CHECK(sp.off == next, "coll %d job %d tile %llu: starts at %llu, not %llu", coll, j,
+                (unsigned long long)lt, (unsigned long long)sp.off, (unsigned long long)next);
+          CHECK(sp.bytes <= T && sp.bytes % 16 == 0, "coll %d job %d tile %llu: %u bytes", coll, j,
+                (unsigned long long)lt, sp.bytes);
+          CHECK(sp.bytes > 0 || body == 0, "coll %d job %d tile %llu: empty", coll, j, (unsigned long long)lt);
+          if (lead && lt > 0)
+            CHECK((dst0 + sp.off) % T == 0, "coll %d job %d tile %llu: off the destination grid", coll, j,
+                  (unsigned long long)lt);
+          next = sp.off + sp.bytes;
+        }
+        CHECK(next == head + body, "coll %d job %d: tiles end at %llu, body at %llu", coll, j,
+              (unsigned long long)next, (unsigned long long)(head + body));
+        if (path == 0) tiles[q] += t;
       }
     }
     for (int t = 0; t < n; ++t)
@@ -129,6 +166,6 @@ int main() {
         }
     ++cases;
   }
-  std::printf("%d layouts checked, %d failures\n", cases, failures);
+  std::printf("%d layouts checked, %ld jobs with a lead tile, %d failures\n", cases, leads, failures);
   return failures ? 1 : 0;
 }

@@ -22,3 +22,5 @@ def test_layout_engine_under_sanitizers(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stderr[-3000:] + r.stdout[-1000:]
     assert "0 failures" in r.stdout
+    leads = int(r.stdout.split(" jobs with a lead tile")[0].split()[-1])
+    assert leads > 0, "no job got tiles cut to the destination grid: " + r.stdout
