@@ -57,12 +57,38 @@ KERNEL_SOURCES = ("include/snac_device.hpp", "include/snac_layout.hpp", "include
                   "copy_reduce_snac_amd/csrc/collectives.hip", "copy_reduce_snac_amd/csrc/internal.hpp")
 
 
+def code_only(src: str) -> str:
+    """C/C++ source without its comments and with whitespace runs collapsed,
+    so that edits to comments or layout alone do not count as kernel
+    changes.  String and character literals are kept as they are."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, name), "rb") as f:
+        with open(os.path.join(ROOT, name), encoding="utf-8") as f:
             h.update(name.encode())
-            h.update(f.read())
+            h.update(code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

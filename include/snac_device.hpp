@@ -482,7 +482,9 @@ __device__ inline bool group_barrier(const snac_dev_ctx& c, uint32_t blocks) {
 // each source.  Every workgroup rebuilds the job table in LDS from the
 // descriptor, numbers the tiles of all jobs with an exclusive scan, and
 // walks tiles block, block + blocks, ...  A lane moves U = kTileBytes /
-// (TH * 16) 16-byte units per tile.
+// (TH * 16) 16-byte units per tile.  A job whose destination does not start
+// on the 16 KiB grid first gets a short tile up to it (job_lead), so that
+// every later tile fills one aligned block of the destination.
 //
 //  * copy: the U loads of a tile, then its stores to one destination or to
 //    all of them (a multicast: one read, N writes).
@@ -500,8 +502,9 @@ __device__ inline bool group_barrier(const snac_dev_ctx& c, uint32_t blocks) {
 //    resource is sized to the tile, so partial tiles need no guards.
 //  * generic: any element-aligned address.  Each job is split into a head
 //    (bytes until the destination reaches a 128-byte line), a body of
-//    aligned 16-byte stores whose sources are read with ld16_any, and a
-//    tail; head and tail move one element per lane in tile 0 of the job.
+//    aligned 16-byte stores (buffer stores, as above) whose sources are read
+//    with ld16_any, and a tail; head and tail move one element per lane in
+//    tile 0 of the job.
 
 constexpr uint32_t kTileBytes = 16384;
 

@@ -380,3 +380,18 @@ def test_tuning_tables_survive_concurrent_use():
         snac.snac_set_tuning_rules(None)
     assert not errors, errors
     assert seen <= {(3, 2)}, seen  # 4 MiB is past table B's first 40 rules: both tables give (3, 2)
+
+
+def test_kernel_hash_ignores_comments_only():
+    """bench.py reports counter-based traffic only while the counters match
+    the kernel sources; comments and layout must not count as changes."""
+    import sys
+
+    sys.path.insert(0, ROOT)
+    import bench
+
+    src = 'int a = 1; // note\n/* block\n comment */ const char* s = "//x /*y*/";  char q = \'"\';\n'
+    assert bench.code_only(src) == 'int a = 1; const char* s = "//x /*y*/"; char q = \'"\';'
+    assert bench.code_only("a  +\n\tb") == bench.code_only("a + b")
+    assert bench.code_only("a + b") != bench.code_only("a - b")
+    assert len(bench.kernel_source_hash()) == 16
