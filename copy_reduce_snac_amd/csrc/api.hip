@@ -124,8 +124,8 @@ constexpr uint32_t kMaxPipeTile = 2048u * 1024u;
 constexpr uint32_t kMinPipeTile = 4096u;
 constexpr uint32_t kMinAutoSlots = 64u;
 constexpr uint32_t kMaxFlagSlots = 4096u;
-constexpr uint64_t kTargetTiles = 64u;  // tiles per message the pipeline aims for
-constexpr uint32_t kMinSplitTile = 65536u;  // ... but no smaller tiles than this
+constexpr uint32_t kMinSplitTile = 65536u;  // smallest tile a call cuts the ring into
+constexpr uint32_t kMaxCallTile = 16u << 20;  // largest tile a call merges slots into
 constexpr size_t kDefaultStaging = 64u * 1024u * 1024u;
 constexpr int kDefaultSpinLog2 = 22;
 
@@ -138,13 +138,11 @@ constexpr int kDefaultSpinLog2 = 22;
 // destinations are written per input byte, so inputs small enough for the
 // Infinity Cache stay there across calls (6.3-6.7 TB/s against 4.9 with
 // streaming loads when they are reused; no difference when they are not).
-// The pipeline runs one workgroup per CU up to 8 MiB per rank (fewer
-// waiting workgroups: at 1 MiB 24.6 us against 31.3, at 4 MiB 60 against
-// 94) and two above that (with 64 tiles per message: bf16 4096x8192 0.34 ms
-// against 0.39 at four per CU with 128 tiles).
+// The pipeline runs one workgroup per CU at every size: bf16 4096x8192
+// N=8, 2 MiB tiles, 295 us against 391 at two per CU; f32 with 4 MiB tiles
+// 604 against 771 (at 1 MiB per rank: 24.6 us against 31.3).
 const snac_tuning_rule kBuiltinRules[] = {
-    {SNAC_RULE_PIPELINE, 1, SNAC_MAX_RANKS, 0, 0, 8u << 20, 1, 0},
-    {SNAC_RULE_PIPELINE, 1, SNAC_MAX_RANKS, 0, (8u << 20) + 1, UINT64_MAX, 2, 0},
+    {SNAC_RULE_PIPELINE, 1, SNAC_MAX_RANKS, 0, 0, UINT64_MAX, 1, 0},
     // multicast copies: cached loads, streaming stores.  AllGather bf16 N=8,
     // 16 MiB per rank in: 180 us against 210 with streaming loads when a
     // producer kernel had just written the inputs, 228 against 235 right
@@ -744,20 +742,41 @@ snac_status snac_pipeline_scale_reduce(snac_ctx* ctx, const void* const* x, void
   a.freed = ctx->freed;
   a.ctrl = ctx->ctrl;
   a.abort_word = ctx->abort_dev;
-  // Tile of this call: the context's, halved (doubling the slots of the same
-  // ring) while the message would have fewer than kTargetTiles tiles, down
-  // to 64 KiB.  On MI355X about 64 tiles per message (1 MiB per rank for
-  // bf16 4096x8192, 2 MiB for f32) with two workgroups per CU ran best --
-  // bigger items mean fewer release and acquire fences, which serialise
-  // GPU-wide -- and smaller tiles only add per-item overhead.
+  // Tile of this call, cut from the context's ring (slots * tile bytes per
+  // rank): about one producer item per workgroup, N * tiles ~ the grid.
+  // Bigger items mean fewer release and acquire fences, which serialise
+  // GPU-wide; fewer items than workgroups leave some idle.  On MI355X, one
+  // workgroup per CU: bf16 4096x8192 N=8 took 295 us with 32 tiles of 2 MiB,
+  // 309 with 64 of 1 MiB, 408 with 16 of 4 MiB; f32 604 us with 32 tiles of
+  // 4 MiB, 631 with 64 of 2 MiB.  Slots are merged only while the message
+  // still fits the ring in one pass, and split no finer than 64 KiB.
+  const uint64_t msg = count * (uint64_t)e;
+  const LaunchCfg cfg = launch_cfg(SNAC_RULE_PIPELINE, n, e, msg);
   const snac_tuning tn = tuning_now();
   uint32_t tile = ctx->tile_bytes, slots = ctx->slots;
   if (!tn.pipeline_tile_bytes) {
-    while (tile / 2 >= kMinSplitTile && (uint64_t)slots * 2 <= ctx->flag_slots &&
-           (count * (uint64_t)e + tile - 1) / tile < kTargetTiles) {
+    const uint64_t ring = (uint64_t)slots * tile;
+    const uint64_t grid = (uint64_t)(device_cu_count() > 0 ? device_cu_count() : 1) * (uint64_t)pipe_wgs_per_cu(cfg);
+    const uint64_t target = (grid + (uint64_t)n - 1) / (uint64_t)n;
+    auto tiles_of = [&](uint64_t t) { return (msg + t - 1) / t; };
+    while (msg <= ring && slots % 2 == 0 && slots / 2 >= 2 && (uint64_t)tile * 2 <= kMaxCallTile &&
+           tiles_of((uint64_t)tile * 2) >= target) {
+      tile <<= 1;
+      slots >>= 1;
+    }
+    while (tile / 2 >= kMinSplitTile && (uint64_t)slots * 2 <= ctx->flag_slots && tiles_of(tile) < target) {
       tile >>= 1;
       slots <<= 1;
     }
+  }
+  // A message that fits the ring takes only the slots it needs (rounded up
+  // to 16: 8 queues of at least 2 slots), so that the staging units, which
+  // interleave the slots, sweep as compact a window as x and out.  bf16
+  // 4096x8192 N=8 in a 128 MiB ring with 2 MiB tiles: 284 us on 32 slots,
+  // 295 on all 64.
+  {
+    const uint64_t need = ((msg + tile - 1) / tile + 15) / 16 * 16;
+    if (msg <= (uint64_t)slots * tile && need < slots) slots = (uint32_t)need;
   }
   a.slots = slots;
   a.tile_bytes = tile;
@@ -765,8 +784,7 @@ snac_status snac_pipeline_scale_reduce(snac_ctx* ctx, const void* const* x, void
   a.spin_limit_log2 = (uint32_t)(tn.spin_limit_log2 ? tn.spin_limit_log2 : kDefaultSpinLog2);
   a.drop_notify = tn.debug_drop_notify;
   a.producer_delay_us = (uint32_t)tn.debug_producer_delay;
-  hipError_t err = launch_pipeline(a, dtype == SNAC_BF16, launch_cfg(SNAC_RULE_PIPELINE, n, e, count * (uint64_t)e),
-                                   (hipStream_t)stream, nullptr);
+  hipError_t err = launch_pipeline(a, dtype == SNAC_BF16, cfg, (hipStream_t)stream, nullptr);
   if (err != hipSuccess) return hip_fail(err, "pipeline launch");
   return ok();
 }

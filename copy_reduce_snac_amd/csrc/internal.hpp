@@ -56,7 +56,7 @@ struct PipeArgs {
   uint64_t count;      // elements
   int32_t nranks;
   int32_t esize;
-  char* staging;       // [nranks][slots][tile_bytes]
+  char* staging;       // [nranks][slots * tile_bytes], units of slots interleaved
   uint64_t* ready;     // [nranks][slots], kFlagStride words apart
   uint64_t* freed;     // [slots][nranks] (one flag per consumer part)
   uint64_t* ctrl;      // control words, kFlagStride apart (kCtrl*)
@@ -75,8 +75,12 @@ struct PipeArgs {
   uint32_t queues;      // independent ticket queues (tile t -> queue t % queues)
   uint32_t qslots;      // slots per queue
   uint32_t rounds;      // max over queues of ceil(tiles_q / qslots)
-  uint32_t tile_elems;  // tile_bytes / esize
-  uint32_t part_elems;  // elements per consumer part (multiple of 16 / esize)
+  uint32_t unit_shift;   // a layout unit is 1 << unit_shift pieces (4 KiB each)
+  uint32_t unit_bytes;   // bytes per unit
+  uint32_t full_units;   // whole units in a rank's message
+  uint32_t tail_tile;    // the tile that owns the short last unit: full_units % tiles
+  uint32_t tail_pieces;  // whole pieces of that unit
+  uint32_t last_bytes;   // bytes of the message's short last piece (0: none)
 };
 
 // control words (uint64 indices into ctrl)
@@ -92,6 +96,8 @@ enum : uint32_t {
 constexpr uint32_t kFlagStride = SNAC_FLAG_STRIDE;  // uint64 words between flags (128 B)
 constexpr uint32_t kUserFlags = 1024;               // flags handed to device-side users
 
+// workgroups per CU of a pipeline launch under cfg
+int pipe_wgs_per_cu(const LaunchCfg& cfg);
 hipError_t launch_pipeline(const PipeArgs& a, int dtype_bf16, const LaunchCfg& cfg, hipStream_t stream,
                            uint32_t* grid_out);
 

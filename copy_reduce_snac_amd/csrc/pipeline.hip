@@ -4,19 +4,31 @@
 //
 // Work items.  The message (count elements per rank) is cut into tiles of
 // tile_bytes per rank.  Tile t of rank r has a producer item P(t, r); the
-// reduction of tile t is split into N consumer parts C(t, p), each reducing
-// 1/N of the tile's elements across all N ranks, so every item moves about
-// the same number of bytes.  Tiles are dealt round-robin to Q independent
-// queues (tile t -> queue t % Q), each with its own ring of staging slots
-// and its own ticket counter; workgroup b draws tickets from queue b % Q.
-// Within a queue, local tile g has group g of the ticket order holding
-// P(g, 0..N-1) followed by C(g - L, 0..N-1), so consumers trail their
-// producers by L tiles (the lookahead).
+// reduction of tile t is split into N consumer parts C(t, p), so every item
+// moves about the same number of bytes.  Tiles are dealt round-robin to Q
+// independent queues (tile t -> queue t % Q), each with its own ring of
+// staging slots and its own ticket counter; workgroup b draws tickets from
+// queue b % Q.  Within a queue, local tile g has group g of the ticket order
+// holding P(g, 0..N-1) followed by C(g - L, 0..N-1), so consumers trail
+// their producers by L tiles (the lookahead).
+//
+// Layout.  Each rank's message is a row of layout units of 1, 2 or 4
+// pieces, a piece being 4 KiB (one 16-byte access per lane of a 256-lane
+// workgroup).  Of nt tiles, tile t owns units t, t + nt, t + 2 nt, ..., and
+// in the rank's staging ring unit j of slot s sits at unit j * slots + s.
+// All the items in flight therefore sweep one compact window of x, staging
+// and out together instead of streaming through separate contiguous tiles:
+// on MI355X (bf16 4096x8192, N=8, 16 KiB units) the producer phase alone
+// took 182 us this way against 201 us with contiguous 1 MiB tiles, and the
+// consumer phase 95 against 107 us.  Producers take a tile's pieces in
+// order; consumer part p takes pieces p, p + N, p + 2 N, ...  Only the
+// message's last unit can be short (whole pieces, then at most one short
+// piece); it belongs to tile (whole units) % nt.
 //
 //   P(t, r)  Stage:   wait until the tile's slot is free (all N consumer
 //                     parts of the slot's previous tile are done), compute
 //                     y = 0.5 * x_r + r in binary32, round to the data type,
-//                     store into staging[r][slot].
+//                     store into the slot's units of staging[r].
 //            Notify:  every wave waits until its stores are accepted by
 //                     the L2, the workgroup meets at a barrier, and one lane
 //                     issues the agent-scope release fence (L2 write-back),
@@ -24,13 +36,14 @@
 //   C(t, p)  Consume: one lane polls ready[r][slot] >= seq for every r
 //                     (relaxed loads with s_sleep back-off) and issues one
 //                     agent-scope acquire fence; barrier; N-to-1 reduce of
-//                     part p of the staged tile into out; barrier; one lane
+//                     the staged units of part p into out; barrier; one lane
 //                     stores freed[slot][p] = seq.
 //
 // One fence per item, not one per wave: agent-scope fences write back or
 // invalidate a whole L2 and serialise across the GPU (measured on MI355X at
 // about 28 ns per workgroup-fence with every CU fencing), so they set the
-// cost of small tiles.
+// cost of small tiles; the host cuts the ring into about one producer item
+// per workgroup.
 //
 // Forward progress: within a queue a workgroup only ever waits for items
 // with smaller tickets of the same queue (P(g) waits for C(g - S), ticketed
@@ -85,10 +98,28 @@ __device__ __forceinline__ u32x4 scale_unit(u32x4 x, float r) {
 // compiler cannot prove a loop exit uniform it may restructure the loop so
 // that lanes of one wave reach a barrier on different iterations.
 
-// Elements of tile t (the last tile may be short).
-__device__ __forceinline__ uint32_t tile_count(const PipeArgs& a, uint32_t t) {
-  const uint64_t e0 = (uint64_t)t * a.tile_elems;
-  return uniform(t + 1 < a.tiles ? a.tile_elems : (uint32_t)(a.count - e0));
+// A piece is one 16-byte access for each of the kThreads lanes; a layout
+// unit is 1 << unit_shift pieces (a.unit_bytes).
+constexpr uint32_t kPiece = kThreads * 16u;
+
+// Where piece s of tile t lives, as byte offsets from the tile's first unit
+// in x / out (units nt apart) and from the slot's first unit in staging
+// (units `slots` apart).
+struct PieceAt {
+  uint64_t x, stg;
+};
+__device__ __forceinline__ PieceAt piece_at(const PipeArgs& a, uint32_t s) {
+  const uint64_t j = s >> a.unit_shift;
+  const uint64_t w = (uint64_t)(s & ((1u << a.unit_shift) - 1u)) * kPiece;
+  return PieceAt{j * a.tiles * a.unit_bytes + w, j * a.slots * a.unit_bytes + w};
+}
+
+// Whole pieces of tile t: its units below the message's whole units, and on
+// the tile holding the short last unit, that unit's whole pieces.  The one
+// short piece (if any) follows them.
+__device__ __forceinline__ uint32_t tile_pieces(const PipeArgs& a, uint32_t t) {
+  const uint32_t jf = a.full_units > t ? (a.full_units - t + a.tiles - 1) / a.tiles : 0u;
+  return uniform((jf << a.unit_shift) + (t == a.tail_tile ? a.tail_pieces : 0u));
 }
 
 template <typename T, int N>
@@ -114,33 +145,39 @@ __device__ void stage_item(const PipeArgs& a, uint32_t t, uint32_t gslot, uint32
       while (wall_clock64() < until) __builtin_amdgcn_s_sleep(8);
     }
   }
-  const uint64_t e0 = (uint64_t)t * a.tile_elems;
-  const uint32_t nbytes = tile_count(a, t) * E;
-  const char* src = static_cast<const char*>(a.x[r]) + e0 * E;
-  char* stg = a.staging + ((uint64_t)r * a.slots + gslot) * a.tile_bytes;
+  const uint32_t np = tile_pieces(a, t);
+  const char* src = static_cast<const char*>(a.x[r]) + (uint64_t)t * a.unit_bytes;
+  char* stg = a.staging + (uint64_t)r * a.slots * a.tile_bytes + (uint64_t)gslot * a.unit_bytes;
   const float rf = (float)r;
-  const uint32_t nvec = nbytes & ~15u;
-  constexpr int U = 4;
+  const uint32_t lane = threadIdx.x * 16u;
+  constexpr uint32_t U = 4;
   // staging stores write through the L2 (see kWriteThrough), so the release
   // fence below has little left to write back
-  const __amdgpu_buffer_rsrc_t stg_r = buffer_rsrc(stg, nvec);
-  for (uint32_t base = 0; base < nvec; base += kThreads * 16u * U) {
+  uint32_t s = 0;
+  for (; s + U <= np; s += U) {
     u32x4 v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t o = base + (threadIdx.x + (uint32_t)u * kThreads) * 16u;
-      if (o < nvec) v[u] = ld16<kCacheStreamLoads>(src + o);
-    }
+    for (uint32_t u = 0; u < U; ++u) v[u] = ld16<kCacheStreamLoads>(src + piece_at(a, s + u).x + lane);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t o = base + (threadIdx.x + (uint32_t)u * kThreads) * 16u;
-      if (o < nvec) bst16<kWriteThrough>(stg_r, o, scale_unit<T>(v[u], rf));
-    }
+    for (uint32_t u = 0; u < U; ++u)
+      bst16<kWriteThrough>(buffer_rsrc(stg + piece_at(a, s + u).stg, kPiece), lane, scale_unit<T>(v[u], rf));
   }
-  const uint32_t tail = (nbytes - nvec) / E;
-  if (threadIdx.x < tail) {
-    const uint32_t o = nvec + threadIdx.x * E;
-    store_elem<T>(stg + o, load_elem<T>(src + o) * 0.5f + rf);
+  for (; s < np; ++s) {
+    const PieceAt p = piece_at(a, s);
+    bst16<kWriteThrough>(buffer_rsrc(stg + p.stg, kPiece), lane, scale_unit<T>(ld16<kCacheStreamLoads>(src + p.x + lane), rf));
+  }
+  if (a.last_bytes && t == a.tail_tile) {  // the message's short last piece, piece np of this tile
+    const PieceAt p = piece_at(a, np);
+    const char* xs = src + p.x;
+    char* d = stg + p.stg;
+    const uint32_t nvec = a.last_bytes & ~15u;
+    if (lane < nvec)
+      bst16<kWriteThrough>(buffer_rsrc(d, nvec), lane, scale_unit<T>(ld16<kCacheStreamLoads>(xs + lane), rf));
+    const uint32_t tail = (a.last_bytes - nvec) / E;
+    if (threadIdx.x < tail) {
+      const uint32_t o = nvec + threadIdx.x * E;
+      store_elem<T>(d + o, load_elem<T>(xs + o) * 0.5f + rf);
+    }
   }
   // Notify.  Every wave waits until the L2 has accepted its staging stores;
   // after the barrier one lane writes the L2 back at agent scope (a single
@@ -179,43 +216,59 @@ __device__ void consume_item(const PipeArgs& a, uint32_t t, uint32_t gslot, uint
   const uint32_t ok = uniform(*s_ok);
   __syncthreads();
   if (ok == 0) return;
-  const uint32_t ne = tile_count(a, t);
-  const uint32_t p0 = part * a.part_elems;
-  const uint32_t pn = p0 >= ne ? 0u : (ne - p0 < a.part_elems ? ne - p0 : a.part_elems);
-  const uint32_t nbytes = pn * E;
+  // this part's pieces of the tile: part + N i
+  const uint32_t np = tile_pieces(a, t);
+  const uint32_t ni = uniform(np > part ? (np - part + (uint32_t)N - 1) / (uint32_t)N : 0u);
   const uint64_t rank_stride = (uint64_t)a.slots * a.tile_bytes;
-  const char* stg = a.staging + (uint64_t)gslot * a.tile_bytes + (uint64_t)p0 * E;
-  char* out = static_cast<char*>(a.out) + ((uint64_t)t * a.tile_elems + p0) * E;
-  const uint32_t nvec = nbytes & ~15u;
+  const char* stg = a.staging + (uint64_t)gslot * a.unit_bytes;
+  char* out = static_cast<char*>(a.out) + (uint64_t)t * a.unit_bytes;
+  const uint32_t lane = threadIdx.x * 16u;
   // the output is written through the L2 as the staging is: the producers'
   // release fences write back every dirty line of their XCD's L2, and
   // write-back output lines would add to that (f32 4096x8192 N=8: 0.629 ms
   // against 0.638 with streaming write-back stores; bf16 0.2-0.6 % faster)
-  const __amdgpu_buffer_rsrc_t out_r = buffer_rsrc(out, nvec);
-  constexpr int U = N <= 4 ? 2 : 1;
-  for (uint32_t base = 0; base < nvec; base += kThreads * 16u * U) {
+  constexpr uint32_t U = N <= 4 ? 2 : 1;
+  uint32_t i = 0;
+  for (; i + U <= ni; i += U) {
     u32x4 v[U][N];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t o = base + (threadIdx.x + (uint32_t)u * kThreads) * 16u;
-      if (o < nvec) {
+    for (uint32_t u = 0; u < U; ++u) {
+      const uint64_t so = piece_at(a, part + (uint32_t)N * (i + u)).stg;
 #pragma unroll
-        for (int k = 0; k < N; ++k) v[u][k] = bld16<kWriteThrough>(buffer_rsrc(stg + k * rank_stride, nvec), o);
-      }
+      for (int k = 0; k < N; ++k) v[u][k] = bld16<kWriteThrough>(buffer_rsrc(stg + k * rank_stride + so, kPiece), lane);
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t o = base + (threadIdx.x + (uint32_t)u * kThreads) * 16u;
-      if (o < nvec) bst16<kWriteThrough>(out_r, o, reduce_unit<T, N>(v[u]));
+    for (uint32_t u = 0; u < U; ++u) {
+      const uint64_t oo = piece_at(a, part + (uint32_t)N * (i + u)).x;
+      bst16<kWriteThrough>(buffer_rsrc(out + oo, kPiece), lane, reduce_unit<T, N>(v[u]));
     }
   }
-  const uint32_t tail = (nbytes - nvec) / E;
-  if (threadIdx.x < tail) {
-    const uint32_t o = nvec + threadIdx.x * E;
-    float acc = load_elem<T>(stg + o);
+  for (; i < ni; ++i) {
+    u32x4 v[N];
+    const PieceAt p = piece_at(a, part + (uint32_t)N * i);
 #pragma unroll
-    for (int k = 1; k < N; ++k) acc = acc + load_elem<T>(stg + k * rank_stride + o);
-    store_elem<T>(out + o, acc);
+    for (int k = 0; k < N; ++k) v[k] = bld16<kWriteThrough>(buffer_rsrc(stg + k * rank_stride + p.stg, kPiece), lane);
+    bst16<kWriteThrough>(buffer_rsrc(out + p.x, kPiece), lane, reduce_unit<T, N>(v));
+  }
+  if (a.last_bytes && t == a.tail_tile && np % (uint32_t)N == part) {  // the short last piece, piece np
+    const PieceAt p = piece_at(a, np);
+    const char* s = stg + p.stg;
+    char* d = out + p.x;
+    const uint32_t nvec = a.last_bytes & ~15u;
+    if (lane < nvec) {
+      u32x4 v[N];
+#pragma unroll
+      for (int k = 0; k < N; ++k) v[k] = bld16<kWriteThrough>(buffer_rsrc(s + k * rank_stride, nvec), lane);
+      bst16<kWriteThrough>(buffer_rsrc(d, nvec), lane, reduce_unit<T, N>(v));
+    }
+    const uint32_t tail = (a.last_bytes - nvec) / E;
+    if (threadIdx.x < tail) {
+      const uint32_t o = nvec + threadIdx.x * E;
+      float acc = load_elem<T>(s + o);
+#pragma unroll
+      for (int k = 1; k < N; ++k) acc = acc + load_elem<T>(s + k * rank_stride + o);
+      store_elem<T>(d + o, acc);
+    }
   }
   // Free the slot.  This edge only has to order this workgroup's staging
   // loads before the producer's next stores to the slot: every load has
@@ -288,6 +341,10 @@ __global__ __launch_bounds__(kThreads) void pipeline_kernel(const PipeArgs a) {
 
 using PipeFn = void (*)(const PipeArgs);
 
+// One workgroup per CU unless a rule or the tuning says otherwise: with
+// about one producer item per workgroup, more workgroups only wait.
+int pipe_wgs_per_cu(const LaunchCfg& cfg) { return cfg.wgs_per_cu > 0 ? cfg.wgs_per_cu : 1; }
+
 template <typename T>
 static PipeFn pipe_kernel(int n) {
   switch (n) {
@@ -317,6 +374,16 @@ hipError_t launch_pipeline(const PipeArgs& in, int dtype_bf16, const LaunchCfg& 
   PipeFn fn = dtype_bf16 ? pipe_kernel<BF16>(a.nranks) : pipe_kernel<F32>(a.nranks);
   if (!fn) return hipErrorInvalidValue;
   const uint64_t e = (uint64_t)a.esize;
+  // The layout needs whole pieces per tile.  A unit is 4 pieces (16 KiB),
+  // or fewer where they do not divide the tile; at 16 ranks one piece.
+  // Measured on MI355X, bf16 64 MiB per rank: N = 6 and 8 ran fastest with
+  // 16 KiB units (N=8: 283 us against 289 with 8 KiB and 297 with 4 KiB),
+  // N = 12 alike within 2 %, N = 16 with 4 KiB units (554 us against 600
+  // with 16 KiB and 625 with 8 KiB).
+  if (a.tile_bytes == 0 || a.tile_bytes % kPiece) return hipErrorInvalidValue;
+  uint32_t shift = a.nranks >= 16 ? 0u : 2u;
+  while (shift > 0 && (a.tile_bytes / kPiece) % (1u << shift)) --shift;
+  const uint64_t ub = (uint64_t)kPiece << shift;
   const uint64_t te = a.tile_bytes / e;
   const uint64_t tiles = (a.count + te - 1) / te;
   if (tiles == 0) return hipSuccess;
@@ -332,10 +399,7 @@ hipError_t launch_pipeline(const PipeArgs& in, int dtype_bf16, const LaunchCfg& 
   hipError_t err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), kThreads, 0);
   if (err != hipSuccess) return err;
   if (per_cu < 1) per_cu = 1;
-  // Measured on MI355X: when the ring holds the whole message no producer
-  // waits for a slot and 4 workgroups per CU keep HBM busiest; when slots
-  // are reused, more workgroups only add waiting ones, and 2 did best.
-  const int want = cfg.wgs_per_cu > 0 ? cfg.wgs_per_cu : (qtiles <= S ? 4 : 2);
+  const int want = pipe_wgs_per_cu(cfg);
   if (want < per_cu) per_cu = want;
   const int cus = device_cu_count();
   uint64_t grid = (uint64_t)(cus > 0 ? cus : 1) * (uint64_t)per_cu;
@@ -355,11 +419,15 @@ hipError_t launch_pipeline(const PipeArgs& in, int dtype_bf16, const LaunchCfg& 
   a.grid = (uint32_t)grid;
   a.tiles = (uint32_t)tiles;
   a.rounds = (uint32_t)((qtiles + S - 1) / S);
-  a.tile_elems = (uint32_t)te;
-  const uint64_t vec = 16 / e;  // elements per 16-byte unit
-  uint64_t pe = (te + (uint64_t)a.nranks - 1) / (uint64_t)a.nranks;
-  pe = (pe + vec - 1) / vec * vec;
-  a.part_elems = (uint32_t)pe;
+  const uint64_t nbytes = a.count * e;
+  const uint64_t full = nbytes / ub;
+  if ((full << shift) >= 0xffffffffull) return hipErrorInvalidValue;
+  a.unit_shift = shift;
+  a.unit_bytes = (uint32_t)ub;
+  a.full_units = (uint32_t)full;
+  a.tail_tile = (uint32_t)(full % tiles);
+  a.tail_pieces = (uint32_t)(nbytes % ub / kPiece);
+  a.last_bytes = (uint32_t)(nbytes % kPiece);
   if (grid_out) *grid_out = (uint32_t)grid;
   hipLaunchKernelGGL(fn, dim3((uint32_t)grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();

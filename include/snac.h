@@ -149,9 +149,12 @@ const char* snac_last_error(void);
  *                           pipeline tile size: the tuning value if set,
  *                           else the largest power of two up to 2 MiB that
  *                           leaves at least 64 slots (minimum 4 KiB).  Without
- *                           a tuning value a call halves the tile (doubling
- *                           the slots) while its message would have fewer
- *                           than 64 tiles, down to 64 KiB.  The size must be
+ *                           a tuning value a call re-cuts the same ring for
+ *                           about one producer item per workgroup (N * tiles
+ *                           ~ workgroups): it merges slots into tiles of up to
+ *                           16 MiB while the message fits the ring, and
+ *                           splits them down to 64 KiB while there are fewer
+ *                           tiles than that.  The size must be
  *                           a multiple of the tile and give at least 2
  *                           slots.  A ring that holds a whole message runs
  *                           fastest.
@@ -418,8 +421,11 @@ typedef struct snac_tuning {
   int32_t wgs_per_cu;      /* workgroups per compute unit in the persistent grid
                               (0: the kernel default -- for messages of at
                               least one 16 KiB tile per CU, 1 for reduces of
-                              >= 3 sources, else 2; for smaller messages,
-                              4 for reduces and AllGather(V), else 2) */
+                              >= 3 sources, else 2; for one-to-one copies
+                              moving >= 1 GiB, 5 single-wave workgroups (4
+                              when a job is not 16-byte aligned); for smaller
+                              messages, 4 for reduces and AllGather(V), else
+                              2; 1 for the pipeline) */
   int32_t cache_policy;    /* 0 library default (= 1), 1 streaming (non-temporal)
                               loads and stores, 2 streaming stores only,
                               3 streaming loads only, 4 cached loads and stores */

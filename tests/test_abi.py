@@ -248,9 +248,9 @@ def test_builtin_tuning_rules_and_lookup():
     assert snac.snac_tuning_lookup(snac.SNAC_COLL_ALL_GATHER_V, 8, 2, 1)["cache_policy"] == 2
     assert snac.snac_tuning_lookup(snac.SNAC_COLL_ALL_TO_ALL, 8, 4, 1)["cache_policy"] == 1
     assert snac.snac_tuning_lookup(snac.SNAC_RULE_ATOM_COPY, 1, 1, 1)["cache_policy"] == 1
-    # the pipeline: one WG per CU for small messages, its own grid above 8 MiB
+    # the pipeline: one WG per CU at every size
     assert snac.snac_tuning_lookup(snac.SNAC_RULE_PIPELINE, 8, 2, MiB)["wgs_per_cu"] == 1
-    assert snac.snac_tuning_lookup(snac.SNAC_RULE_PIPELINE, 8, 2, 64 * MiB)["wgs_per_cu"] == 2
+    assert snac.snac_tuning_lookup(snac.SNAC_RULE_PIPELINE, 8, 2, 64 * MiB)["wgs_per_cu"] == 1
 
 
 def test_tuning_rules_first_match_and_override():
