@@ -743,13 +743,14 @@ snac_status snac_pipeline_scale_reduce(snac_ctx* ctx, const void* const* x, void
   a.ctrl = ctx->ctrl;
   a.abort_word = ctx->abort_dev;
   // Tile of this call, cut from the context's ring (slots * tile bytes per
-  // rank): about one producer item per workgroup, N * tiles ~ the grid.
-  // Bigger items mean fewer release and acquire fences, which serialise
-  // GPU-wide; fewer items than workgroups leave some idle.  On MI355X, one
-  // workgroup per CU: bf16 4096x8192 N=8 took 295 us with 32 tiles of 2 MiB,
-  // 309 with 64 of 1 MiB, 408 with 16 of 4 MiB; f32 604 us with 32 tiles of
-  // 4 MiB, 631 with 64 of 2 MiB.  Slots are merged only while the message
-  // still fits the ring in one pass, and split no finer than 64 KiB.
+  // rank): about one producer item per workgroup per pass over the ring,
+  // N * min(tiles, slots) ~ the grid.  Bigger items mean fewer release and
+  // acquire fences, which serialise GPU-wide; fewer items than workgroups
+  // leave some idle.  On MI355X, one workgroup per CU, bf16 4096x8192 N=8:
+  // 295 us with 32 tiles of 2 MiB, 309 with 64 of 1 MiB, 408 with 16 of
+  // 4 MiB (f32: 604 us with 32 tiles of 4 MiB, 631 with 64 of 2 MiB); in a
+  // 16 MiB ring, 336 us with 32 slots of 512 KiB, 399 with 64 of 256 KiB,
+  // 417 with 16 of 1 MiB.  Tiles are split no finer than 64 KiB.
   const uint64_t msg = count * (uint64_t)e;
   const LaunchCfg cfg = launch_cfg(SNAC_RULE_PIPELINE, n, e, msg);
   const snac_tuning tn = tuning_now();
@@ -759,8 +760,10 @@ snac_status snac_pipeline_scale_reduce(snac_ctx* ctx, const void* const* x, void
     const uint64_t grid = (uint64_t)(device_cu_count() > 0 ? device_cu_count() : 1) * (uint64_t)pipe_wgs_per_cu(cfg);
     const uint64_t target = (grid + (uint64_t)n - 1) / (uint64_t)n;
     auto tiles_of = [&](uint64_t t) { return (msg + t - 1) / t; };
-    while (msg <= ring && slots % 2 == 0 && slots / 2 >= 2 && (uint64_t)tile * 2 <= kMaxCallTile &&
-           tiles_of((uint64_t)tile * 2) >= target) {
+    // merge: a message that fits the ring keeps at least `target` tiles, one
+    // that does not keeps at least `target` slots (the tiles of one pass)
+    while (slots % 2 == 0 && slots / 2 >= 2 && (uint64_t)tile * 2 <= kMaxCallTile &&
+           (msg <= ring ? tiles_of((uint64_t)tile * 2) >= target : slots / 2 >= target)) {
       tile <<= 1;
       slots >>= 1;
     }
