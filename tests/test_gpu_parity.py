@@ -276,7 +276,8 @@ def test_pipeline(n, dtype):
         snac.snac_finalize(ctx)
 
 
-@pytest.mark.parametrize("tile,lookahead,wgs", [(4096, 1, 1), (16384, 3, 2), (65536, 0, 4), (262144, 7, 1)])
+@pytest.mark.parametrize("tile,lookahead,wgs", [(4096, 1, 1), (8192, 0, 1), (12288, 2, 1), (16384, 3, 2), (65536, 0, 4),
+                                                (262144, 7, 1)])
 def test_pipeline_tunings(tile, lookahead, wgs):
     n, dtype = 5, "bf16"
     t0 = snac.snac_get_tuning()
@@ -295,6 +296,33 @@ def test_pipeline_tunings(tile, lookahead, wgs):
             snac.snac_finalize(ctx)
     finally:
         snac.snac_set_tuning(**t0)
+
+
+KiB, MiB = 1 << 10, 1 << 20
+
+
+@pytest.mark.parametrize("n,ring,count,dtype", [
+    (8, 8 * MiB, (1 << 20) + 3, "bf16"),     # fits the ring: tiles split to 64 KiB, 33 tiles, compacted slots
+    (8, 4 * MiB, 5 * (1 << 20) + 3, "bf16"),  # 10 MiB through a 4 MiB ring: slots merged, several passes
+    (4, 64 * MiB, 47107, "bf16"),              # 5 units + 3 pieces + 6 bytes in a large ring
+    (16, 16 * MiB, (2 << 20) + 3, "bf16"),     # 16 ranks: 4 KiB units
+    (3, 2 * MiB, 1_000_003, "f32"),            # 4 MB through a 2 MiB ring
+    (2, 64 * MiB, 8 * (1 << 20) + 1, "f32"),   # N=2: 132 tiles of 256 KiB, one element past the last unit
+])
+def test_pipeline_layouts(n, ring, count, dtype):
+    """Default tiles across ring sizes, rank counts and short last units: the
+    call re-cuts the ring (merged or split slots, compacted when the message
+    fits) and tiles own interleaved units of the message."""
+    ctx = snac.snac_init(n, ring)
+    try:
+        xs = gen(n, count, dtype, seed=count % 1000 + n)
+        xb = [DevBuf(x.nbytes, data=x) for x in xs]
+        ob = DevBuf(xs[0].nbytes)
+        snac.snac_pipeline_scale_reduce(ctx, [b.ptr for b in xb], ob.ptr, count, dtype)
+        snac.snac_check(ctx)
+        run_and_check([ob], [oracle.pipeline_scale_reduce(xs, dtype)], dtype, f"pipeline N={n} ring={ring} count={count}")
+    finally:
+        snac.snac_finalize(ctx)
 
 
 def test_pipeline_alternating_inputs():
