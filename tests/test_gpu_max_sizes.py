@@ -1,10 +1,11 @@
 """Sizes past the 32-bit boundaries: a copy of more than 4 GiB, an AllReduce
-with more than 2^30 elements per rank and an AllToAll whose chunks are
-2 GiB.  Byte offsets, element indices and tile numbers must not wrap.
+with more than 2^30 elements per rank, an AllToAll whose chunks are 2 GiB
+and a SNAC pipeline call of 5 GiB per rank.  Byte offsets, element indices,
+tile and unit numbers must not wrap.
 
 The copy is compared whole on the GPU (a copy equals its source byte for
-byte, at any size).  The AllReduce is checked by the oracle's reduce_n on
-sampled positions, the AllToAll by its definition (chunk s of output d is
+byte, at any size).  The AllReduce and the pipeline are checked by the
+oracle on sampled positions (both are elementwise across ranks), the AllToAll by its definition (chunk s of output d is
 chunk d of input s) on sampled positions: the first and last 4096 elements
 of every output, positions around each 2^31 and 2^32 byte boundary, and
 2^16 random positions.  The inputs are drawn by torch on the GPU."""
@@ -122,4 +123,25 @@ def test_all_to_all_with_2_gib_chunks(torch):
             want[sel] = gather(torch, xs[s], src_idx).numpy().view(np.uint32)
         assert np.array_equal(got, want), f"AllToAll dst[{d}] with 2 GiB chunks"
     del xs, outs
+    torch.cuda.empty_cache()
+
+
+def test_pipeline_past_4_gib(torch):
+    n = 2
+    m = (1 << 31) + (1 << 29) + 7  # bf16 elements per rank: 5 GiB + 14 bytes
+    xs = [random_bf16(torch, m, seed=60 + r) for r in range(n)]
+    out = torch.empty_like(xs[0])
+    ctx = snac.snac_init(n, 0)
+    try:
+        snac.snac_pipeline_scale_reduce(ctx, xs, out, m, "bf16")
+        torch.cuda.synchronize()
+        snac.snac_check(ctx)
+    finally:
+        snac.snac_finalize(ctx)
+    idx = sample_idx(m, 2, seed=61)
+    ins = [gather(torch, x, idx).view(torch.int16).numpy().view(np.uint16) for x in xs]
+    want = oracle.pipeline_scale_reduce(ins, "bf16")
+    got = gather(torch, out, idx).view(torch.int16).numpy().view(np.uint16)
+    assert_same(got, want, "bf16", "pipeline past 4 GiB per rank")
+    del xs, out
     torch.cuda.empty_cache()
