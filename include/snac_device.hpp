@@ -113,17 +113,36 @@ __device__ __forceinline__ u32x4 ld16_a4(const char* p) {
     return *reinterpret_cast<const u32x4_a4*>(p);
 }
 
-// 16 bytes from any address.  m = p & 3 must be uniform across the wave.
-// m == 0: one dword-aligned dwordx4.  Otherwise the 20 bytes starting at the
-// dword below p are loaded (every dword touched holds at least one wanted
-// byte, so nothing outside the source range's dwords is read) and shifted
-// into place with v_alignbyte_b32.
 template <int CP>
-__device__ __forceinline__ u32x4 ld16_any(const char* p, uint32_t m) {
-  if (m == 0) return ld16_a4<CP>(p);
+__device__ __forceinline__ uint32_t ld4(const char* p) {
+  if constexpr (CP == kCacheStream || CP == kCacheStreamLoads)
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+  else
+    return *reinterpret_cast<const uint32_t*>(p);
+}
+
+// 16 bytes from any address p, in two steps, for m = p & 3 (uniform across
+// the wave) not 0: ld20 loads the 20 bytes starting at the dword below p
+// (every dword touched holds at least one wanted byte, so nothing outside
+// the source range's dwords is read), shift16 moves them into place with
+// v_alignbyte_b32.  Callers test m once per tile (m == 0: one dword-aligned
+// dwordx4 per unit, ld16_a4) and issue every unit's loads before the first
+// shift: with the test and the shift inside each unit's load, each unit
+// became its own block and the compiler waited for its loads before issuing
+// the next unit's, which made a 1 GiB copy from a source one byte off its
+// destination's alignment 2.3x slower on MI355X.  The extra dword takes the
+// same cache policy as the dwordx4: it is the next lane's first dword, and
+// a plain load behind a streaming one fetched those lines again.
+// (m == 0 is allowed: the extra dword is then the unit's own last one, so
+// nothing past the unit is read, and shift16 by 0 returns the dwordx4.)
+template <int CP>
+__device__ __forceinline__ void ld20(const char* p, uint32_t m, u32x4& a, uint32_t& e) {
   const char* b = p - m;
-  const u32x4 a = ld16_a4<CP>(b);
-  const uint32_t e = *reinterpret_cast<const uint32_t*>(b + 16);
+  a = ld16_a4<CP>(b);
+  e = ld4<CP>(b + (m ? 16u : 12u));
+}
+
+__device__ __forceinline__ u32x4 shift16(u32x4 a, uint32_t e, uint32_t m) {
   u32x4 r;
   r.x = __builtin_amdgcn_alignbyte(a.y, a.x, m);
   r.y = __builtin_amdgcn_alignbyte(a.z, a.y, m);
@@ -257,7 +276,8 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t x) {
 
 // dst[0..bytes) = src[0..bytes), bytewise, any alignment; the ranges must
 // not overlap.  The destination is stored in aligned 16-byte units after a
-// head of at most 15 bytes; the source is read with ld16_any.
+// head of at most 15 bytes; the source is read with ld16_a4, or ld20 and
+// shift16 when it is not dword-aligned there.
 template <int CP = kCacheStream>
 __device__ void copy(void* dst, const void* src, uint64_t bytes) {
   char* d = static_cast<char*>(dst);
@@ -273,10 +293,26 @@ __device__ void copy(void* dst, const void* src, uint64_t bytes) {
   const uint64_t step = (uint64_t)nt * 16u * U;
   for (uint64_t base = 0; base < body; base += step) {
     u32x4 v[U];
+    uint32_t e[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const uint64_t o = base + ((uint64_t)threadIdx.x + (uint64_t)u * nt) * 16u;
-      if (o < body) v[u] = ld16_any<CP>(sb + o, m);
+      v[u] = u32x4{0u, 0u, 0u, 0u};
+      e[u] = 0u;
+    }
+    if (m == 0) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint64_t o = base + ((uint64_t)threadIdx.x + (uint64_t)u * nt) * 16u;
+        if (o < body) v[u] = ld16_a4<CP>(sb + o);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint64_t o = base + ((uint64_t)threadIdx.x + (uint64_t)u * nt) * 16u;
+        if (o < body) ld20<CP>(sb + o, m, v[u], e[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = shift16(v[u], e[u], m);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -305,13 +341,31 @@ __device__ void reduce(void* const* dst, int ndst, const void* const* src, uint6
   if (head > bytes) head = bytes;
   const uint64_t body = (bytes - head) & ~(uint64_t)15;
   uint32_t m[N];
+  uint32_t any = 0;
 #pragma unroll
-  for (int k = 0; k < N; ++k) m[k] = (uint32_t)(((uintptr_t)src[k] + head) & 3u);
+  for (int k = 0; k < N; ++k) {
+    m[k] = (uint32_t)(((uintptr_t)src[k] + head) & 3u);
+    any |= m[k];
+  }
+  // one test per call, not per source and unit (see ld20): dword-aligned
+  // sources take one dwordx4 each; otherwise every source takes ld20, whose
+  // shift by m[k] = 0 leaves the dwordx4 as it is
   for (uint64_t o = (uint64_t)threadIdx.x * 16u; o < body; o += (uint64_t)nt * 16u) {
-    UnitAcc<T> acc;
-    acc.set(ld16_any<CP>(static_cast<const char*>(src[0]) + head + o, m[0]));
+    u32x4 v[N];
+    if (any == 0) {
 #pragma unroll
-    for (int k = 1; k < N; ++k) acc.add(ld16_any<CP>(static_cast<const char*>(src[k]) + head + o, m[k]));
+      for (int k = 0; k < N; ++k) v[k] = ld16_a4<CP>(static_cast<const char*>(src[k]) + head + o);
+    } else {
+      uint32_t e[N];
+#pragma unroll
+      for (int k = 0; k < N; ++k) ld20<CP>(static_cast<const char*>(src[k]) + head + o, m[k], v[k], e[k]);
+#pragma unroll
+      for (int k = 0; k < N; ++k) v[k] = shift16(v[k], e[k], m[k]);
+    }
+    UnitAcc<T> acc;
+    acc.set(v[0]);
+#pragma unroll
+    for (int k = 1; k < N; ++k) acc.add(v[k]);
     const u32x4 r = acc.out();
     for (int d = 0; d < ndst; ++d) st16<CP>(static_cast<char*>(dst[d]) + head + o, r);
   }
@@ -503,8 +557,8 @@ __device__ inline bool group_barrier(const snac_dev_ctx& c, uint32_t blocks) {
 //  * generic: any element-aligned address.  Each job is split into a head
 //    (bytes until the destination reaches a 128-byte line), a body of
 //    aligned 16-byte stores (buffer stores, as above) whose sources are read
-//    with ld16_any, and a tail; head and tail move one element per lane in
-//    tile 0 of the job.
+//    with ld16_a4, or ld20 and shift16 when not dword-aligned, and a tail;
+//    head and tail move one element per lane in tile 0 of the job.
 
 constexpr uint32_t kTileBytes = 16384;
 
@@ -744,8 +798,12 @@ __device__ void reduce_edges(const CollDesc& d, const JobL& J, uint32_t head, ui
 
 // Issue the U loads of source k of one tile.  FULL: the tile holds U whole
 // units per lane; otherwise units past the tile's body are left zero (and
-// are never stored).
-template <int TH, int U, int CP, bool ALIGNED, bool FULL>
+// are never stored).  SHIFT (generic jobs only): some source of the tile is
+// not dword-aligned, so every source is read with ld20 and shift16 (a
+// shift by 0 leaves a dword-aligned source as it is); without SHIFT each
+// unit is one dword-aligned dwordx4.  The caller picks SHIFT once per tile
+// and runs load, add and store under that one test (see ld20).
+template <int TH, int U, int CP, bool ALIGNED, bool FULL, bool SHIFT = false>
 __device__ __forceinline__ void reduce_load(const CollDesc& d, const TileRef& t, int k, u32x4 (&v)[U]) {
   const uint32_t lane = threadIdx.x * 16u;
   const char* sp = static_cast<const char*>(d.src[k]) + t.J.src_off + t.toff;
@@ -753,19 +811,43 @@ __device__ __forceinline__ void reduce_load(const CollDesc& d, const TileRef& t,
     const __amdgpu_buffer_rsrc_t r = buffer_rsrc(sp, t.rem);
 #pragma unroll
     for (int u = 0; u < U; ++u) v[u] = bld16<CP>(r, lane + (uint32_t)u * TH * 16u);
-    return;
-  }
-  const uint32_t m = uniform((uint32_t)(uintptr_t)sp & 3u);
+  } else if constexpr (!SHIFT) {
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const uint32_t o = lane + (uint32_t)u * TH * 16u;
-    if constexpr (FULL) {
-      v[u] = ld16_any<CP>(sp + o, m);
-    } else {
-      v[u] = u32x4{0u, 0u, 0u, 0u};
-      if (o < t.rem) v[u] = ld16_any<CP>(sp + o, m);
+    for (int u = 0; u < U; ++u) {
+      const uint32_t o = lane + (uint32_t)u * TH * 16u;
+      if constexpr (FULL) {
+        v[u] = ld16_a4<CP>(sp + o);
+      } else {
+        v[u] = u32x4{0u, 0u, 0u, 0u};
+        if (o < t.rem) v[u] = ld16_a4<CP>(sp + o);
+      }
     }
+  } else {
+    const uint32_t m = uniform((uint32_t)(uintptr_t)sp & 3u);
+    uint32_t e[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t o = lane + (uint32_t)u * TH * 16u;
+      if constexpr (FULL) {
+        ld20<CP>(sp + o, m, v[u], e[u]);
+      } else {
+        v[u] = u32x4{0u, 0u, 0u, 0u};
+        e[u] = 0u;
+        if (o < t.rem) ld20<CP>(sp + o, m, v[u], e[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = shift16(v[u], e[u], m);
   }
+}
+
+// Whether any source of a generic tile is not dword-aligned (uniform).
+template <int N>
+__device__ __forceinline__ bool tile_needs_shift(const CollDesc& d, const TileRef& t) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int k = 0; k < N; ++k) m |= (uint32_t)(uintptr_t)(static_cast<const char*>(d.src[k]) + t.J.src_off + t.toff);
+  return uniform(m & 3u) != 0;
 }
 
 // The reduced units of one tile, sources added in rank order.  Two register
@@ -773,22 +855,22 @@ __device__ __forceinline__ void reduce_load(const CollDesc& d, const TileRef& t,
 // into the other.  The source loop is deliberately not unrolled: unrolled,
 // the compiler issues every source's loads before the first add, which
 // measured about 5 % slower on MI355X than keeping two sources in flight.
-template <int N, typename T, int TH, int U, int CP, bool ALIGNED, bool FULL>
+template <int N, typename T, int TH, int U, int CP, bool ALIGNED, bool FULL, bool SHIFT = false>
 __device__ __forceinline__ void reduce_tile(const CollDesc& d, const TileRef& t, u32x4 (&r)[U]) {
   u32x4 a[U], b[U];
   UnitAcc<T> acc[U];
-  reduce_load<TH, U, CP, ALIGNED, FULL>(d, t, 0, a);
-  if constexpr (N > 1) reduce_load<TH, U, CP, ALIGNED, FULL>(d, t, 1, b);
+  reduce_load<TH, U, CP, ALIGNED, FULL, SHIFT>(d, t, 0, a);
+  if constexpr (N > 1) reduce_load<TH, U, CP, ALIGNED, FULL, SHIFT>(d, t, 1, b);
 #pragma unroll
   for (int u = 0; u < U; ++u) acc[u].set(a[u]);
   int k = 1;  // next source to add; it is in b
 #pragma unroll 1
   for (; k + 1 < N; k += 2) {
-    reduce_load<TH, U, CP, ALIGNED, FULL>(d, t, k + 1, a);
+    reduce_load<TH, U, CP, ALIGNED, FULL, SHIFT>(d, t, k + 1, a);
     __builtin_amdgcn_sched_barrier(0);  // issue these loads before waiting on b
 #pragma unroll
     for (int u = 0; u < U; ++u) acc[u].add(b[u]);
-    if (k + 2 < N) reduce_load<TH, U, CP, ALIGNED, FULL>(d, t, k + 2, b);
+    if (k + 2 < N) reduce_load<TH, U, CP, ALIGNED, FULL, SHIFT>(d, t, k + 2, b);
     __builtin_amdgcn_sched_barrier(0);  // ... and these before waiting on a
 #pragma unroll
     for (int u = 0; u < U; ++u) acc[u].add(a[u]);
@@ -804,11 +886,11 @@ __device__ __forceinline__ void reduce_tile(const CollDesc& d, const TileRef& t,
 // Small tiles (one unit per lane): every source's load is issued before
 // the first add, so a tile costs one memory round trip -- what matters when
 // a message has fewer tiles than the GPU has CUs.
-template <int N, typename T, int TH, int CP, bool ALIGNED, bool FULL>
+template <int N, typename T, int TH, int CP, bool ALIGNED, bool FULL, bool SHIFT = false>
 __device__ __forceinline__ void reduce_tile_allin(const CollDesc& d, const TileRef& t, u32x4 (&r)[1]) {
   u32x4 v[N][1];
 #pragma unroll
-  for (int k = 0; k < N; ++k) reduce_load<TH, 1, CP, ALIGNED, FULL>(d, t, k, v[k]);
+  for (int k = 0; k < N; ++k) reduce_load<TH, 1, CP, ALIGNED, FULL, SHIFT>(d, t, k, v[k]);
   UnitAcc<T> acc;
   acc.set(v[0][0]);
 #pragma unroll
@@ -831,7 +913,8 @@ __device__ inline void copy_edges(const CollDesc& d, const JobL& J, uint32_t hea
   }
 }
 
-template <int TH, int U, int CP, bool ALIGNED>
+// The U loads of one copy tile; FULL and SHIFT as for reduce_load.
+template <int TH, int U, int CP, bool ALIGNED, bool FULL = false, bool SHIFT = false>
 __device__ __forceinline__ void copy_load(const CollDesc& d, const TileRef& t, u32x4 (&v)[U]) {
   const char* sp = static_cast<const char*>(d.src[t.J.src_rank]) + t.J.src_off + t.toff;
   const uint32_t lane = threadIdx.x * 16u;
@@ -839,19 +922,54 @@ __device__ __forceinline__ void copy_load(const CollDesc& d, const TileRef& t, u
     const __amdgpu_buffer_rsrc_t r = buffer_rsrc(sp, t.rem);
 #pragma unroll
     for (int u = 0; u < U; ++u) v[u] = bld16<CP>(r, lane + (uint32_t)u * TH * 16u);
-    return;
-  }
-  const uint32_t m = uniform((uint32_t)(uintptr_t)sp & 3u);
-  if (t.rem == (uint32_t)TH * 16u * U) {  // full tile: no per-unit guards
+  } else if constexpr (!SHIFT) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = ld16_any<CP>(sp + lane + (uint32_t)u * TH * 16u, m);
-    return;
-  }
+    for (int u = 0; u < U; ++u) {
+      const uint32_t o = lane + (uint32_t)u * TH * 16u;
+      if constexpr (FULL) {
+        v[u] = ld16_a4<CP>(sp + o);
+      } else {
+        v[u] = u32x4{0u, 0u, 0u, 0u};
+        if (o < t.rem) v[u] = ld16_a4<CP>(sp + o);
+      }
+    }
+  } else {
+    const uint32_t m = uniform((uint32_t)(uintptr_t)sp & 3u);
+    uint32_t e[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const uint32_t o = lane + (uint32_t)u * TH * 16u;
-    if (o < t.rem) v[u] = ld16_any<CP>(sp + o, m);
+    for (int u = 0; u < U; ++u) {
+      const uint32_t o = lane + (uint32_t)u * TH * 16u;
+      if constexpr (FULL) {
+        ld20<CP>(sp + o, m, v[u], e[u]);
+      } else {
+        v[u] = u32x4{0u, 0u, 0u, 0u};
+        e[u] = 0u;
+        if (o < t.rem) ld20<CP>(sp + o, m, v[u], e[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = shift16(v[u], e[u], m);
   }
+}
+
+// One whole copy tile: loads (FULL, SHIFT as above) and stores under one
+// compile-time path, so that no loaded value crosses a branch.
+template <int TH, int U, int CP, bool ALIGNED, bool FULL, bool SHIFT>
+__device__ __forceinline__ void copy_tile(const CollDesc& d, const TileRef& t, uint32_t lane) {
+  u32x4 v[U];
+  copy_load<TH, U, CP, ALIGNED, FULL, SHIFT>(d, t, v);
+  store_units<TH, U, CP, 0, ALIGNED>(d, t.J.dst_rank, t.J.dst_off + t.toff, lane, t.rem, v);
+}
+
+// One whole reduce tile, likewise.
+template <int N, typename T, int TH, int U, int CP, bool ALIGNED, bool FULL, bool SHIFT>
+__device__ __forceinline__ void reduce_tile_store(const CollDesc& d, const TileRef& t, uint32_t lane) {
+  u32x4 r[U];
+  if constexpr (U == 1)
+    reduce_tile_allin<N, T, TH, CP, ALIGNED, FULL, SHIFT>(d, t, r);
+  else
+    reduce_tile<N, T, TH, U, CP, ALIGNED, FULL, SHIFT>(d, t, r);
+  store_units<TH, U, CP, N, ALIGNED>(d, t.J.dst_rank, t.J.dst_off + t.toff, lane, t.rem, r);
 }
 
 // ----------------------------------------------------------- tile loops
@@ -879,22 +997,24 @@ __device__ void run_reduce(const CollDesc& d, uint32_t block, uint32_t blocks) {
   jc.init(jobs, nj, tile);
   for (; tile < total; tile += blocks) {
     const TileRef t = jc.at(tile);
-    u32x4 r[U];
-    if constexpr (U == 1) {
-      if (ALIGNED || t.rem == TILE)
-        reduce_tile_allin<N, T, TH, CP, ALIGNED, true>(d, t, r);
-      else
-        reduce_tile_allin<N, T, TH, CP, ALIGNED, false>(d, t, r);
+    if constexpr (ALIGNED) {
+      reduce_tile_store<N, T, TH, U, CP, true, true, false>(d, t, lane);
     } else {
-      if (ALIGNED || t.rem == TILE)
-        reduce_tile<N, T, TH, U, CP, ALIGNED, true>(d, t, r);
-      else
-        reduce_tile<N, T, TH, U, CP, ALIGNED, false>(d, t, r);
-    }
-    if constexpr (!ALIGNED) {
       if (t.lt == 0) reduce_edges<T, N>(d, t.J, t.head, t.body);
+      const bool full = t.rem == TILE;
+      // one test per tile, around load, add and store (see ld20)
+      if (tile_needs_shift<N>(d, t)) {
+        if (full)
+          reduce_tile_store<N, T, TH, U, CP, false, true, true>(d, t, lane);
+        else
+          reduce_tile_store<N, T, TH, U, CP, false, false, true>(d, t, lane);
+      } else {
+        if (full)
+          reduce_tile_store<N, T, TH, U, CP, false, true, false>(d, t, lane);
+        else
+          reduce_tile_store<N, T, TH, U, CP, false, false, false>(d, t, lane);
+      }
     }
-    store_units<TH, U, CP, N, ALIGNED>(d, t.J.dst_rank, t.J.dst_off + t.toff, lane, t.rem, r);
   }
 }
 
@@ -912,12 +1032,26 @@ __device__ void run_copy(const CollDesc& d, uint32_t block, uint32_t blocks) {
   jc.init(jobs, nj, tile);
   for (; tile < total; tile += blocks) {
     const TileRef cur = jc.at(tile);
-    u32x4 v[U];
-    copy_load<TH, U, CP, ALIGNED>(d, cur, v);
-    if constexpr (!ALIGNED) {
+    if constexpr (ALIGNED) {
+      copy_tile<TH, U, CP, true, true, false>(d, cur, lane);
+    } else {
       if (cur.lt == 0) copy_edges(d, cur.J, cur.head, cur.body);
+      // one test per tile, around loads and stores (see ld20)
+      const char* sp = static_cast<const char*>(d.src[cur.J.src_rank]) + cur.J.src_off + cur.toff;
+      const bool shift = uniform((uint32_t)(uintptr_t)sp & 3u) != 0;
+      const bool full = cur.rem == (uint32_t)TH * 16u * U;
+      if (shift) {
+        if (full)
+          copy_tile<TH, U, CP, false, true, true>(d, cur, lane);
+        else
+          copy_tile<TH, U, CP, false, false, true>(d, cur, lane);
+      } else {
+        if (full)
+          copy_tile<TH, U, CP, false, true, false>(d, cur, lane);
+        else
+          copy_tile<TH, U, CP, false, false, false>(d, cur, lane);
+      }
     }
-    store_units<TH, U, CP, 0, ALIGNED>(d, cur.J.dst_rank, cur.J.dst_off + cur.toff, lane, cur.rem, v);
   }
 }
 
