@@ -10,6 +10,10 @@
 * No writes through the scalar data cache: no scalar memory stores or
   atomics and no scalar cache write-back or discard, in any kernel; data
   leaves the kernels through vector stores only.
+* A copy tile whose source is not dword-aligned issues all its loads
+  (dwordx4 and the extra dword of each unit) before waiting on any of
+  them.  With a branch inside each unit's load the compiler had waited for
+  every unit in turn, one load group in flight per wave.
 """
 from __future__ import annotations
 
@@ -106,3 +110,40 @@ SCALAR_WRITES = re.compile(r"^\s*(s_store_|s_buffer_store_|s_scratch_store_|s_at
 def test_no_scalar_cache_writes(asm, src):
     bad = SCALAR_WRITES.findall(asm[src])
     assert not bad, f"{src}: {sorted(set(bad))}"
+
+
+def _longest_unwaited_run(lines: list[str], op: str) -> int:
+    """Most `op` instructions issued in a row with no s_waitcnt on vector
+    memory between them."""
+    best = run = 0
+    for l in lines:
+        t = l.strip()
+        if t.startswith(op + " "):
+            run += 1
+            best = max(best, run)
+        elif t.startswith("s_waitcnt") and "vmcnt" in t:
+            run = 0
+    return best
+
+
+@pytest.mark.parametrize("shape", ["Li64ELj4096E", "Li256ELj16384E", "Li64ELj16384E"])
+def test_misaligned_copy_tile_issues_every_load_first(asm, shape):
+    # generic (not aligned) copy kernels of each tile shape, every cache policy
+    ks = {k: v for k, v in _kernels(asm["collectives.hip"]).items()
+          if k.startswith("_ZN4snac11copy_kernelI") and "Lb0E" in k and shape in k}
+    assert ks, shape
+    for name, lines in ks.items():
+        # the extra dwords of the units of one tile (4 per lane in these shapes)
+        assert _longest_unwaited_run(lines, "global_load_dword") >= 4, f"{name}: misaligned loads serialised"
+
+
+def test_misaligned_reduce_tile_issues_every_load_first(asm):
+    # generic reduce kernels: the 16 KiB-tile form keeps a source's 4 units
+    # per lane in flight, the small-tile form every source's unit
+    ks = {k: v for k, v in _kernels(asm["collectives.hip"]).items()
+          if k.startswith("_ZN4snac13reduce_kernelI") and re.search(r"Lb0ELb[01]E", k)}
+    assert len(ks) == 96
+    for name, lines in ks.items():
+        n = int(re.match(r"_ZN4snac13reduce_kernelILi(\d+)E", name).group(1))
+        want = n if "Lb0ELb1E" in name else 4
+        assert _longest_unwaited_run(lines, "global_load_dword") >= want, f"{name}: misaligned loads serialised"
