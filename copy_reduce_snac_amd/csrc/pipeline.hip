@@ -33,11 +33,11 @@
 //                     the L2, the workgroup meets at a barrier, and one lane
 //                     issues the agent-scope release fence (L2 write-back),
 //                     waits for it, and stores ready[r][slot] = seq.
-//   C(t, p)  Consume: one lane polls ready[r][slot] >= seq for every r
-//                     (relaxed loads with s_sleep back-off) and issues one
-//                     agent-scope acquire fence; barrier; N-to-1 reduce of
-//                     the staged units of part p into out; barrier; one lane
-//                     stores freed[slot][p] = seq.
+//   C(t, p)  Consume: the first wave polls ready[r][slot] >= seq, lane r
+//                     for rank r (relaxed loads with s_sleep back-off), and
+//                     issues one agent-scope acquire fence; barrier; N-to-1
+//                     reduce of the staged units of part p into out;
+//                     barrier; one lane stores freed[slot][p] = seq.
 //
 // One fence per item, not one per wave: agent-scope fences write back or
 // invalidate a whole L2 and serialise across the GPU (measured on MI355X at
@@ -127,11 +127,10 @@ __device__ void stage_item(const PipeArgs& a, uint32_t t, uint32_t gslot, uint32
                         uint32_t* s_ok) {
   constexpr uint32_t E = T::kSize;
   if (round > 0) {
-    if (threadIdx.x == 0) {
-      bool ok = true;
-      for (int p = 0; p < N && ok; ++p)
-        ok = wait_geq(&a.freed[((uint64_t)gslot * N + p) * kFlagStride], epoch + round, pipe_wait(a));
-      *s_ok = ok ? 1u : 0u;
+    if (threadIdx.x < 64) {  // the first wave, lane p polling part p's flag
+      const bool ok = wait_all_geq(&a.freed[(uint64_t)gslot * N * kFlagStride], N, kFlagStride, epoch + round,
+                                   pipe_wait(a));
+      if (threadIdx.x == 0) *s_ok = ok ? 1u : 0u;
     }
     __syncthreads();
     const uint32_t ok = uniform(*s_ok);
@@ -202,15 +201,14 @@ __device__ void consume_item(const PipeArgs& a, uint32_t t, uint32_t gslot, uint
   // Consume: one lane sees every rank's flag, then one acquire fence (an L2
   // and L1 invalidate shared by the whole workgroup's CU) before the barrier
   // releases the other waves to read the staged data.
-  if (threadIdx.x == 0) {
-    bool ok = true;
-    for (int r = 0; r < N && ok; ++r)
-      ok = wait_geq(&a.ready[((uint64_t)r * a.slots + gslot) * kFlagStride], seq, pipe_wait(a));
+  if (threadIdx.x < 64) {  // the first wave, lane r polling rank r's flag
+    const bool ok = wait_all_geq(&a.ready[(uint64_t)gslot * kFlagStride], N, (uint64_t)a.slots * kFlagStride, seq,
+                                 pipe_wait(a));
     if (ok) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       wait_vm();
     }
-    *s_ok = ok ? 1u : 0u;
+    if (threadIdx.x == 0) *s_ok = ok ? 1u : 0u;
   }
   __syncthreads();
   const uint32_t ok = uniform(*s_ok);

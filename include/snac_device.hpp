@@ -456,6 +456,40 @@ __device__ inline bool wait_geq(const uint64_t* flag, uint64_t target, const Wai
   return true;
 }
 
+// Wave-level wait: the calling wave (all 64 lanes active, and no other wave
+// of the workgroup in it) waits until flags[i * stride] >= target for every
+// i < n (n <= 64), lane i polling flag i, so a poll costs one memory round
+// trip however many flags there are.  One lane polling n flags in turn
+// paid n round trips (about 1 us each on MI355X) even when every flag was
+// already set.  Back-off, bounds and errors as in wait_geq; the result is
+// the same in every lane.
+__device__ inline bool wait_all_geq(const uint64_t* flags, int n, uint64_t stride, uint64_t target, const WaitCtl& w) {
+  const uint32_t lane = threadIdx.x & 63u;
+  const bool mine = (int)lane < n;
+  const uint64_t* f = flags + (uint64_t)(mine ? lane : 0u) * stride;
+  const uint64_t limit = 1ull << w.spin_limit_log2;
+  uint64_t spins = 0;
+  uint32_t naps = 1;
+  for (;;) {
+    const bool ok = !mine || ld_relaxed(f) >= target;
+    if (__builtin_amdgcn_ballot_w64(!ok) == 0) return true;
+    if ((spins & 15u) == 15u) {
+      if (uniform64(ld_relaxed(w.status)) != 0) return false;
+      uint32_t* ab = const_cast<uint32_t*>(w.abort_word);
+      if (ab && uniform(__hip_atomic_load(ab, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)) != 0) {
+        if (lane == 0) latch_status(w.status, kStatusAborted);
+        return false;
+      }
+    }
+    if (++spins >= limit) {
+      if (lane == 0) latch_status(w.status, kStatusTimeout);
+      return false;
+    }
+    for (uint32_t i = 0; i < naps; ++i) __builtin_amdgcn_s_sleep(1);
+    if (spins >= 16 && naps < 8) naps <<= 1;
+  }
+}
+
 // Notify (workgroup-level; every thread calls it): once every wave's stores
 // are accepted by the L2, one lane writes the L2 back at agent scope and
 // stores *flag = value.  After a consumer's acquire sees the value, every
@@ -470,19 +504,19 @@ __device__ inline void notify(uint64_t* flag, uint64_t value) {
   }
 }
 
-// Consume (workgroup-level): one lane waits for flags[i * stride] >= target
-// for i < n, then issues one acquire fence; the workgroup meets at a
-// barrier.  Returns false on timeout or abort (the same in every thread).
+// Consume (workgroup-level): the first wave waits for flags[i * stride] >=
+// target for i < n (n <= 64, one lane per flag), then issues one acquire
+// fence; the workgroup meets at a barrier.  Returns false on timeout or
+// abort (the same in every thread).
 __device__ inline bool consume(const uint64_t* flags, int n, uint64_t stride, uint64_t target, const WaitCtl& w) {
   __shared__ uint32_t s_ok;
-  if (threadIdx.x == 0) {
-    bool ok = true;
-    for (int i = 0; i < n && ok; ++i) ok = wait_geq(flags + (uint64_t)i * stride, target, w);
+  if (threadIdx.x < 64) {
+    const bool ok = wait_all_geq(flags, n, stride, target, w);
     if (ok) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       wait_vm();
     }
-    s_ok = ok ? 1u : 0u;
+    if (threadIdx.x == 0) s_ok = ok ? 1u : 0u;
   }
   __syncthreads();
   const uint32_t ok = uniform(s_ok);
