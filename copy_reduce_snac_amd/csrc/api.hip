@@ -265,8 +265,15 @@ void finish_plan(Plan& p) {
     p.tiles = count_tiles(kShapeSmall);
   } else if (p.tiles > 0) {
     uint64_t job_bytes = 0;
-    for (int j = 0; j < nj; ++j) job_bytes += make_job(p.d, j).bytes;
-    p.shape = large_shape(p.d, job_bytes);
+    bool byte_shift = false;  // a one-to-one copy reading across the dword grid
+    for (int j = 0; j < nj; ++j) {
+      const Job jb = make_job(p.d, j);
+      job_bytes += jb.bytes;
+      if (!aligned && jb.bytes && !coll_is_reduce(p.d.coll) && jb.src_rank >= 0 && jb.dst_rank >= 0 &&
+          (((uintptr_t)p.d.src[jb.src_rank] + jb.src_off) - ((uintptr_t)p.d.dst[jb.dst_rank] + jb.dst_off)) & 3u)
+        byte_shift = true;
+    }
+    p.shape = large_shape(p.d, job_bytes, byte_shift);
     if (p.shape != kShapeTile) p.tiles = count_tiles(p.shape);
   }
 }

@@ -51,7 +51,10 @@ __global__ __launch_bounds__(TH) void copy_kernel(const CollDesc d) {
 // 5.96-5.97 against 5.58-5.69, AllToAllV with misaligned Dirichlet counts
 // 5.74 against 5.61-5.63.  Below about 512 MiB moved the 16 KiB tiles are
 // faster (copy 64 MiB: 6.05 against 5.75; AllToAll 16 MiB per rank: 5.85
-// against 5.64).
+// against 5.64).  Copies whose source sits at a byte offset from the
+// destination's dword grid keep the 16 KiB tiles at every size: their full
+// tiles funnel through DPP lane shifts (funnel_next), which single-wave
+// 4 KiB tiles did not profit from.
 constexpr int kStreamThreads = 64;
 constexpr uint32_t kStreamTile = 4096;
 constexpr uint64_t kStreamCopyBytes = 1ull << 30;
@@ -129,8 +132,8 @@ uint32_t coll_tile_bytes(const CollDesc& d, int shape) {
   return shape == kShapeStream ? kStreamTile : kTileBytes;
 }
 
-int large_shape(const CollDesc& d, uint64_t job_bytes) {
-  if (coll_is_reduce(d.coll) || is_multicast_copy(d)) return kShapeTile;
+int large_shape(const CollDesc& d, uint64_t job_bytes, bool byte_shift) {
+  if (coll_is_reduce(d.coll) || is_multicast_copy(d) || byte_shift) return kShapeTile;
   return 2 * job_bytes >= kStreamCopyBytes ? kShapeStream : kShapeTile;
 }
 

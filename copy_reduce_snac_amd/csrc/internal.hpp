@@ -29,8 +29,10 @@ enum Shape : int { kShapeTile = 0, kShapeSmall = 1, kShapeStream = 2 };
 uint32_t coll_tile_bytes(const CollDesc& d, int shape);
 
 // The shape of a message that fills the GPU with 16 KiB tiles, given the
-// bytes its jobs copy or reduce (each job's bytes once).
-int large_shape(const CollDesc& d, uint64_t job_bytes);
+// bytes its jobs copy or reduce (each job's bytes once) and whether some
+// one-to-one copy job reads its source at a byte offset from its
+// destination's dword grid.
+int large_shape(const CollDesc& d, uint64_t job_bytes, bool byte_shift);
 
 // Launch the copy or reduce kernel for a collective descriptor.  `tiles` is
 // the total tile count of the layout at coll_tile_bytes(d, shape) (computed

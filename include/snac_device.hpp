@@ -142,6 +142,33 @@ __device__ __forceinline__ void ld20(const char* p, uint32_t m, u32x4& a, uint32
   e = ld4<CP>(b + (m ? 16u : 12u));
 }
 
+// Lane i gets lane i + 1's v (DPP whole-wave shift left, wave_shl:1); lane
+// 63, which has no next lane, keeps `old`.
+__device__ __forceinline__ uint32_t from_next_lane(uint32_t v, uint32_t old) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, 0x130, 0xf, 0xf, false);
+}
+
+// Byte-misaligned units whose lanes cover consecutive 16 bytes of a full
+// tile (every lane active): v[u] holds the aligned 16 bytes at c = p - m16
+// (m16 = 4 Q + s, s != 0), e[u] in lane 63 of each wave the 16 bytes at
+// c + 4 (Q + 1), which end at the last dword of the next 16 it needs (the
+// other lanes get those dwords from their next lane).  On return v[u] holds
+// the 16 bytes at p.
+template <int Q, int U>
+__device__ __forceinline__ void funnel_next(u32x4 (&v)[U], const u32x4 (&e)[U], uint32_t s) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    uint32_t n[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) n[i] = from_next_lane(v[u][i], i <= Q ? e[u][(i + 3 - Q) & 3] : 0u);
+    const uint32_t w[8] = {v[u].x, v[u].y, v[u].z, v[u].w, n[0], n[1], n[2], n[3]};
+    u32x4 r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r[k] = __builtin_amdgcn_alignbyte(w[Q + k + 1], w[Q + k], s);
+    v[u] = r;
+  }
+}
+
 __device__ __forceinline__ u32x4 shift16(u32x4 a, uint32_t e, uint32_t m) {
   u32x4 r;
   r.x = __builtin_amdgcn_alignbyte(a.y, a.x, m);
@@ -966,6 +993,27 @@ __device__ __forceinline__ void copy_load(const CollDesc& d, const TileRef& t, u
         v[u] = u32x4{0u, 0u, 0u, 0u};
         if (o < t.rem) v[u] = ld16_a4<CP>(sp + o);
       }
+    }
+  } else if constexpr (FULL && TH >= 256) {
+    // aligned loads; each lane takes the next lane's first words through a
+    // DPP shift, and lane 63 of each wave loads its own (see funnel_next)
+    const uint32_t m16 = uniform((uint32_t)(uintptr_t)sp & 15u);
+    const uint32_t q = m16 >> 2, s = m16 & 3u;
+    const char* c = sp - m16;
+    const bool last = (threadIdx.x & 63u) == 63u;
+    u32x4 e[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = ld16<CP>(c + lane + (uint32_t)u * TH * 16u);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      e[u] = u32x4{0u, 0u, 0u, 0u};
+      if (last) e[u] = ld16_a4<CP>(c + lane + (uint32_t)u * TH * 16u + 4u * (q + 1u));
+    }
+    switch (q) {
+      case 0: funnel_next<0, U>(v, e, s); break;
+      case 1: funnel_next<1, U>(v, e, s); break;
+      case 2: funnel_next<2, U>(v, e, s); break;
+      default: funnel_next<3, U>(v, e, s); break;
     }
   } else {
     const uint32_t m = uniform((uint32_t)(uintptr_t)sp & 3u);

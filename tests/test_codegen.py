@@ -14,6 +14,8 @@
   (dwordx4 and the extra dword of each unit) before waiting on any of
   them.  With a branch inside each unit's load the compiler had waited for
   every unit in turn, one load group in flight per wave.
+* Full byte-misaligned tiles of the 256-thread copy kernels take the next
+  lane's bytes through DPP whole-wave shifts (wave_shl:1).
 """
 from __future__ import annotations
 
@@ -147,3 +149,11 @@ def test_misaligned_reduce_tile_issues_every_load_first(asm):
         n = int(re.match(r"_ZN4snac13reduce_kernelILi(\d+)E", name).group(1))
         want = n if "Lb0ELb1E" in name else 4
         assert _longest_unwaited_run(lines, "global_load_dword") >= want, f"{name}: misaligned loads serialised"
+
+
+def test_misaligned_256_thread_copy_uses_dpp_shifts(asm):
+    ks = {k: v for k, v in _kernels(asm["collectives.hip"]).items()
+          if k.startswith("_ZN4snac11copy_kernelI") and "Lb0ELi256ELj16384E" in k}
+    assert ks
+    for name, lines in ks.items():
+        assert any("wave_shl:1" in l for l in lines), f"{name}: no DPP lane shift"
