@@ -485,12 +485,23 @@ __device__ inline bool wait_geq(const uint64_t* flag, uint64_t target, const Wai
 
 // Wave-level wait: the calling wave (all 64 lanes active, and no other wave
 // of the workgroup in it) waits until flags[i * stride] >= target for every
-// i < n (n <= 64), lane i polling flag i, so a poll costs one memory round
-// trip however many flags there are.  One lane polling n flags in turn
-// paid n round trips (about 1 us each on MI355X) even when every flag was
-// already set.  Back-off, bounds and errors as in wait_geq; the result is
-// the same in every lane.
+// i < n, lane i polling flag i (flags 64 and up in further groups of 64), so
+// a poll costs one memory round trip however many flags there are.  One
+// lane polling n flags in turn paid n round trips (about 1 us each on
+// MI355X) even when every flag was already set.  Back-off, bounds and
+// errors as in wait_geq; the result is the same in every lane.
+__device__ inline bool wait_group_geq(const uint64_t* flags, int n, uint64_t stride, uint64_t target,
+                                      const WaitCtl& w);
+
 __device__ inline bool wait_all_geq(const uint64_t* flags, int n, uint64_t stride, uint64_t target, const WaitCtl& w) {
+  for (int base = 0; base < n; base += 64)
+    if (!wait_group_geq(flags + (uint64_t)base * stride, n - base < 64 ? n - base : 64, stride, target, w)) return false;
+  return true;
+}
+
+// One group of at most 64 flags (wait_all_geq).
+__device__ inline bool wait_group_geq(const uint64_t* flags, int n, uint64_t stride, uint64_t target,
+                                      const WaitCtl& w) {
   const uint32_t lane = threadIdx.x & 63u;
   const bool mine = (int)lane < n;
   const uint64_t* f = flags + (uint64_t)(mine ? lane : 0u) * stride;
@@ -532,9 +543,9 @@ __device__ inline void notify(uint64_t* flag, uint64_t value) {
 }
 
 // Consume (workgroup-level): the first wave waits for flags[i * stride] >=
-// target for i < n (n <= 64, one lane per flag), then issues one acquire
-// fence; the workgroup meets at a barrier.  Returns false on timeout or
-// abort (the same in every thread).
+// target for i < n (one lane per flag, in groups of 64), then issues one
+// acquire fence; the workgroup meets at a barrier.  Returns false on
+// timeout or abort (the same in every thread).
 __device__ inline bool consume(const uint64_t* flags, int n, uint64_t stride, uint64_t target, const WaitCtl& w) {
   __shared__ uint32_t s_ok;
   if (threadIdx.x < 64) {

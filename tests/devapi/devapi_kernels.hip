@@ -130,6 +130,32 @@ __global__ __launch_bounds__(TH) void flags_kernel(const snac_dev_ctx ctx, snac_
   if (threadIdx.x == 0) ok_out[blockIdx.x] = ok ? 1u : 0u;
 }
 
+// ---- one consumer of many flags
+//
+// Workgroups k < K each store vals[k] = k + 1 and notify user flag k =
+// target; the last workgroup consumes all K flags at once (more than one
+// wave's worth when K > 64), then sums vals[] -- every value must be the
+// producer's, made visible by its release and the consumer's acquire.
+
+__global__ __launch_bounds__(TH) void many_flags_kernel(const snac_dev_ctx ctx, uint32_t* vals, int K, uint64_t target,
+                                                        uint64_t* sum_out, uint32_t* ok_out) {
+  const snac::WaitCtl w = snac::wait_ctl(ctx);
+  constexpr uint64_t F = SNAC_FLAG_STRIDE;
+  if ((int)blockIdx.x < K) {
+    if (threadIdx.x == 0) vals[blockIdx.x] = blockIdx.x + 1u;
+    snac::notify(ctx.flags + (uint64_t)blockIdx.x * F, target);
+    if (threadIdx.x == 0) ok_out[blockIdx.x] = 1u;
+    return;
+  }
+  const bool ok = snac::consume(ctx.flags, K, F, target, w);
+  if (threadIdx.x == 0) {
+    uint64_t sum = 0;
+    for (int k = 0; k < K; ++k) sum += vals[k];
+    *sum_out = sum;
+    ok_out[K] = ok ? 1u : 0u;
+  }
+}
+
 // N dispatch tables (N in {1, 2, 3, 4, 8, 16})
 #define SNAC_DISPATCH_N(MACRO) MACRO(1) MACRO(2) MACRO(3) MACRO(4) MACRO(8) MACRO(16)
 
@@ -267,6 +293,14 @@ int devtest_flags(const snac_dev_ctx* ctx, const snac_coll_desc* xs, float* stag
     return hipErrorInvalidValue;
   if (!fits((const void*)&flags_kernel, n + 1)) return -1;
   hipLaunchKernelGGL(flags_kernel, dim3(n + 1), dim3(TH), 0, s, *ctx, *xs, stage, out, n, S, R, B, base, ok_out);
+  return hipGetLastError();
+}
+
+int devtest_many_flags(const snac_dev_ctx* ctx, uint32_t* vals, int K, uint64_t target, uint64_t* sum_out,
+                       uint32_t* ok_out, hipStream_t s) {
+  if (!ctx || K < 1 || (uint64_t)K > ctx->nflags) return hipErrorInvalidValue;
+  if (!fits((const void*)&many_flags_kernel, K + 1)) return -1;
+  hipLaunchKernelGGL(many_flags_kernel, dim3(K + 1), dim3(TH), 0, s, *ctx, vals, K, target, sum_out, ok_out);
   return hipGetLastError();
 }
 

@@ -226,7 +226,7 @@ def test_binding_structs_match_c_layout(cls):
 def test_devtest_fixture_exports_its_launchers():
     lib = ctypes.CDLL(os.path.join(ROOT, "tests", "devapi", "libsnac_devtest.so"))
     for n in ("devtest_copy_slices", "devtest_reduce_slices", "devtest_collective", "devtest_collective_nosync",
-              "devtest_fused_scale_allreduce"):
+              "devtest_fused_scale_allreduce", "devtest_flags", "devtest_many_flags"):
         assert hasattr(lib, n)
 
 

@@ -37,6 +37,7 @@ def dev():
         "devtest_fused_scale_allreduce": [_DP, _CP, _DP, _U64, _VP, _I, _VP, _VP],
         "devtest_flags": [_CP, _DP, _VP, _VP, _I, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, _U64, _VP,
                           _VP],
+        "devtest_many_flags": [_CP, _VP, _I, _U64, _VP, _VP, _VP],
     }
     for name, args in sigs.items():
         f = getattr(lib, name)
@@ -324,5 +325,29 @@ def test_stage_notify_consume_by_hand(dev, n, S):
             assert int(ok.sum().item()) == n + 1
             assert_same(out.cpu().numpy().reshape(R, B), want, "f32", f"n={n} S={S} call {call}")
             base += R
+    finally:
+        snac.snac_finalize(ctx)
+
+
+@pytest.mark.parametrize("K", [1, 63, 64, 65, 130, 1000])
+def test_consume_many_flags(dev, K):
+    """One consumer waits on K flags at once: one lane per flag, in groups
+    of 64.  Each producer's value must be visible after the consume."""
+    import torch
+
+    ctx = snac.snac_init(2, 0)
+    try:
+        dctx = snac.snac_get_device_context(ctx)
+        vals = torch.zeros(K, dtype=torch.int32, device="cuda")
+        total = torch.zeros(1, dtype=torch.int64, device="cuda")
+        for call in range(2):  # flags are never reset: the target rises
+            vals.zero_()
+            ok = ok_buffer(K + 1)
+            launch(dev.devtest_many_flags(ctypes.byref(dctx), vals.data_ptr(), K, call + 1, total.data_ptr(),
+                                          ok.data_ptr(), None))
+            torch.cuda.synchronize()
+            snac.snac_check(ctx)
+            assert int(ok.sum().item()) == K + 1
+            assert int(total.item()) == K * (K + 1) // 2
     finally:
         snac.snac_finalize(ctx)
