@@ -569,9 +569,13 @@ __device__ inline bool consume(const uint64_t* flags, int n, uint64_t stride, ui
 // barrier at a time.  Returns false on timeout or abort.
 //
 // Words: barrier[0] counts arrivals, barrier[SNAC_FLAG_STRIDE] is the
-// generation.  A workgroup reads the generation before it arrives; the last
-// arrival resets the count and then advances the generation with a release
-// store, which the others wait for.
+// generation.  A workgroup reads the generation, releases its stores (one
+// fence) and counts itself in with a relaxed add.  The last arrival acquires
+// every other arrival's stores (their fences head the release sequence of
+// the count), resets the count and advances the generation with a release
+// store; the others wait for it and acquire.  So a workgroup pays two
+// agent-scope fences, which serialise GPU-wide, and the last one four; an
+// acquire-release add cost every workgroup two more.
 __device__ inline bool group_barrier(uint64_t* barrier, uint32_t blocks, const WaitCtl& w) {
   __shared__ uint32_t s_ok;
   wait_vm();
@@ -581,9 +585,10 @@ __device__ inline bool group_barrier(uint64_t* barrier, uint32_t blocks, const W
     uint64_t* gen = barrier + SNAC_FLAG_STRIDE;
     const uint64_t g = ld_relaxed(gen);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    const uint64_t old = __hip_atomic_fetch_add(count, (uint64_t)1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t old = __hip_atomic_fetch_add(count, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     bool ok = true;
     if (old + 1 == blocks) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       st_relaxed(count, 0);
       __hip_atomic_store(gen, g + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     } else {
@@ -1169,10 +1174,9 @@ __device__ void run_copy(const CollDesc& d, uint32_t block, uint32_t blocks) {
 // visible once the kernel has ended (to the next kernel on the stream), not
 // inside it.  It suits a kernel whose collective is its last step; the
 // workgroups need not be co-resident, and it returns false only on an
-// argument mismatch.  On MI355X the barrier costs about 33 us at the end of
-// a 256 MiB-per-rank bf16 N=8 AllReduce (0.785 against 0.752 ms): the
-// release fence of every workgroup about 24 us, the acquire fence and the
-// arrival counter the rest.
+// argument mismatch.  On MI355X the barrier costs about 24 us at the end of
+// a 256 MiB-per-rank bf16 N=8 AllReduce (0.779 against 0.755 ms), most of it
+// the release fence of every workgroup (see group_barrier).
 template <typename T = F32, int N = 1, int TH = 256, int CP = kCacheStream, bool SYNC = true>
 __device__ bool collective(const CollDesc& desc, const snac_dev_ctx& ctx, uint32_t block, uint32_t blocks,
                            uint32_t coll_blocks) {
