@@ -323,8 +323,12 @@ __global__ __launch_bounds__(kThreads) void pipeline_kernel(const PipeArgs a) {
   if (threadIdx.x == 0) {
     const uint64_t per_queue = gridDim.x / Q;  // the grid is a multiple of Q
     uint64_t* qdone = &a.ctrl[kCtrlQDone + q * kFlagStride];
-    const uint64_t oq = __hip_atomic_fetch_add(qdone, (uint64_t)1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    // a release add (one write-back per workgroup; acquire-release added an
+    // invalidate to every one of them, serialising GPU-wide), and one
+    // acquire in the last workgroup before it resets the queue's counters
+    const uint64_t oq = __hip_atomic_fetch_add(qdone, (uint64_t)1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     if (oq == per_queue - 1) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       __hip_atomic_store(ticket, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(qdone, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const uint64_t old =
