@@ -53,10 +53,11 @@
 // co-residency assumption about the grid is needed.
 //
 // Sequence numbers are monotonic across calls: seq = epoch + round + 1 with
-// round = g / S.  The last workgroup to finish (acq_rel counters, per queue
-// then global) adds the largest round count to the epoch and clears the
-// ticket and done counters, all in device memory, so consecutive launches (also inside a replayed
-// graph) need no host bookkeeping and no reset pass.
+// round = g / S.  The last workgroup to finish (release adds on per-queue
+// counters, then one global counter) adds the largest round count to the
+// epoch and clears the ticket and done counters, all in device memory, so
+// consecutive launches (also inside a replayed graph) need no host
+// bookkeeping and no reset pass.
 //
 // Waits are bounded: after 2^spin_limit_log2 polls a wait latches
 // SNAC_E_TIMEOUT in the status word and gives up; a host-mapped abort word
