@@ -176,12 +176,19 @@ static KernelFn small_kernel(const CollDesc& d, bool aligned) {
 // workgroup: four per CU for reduces and multicast copies (AllReduce
 // bf16 N=8 at 2 MiB per rank 10 % faster than at one per CU, AllGather at
 // 256 KiB per rank in 28 % faster than at two), two for other copies,
-// whose workgroups each rebuild a larger job table.
-static int default_wgs_per_cu(const CollDesc& d, int shape, bool aligned) {
+// whose workgroups each rebuild a larger job table.  One-to-one copies
+// with at most 8 tiles per CU (up to 32 MiB moved at 256 CUs) are latency
+// bound rather than stream bound, and four per CU finish them sooner:
+// AllToAll u32 N=8 at 1.5, 2 and 4 MiB per rank took 9.8, 11.8 and 18.0 us
+// against 13.0, 13.9 and 19.6 at two (single calls, inputs evicted), and
+// 7.1, 8.8 and 14.8 against 9.2, 11.2 and 16.2 us in graph replays; a
+// 16 MiB copy 4-6 % less.  From 6 MiB per rank up two per CU is faster.
+static int default_wgs_per_cu(const CollDesc& d, int shape, bool aligned, uint64_t tiles, int cus) {
   const bool reduce = coll_is_reduce(d.coll);
   if (shape == kShapeSmall) return reduce || is_multicast_copy(d) ? 4 : 2;
   if (shape == kShapeStream) return aligned ? 5 : 4;
-  return reduce && d.nsrc >= 3 ? 1 : 2;
+  if (reduce) return d.nsrc >= 3 ? 1 : 2;
+  return !is_multicast_copy(d) && tiles <= 8u * (uint64_t)(cus > 0 ? cus : 1) ? 4 : 2;
 }
 
 hipError_t launch_collective(const CollDesc& d, bool aligned, int shape, uint64_t tiles, const LaunchCfg& cfg,
@@ -209,9 +216,9 @@ hipError_t launch_collective(const CollDesc& d, bool aligned, int shape, uint64_
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), threads, 0);
   if (e != hipSuccess) return e;
   if (per_cu < 1) per_cu = 1;
-  const int want = cfg.wgs_per_cu > 0 ? cfg.wgs_per_cu : default_wgs_per_cu(d, shape, aligned);
-  if (want < per_cu) per_cu = want;
   const int cus = device_cu_count();
+  const int want = cfg.wgs_per_cu > 0 ? cfg.wgs_per_cu : default_wgs_per_cu(d, shape, aligned, tiles, cus);
+  if (want < per_cu) per_cu = want;
   uint64_t grid = (uint64_t)(cus > 0 ? cus : 1) * (uint64_t)per_cu;
   if (grid > tiles) grid = tiles;
   hipLaunchKernelGGL(fn, dim3((uint32_t)grid), dim3(threads), 0, stream, d);

@@ -414,6 +414,37 @@ def test_large_tiles_v_collectives(ctxs, dtype):
     run_and_check(db, want, dtype, f"AGV large {dtype}")
 
 
+# One-to-one copies of 16 KiB tiles launch four workgroups per CU up to 8
+# tiles per CU (2048 tiles on a 256-CU part: 32 MiB moved) and two beyond;
+# these sizes sit inside that range, at its edge and just past it.
+@pytest.mark.parametrize("per_rank", [1 << 20, 4 << 20, (4 << 20) + 2048])
+def test_mid_size_all_to_all_launch_range(ctxs, per_rank):
+    n = 8
+    srcs = gen(n, per_rank // 4, "u32", seed=per_rank % 89)
+    sb = [DevBuf(per_rank, offset=4 * (k % 2), data=s) for k, s in enumerate(srcs)]
+    db = [DevBuf(per_rank, offset=16 * (k % 3)) for k in range(n)]
+    snac.snac_all_to_all(ctxs(n), [b.ptr for b in sb], [b.ptr for b in db], per_rank, "u32")
+    run_and_check(db, oracle.all_to_all(srcs), "u32", f"A2A {per_rank} B/rank")
+
+
+def test_mid_size_v_and_copy_launch_range(ctxs):
+    n = 8
+    m = (1 << 20) // 4  # 1 MiB of u32 per rank: about 512 tiles in all
+    srcs = gen(n, m, "u32", seed=61)
+    c = wl.v_counts(n, m, n, cfg=wl.CFG_TEST, seed=61)
+    want = oracle.all_to_all_v(srcs, c)
+    sb = [DevBuf(s.nbytes, data=s) for s in srcs]
+    db = [DevBuf(np.asarray(w).nbytes, offset=4) for w in want]
+    snac.snac_all_to_all_v(ctxs(n), [b.ptr for b in sb], [b.ptr for b in db], c.reshape(-1).tolist(), "u32")
+    run_and_check(db, want, "u32", "A2AV 1 MiB/rank")
+    nbytes = (12 << 20) + 5
+    data = wl.raw_bytes(nbytes, wl.CFG_TEST, 0, seed=62)
+    s = DevBuf(nbytes, offset=3, data=data)
+    d = DevBuf(nbytes, offset=0)
+    snac.snac_copy(d.ptr, s.ptr, nbytes)
+    run_and_check([d], [oracle.copy(data)], "byte", "copy 12 MiB + 5 from a byte offset")
+
+
 @pytest.mark.parametrize("per_rank", [256 * 16384 - 16, 256 * 16384, 256 * 16384 + 16])
 def test_small_and_large_tiles_meet(ctxs, per_rank):
     """Sizes on both sides of the switch between the two tile sizes."""
