@@ -183,11 +183,15 @@ static KernelFn small_kernel(const CollDesc& d, bool aligned) {
 // against 13.0, 13.9 and 19.6 at two (single calls, inputs evicted), and
 // 7.1, 8.8 and 14.8 against 9.2, 11.2 and 16.2 us in graph replays; a
 // 16 MiB copy 4-6 % less.  From 6 MiB per rank up two per CU is faster.
+// Reduces of at most 2 tiles per CU (AllReduce and ReduceScatter of 4-8 MiB
+// per rank) likewise run two per CU, one tile each: bf16 N=8 AllReduce at
+// 6 and 8 MiB per rank 18.7 and 21.9 us against 20.1 and 23.3 in graph
+// replays, ReduceScatter at 5-8 MiB per rank 4-7 % less.
 static int default_wgs_per_cu(const CollDesc& d, int shape, bool aligned, uint64_t tiles, int cus) {
   const bool reduce = coll_is_reduce(d.coll);
   if (shape == kShapeSmall) return reduce || is_multicast_copy(d) ? 4 : 2;
   if (shape == kShapeStream) return aligned ? 5 : 4;
-  if (reduce) return d.nsrc >= 3 ? 1 : 2;
+  if (reduce) return d.nsrc >= 3 && tiles > 2u * (uint64_t)(cus > 0 ? cus : 1) ? 1 : 2;
   return !is_multicast_copy(d) && tiles <= 8u * (uint64_t)(cus > 0 ? cus : 1) ? 4 : 2;
 }
 

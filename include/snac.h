@@ -421,7 +421,8 @@ typedef struct snac_tuning {
   int32_t wgs_per_cu;      /* workgroups per compute unit in the persistent grid
                               (0: the kernel default -- for messages of at
                               least one 16 KiB tile per CU, 1 for reduces of
-                              >= 3 sources, 4 for one-to-one copies of at
+                              >= 3 sources and more than 2 tiles per CU,
+                              4 for one-to-one copies of at
                               most 8 tiles per CU, else 2; for one-to-one
                               copies moving >= 1 GiB, 5 single-wave workgroups (4
                               when a job is not 16-byte aligned); for smaller

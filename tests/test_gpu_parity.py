@@ -427,6 +427,21 @@ def test_mid_size_all_to_all_launch_range(ctxs, per_rank):
     run_and_check(db, oracle.all_to_all(srcs), "u32", f"A2A {per_rank} B/rank")
 
 
+# Reduces of at most 2 tiles per CU (4-8 MiB per rank on a 256-CU part)
+# launch two workgroups per CU, larger ones one.
+@pytest.mark.parametrize("per_rank", [(6 << 20) + 32, 8 << 20, (8 << 20) + 16384])
+def test_mid_size_reduce_launch_range(ctxs, per_rank):
+    n = 8
+    srcs = gen(n, per_rank // 2, "bf16", seed=per_rank % 83)
+    sb = [DevBuf(per_rank, data=s) for s in srcs]
+    db = [DevBuf(per_rank, offset=16 * (k % 2)) for k in range(n)]
+    snac.snac_all_reduce(ctxs(n), [b.ptr for b in sb], [b.ptr for b in db], per_rank, "bf16")
+    run_and_check(db, oracle.all_reduce(srcs, "bf16"), "bf16", f"AR {per_rank} B/rank")
+    rb = [DevBuf(per_rank // n) for _ in range(n)]
+    snac.snac_reduce_scatter(ctxs(n), [b.ptr for b in sb], [b.ptr for b in rb], per_rank, "bf16")
+    run_and_check(rb, oracle.reduce_scatter(srcs, "bf16"), "bf16", f"RS {per_rank} B/rank")
+
+
 def test_mid_size_v_and_copy_launch_range(ctxs):
     n = 8
     m = (1 << 20) // 4  # 1 MiB of u32 per rank: about 512 tiles in all
