@@ -347,7 +347,38 @@ def pin_pipeline_closed_form():
     assert bf16_value(int(out[0])) == 3.0
 
 
+def pin_copy():
+    """The copy Atom moves bytes, not values: every binary32 bit pattern
+    survives, signalling NaNs, payloads, infinities and -0 included; the
+    length and element type are kept; the result is a buffer of its own.
+    Checked against Python ``bytes`` built from the integer values, a path
+    that shares nothing with NumPy's array copy."""
+    pats = [0x7F800001, 0xFF800001, 0x7FBFFFFF, 0x7FC00000, 0xFFC00001, 0xFFFFFFFF, 0x7F800000, 0xFF800000,
+            0x80000000, 0x00000000, 0x00000001, 0x807FFFFF, 0x3F800000]
+    words = np.array(pats, dtype=np.uint32)
+    f = words.view(np.float32)
+    out = oc.copy(f)
+    assert out.dtype == np.float32 and out.shape == f.shape
+    assert out.tobytes() == b"".join(struct.pack("<I", p) for p in pats)
+    # bf16 NaN and infinity patterns as 16-bit words
+    h = np.array([0x7F81, 0xFF81, 0x7FC1, 0x7F80, 0xFF80, 0x8000, 0x0001], dtype=np.uint16)
+    assert oc.copy(h).tobytes() == b"".join(struct.pack("<H", int(p)) for p in h.tolist())
+    # raw random bytes of ragged lengths, 0 included
+    for n in (0, 1, 3, 15, 4099):
+        b = wl.raw_bytes(n, wl.CFG_TEST, 7)
+        o = oc.copy(b)
+        assert o.dtype == b.dtype and len(o) == n
+        assert o.tobytes() == bytes(int(v) for v in b.tolist())
+    # a separate buffer: writing the copy leaves the source alone
+    b = wl.raw_bytes(64, wl.CFG_TEST, 8)
+    keep = bytes(int(v) for v in b.tolist())
+    o = oc.copy(b)
+    o[:] ^= 0xFF
+    assert b.tobytes() == keep
+
+
 PINS = [
+    pin_copy,
     pin_worked_example,
     pin_closed_form_small_integers,
     pin_rank_order,
@@ -480,6 +511,23 @@ def _mut_pipeline_unrounded(xs, dtype):
     return oc._narrow(acc, dtype)
 
 
+def _mut_copy_through_f64(src):
+    # a value copy: widening quiets signalling NaNs
+    a = np.asarray(src)
+    if a.dtype == np.float32:
+        with np.errstate(invalid="ignore"):
+            return a.astype(np.float64).astype(np.float32)
+    return np.array(a, copy=True)
+
+
+def _mut_copy_short(src):
+    return np.array(src, copy=True)[:-1] if len(src) else np.array(src, copy=True)
+
+
+def _mut_copy_alias(src):
+    return src
+
+
 _orig = {
     "reduce_n": oc.reduce_n,
     "reduce_scatter": oc.reduce_scatter,
@@ -488,6 +536,9 @@ _orig = {
 }
 
 MUTATIONS = {
+    "copy through float64": (oc, "copy", _mut_copy_through_f64),
+    "copy drops last element": (oc, "copy", _mut_copy_short),
+    "copy aliases its source": (oc, "copy", _mut_copy_alias),
     "reduce drops last rank": (oc, "reduce_n", _mut_drop_last),
     "reduce in reverse order": (oc, "reduce_n", _mut_reverse),
     "reduce in pairwise order": (oc, "reduce_n", _mut_pairwise),
