@@ -7,6 +7,8 @@
 // copies that move at least 1 GiB single waves on 4 KiB tiles.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "internal.hpp"
 #include "snac_device.hpp"
 
@@ -137,18 +139,24 @@ int large_shape(const CollDesc& d, uint64_t job_bytes, bool byte_shift) {
   return 2 * job_bytes >= kStreamCopyBytes ? kShapeStream : kShapeTile;
 }
 
+// CU count of the current device, cached per device.  Several host threads
+// may launch at once (different contexts), so the cache is a table of
+// atomics: a thread that finds no entry queries the device and stores it;
+// two threads doing so at once store the same value.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
 int device_cu_count() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
-  static int cached_dev = -1;
-  static int cached_cus = 0;
-  if (dev != cached_dev) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cached_dev = dev;
-    cached_cus = cus;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int c = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
   }
-  return cached_cus;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < kMaxDevices) g_cu_count[dev].store(cus, std::memory_order_relaxed);
+  return cus;
 }
 
 // Small-tile kernels: streaming accesses (the cache policy does not matter
