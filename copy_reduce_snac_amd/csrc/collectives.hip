@@ -31,7 +31,8 @@ template <int N, typename T, int CP, bool ALIGNED, bool SMALL = false>
 __global__ __launch_bounds__(SMALL ? kSmallReduceThreads : kReduceThreads) void reduce_kernel(const CollDesc d) {
   constexpr int TH = SMALL ? kSmallReduceThreads : kReduceThreads;
   constexpr uint32_t TILE = SMALL ? TH * 16u : kTileBytes;
-  run_reduce<N, T, TH, CP, ALIGNED, TILE>(d, blockIdx.x, gridDim.x);
+  __shared__ __align__(16) char lds[engine_lds_bytes<TH, kMaxRanks>()];
+  run_reduce<N, T, TH, CP, ALIGNED, TILE>(d, blockIdx.x, gridDim.x, lds);
 }
 
 // Byte copy of the collective's jobs, the whole grid.  TH = 256 for
@@ -42,7 +43,8 @@ constexpr int kMulticastThreads = 64;
 
 template <int CP, bool ALIGNED, int TH, uint32_t TILE = kTileBytes>
 __global__ __launch_bounds__(TH) void copy_kernel(const CollDesc d) {
-  run_copy<TH, CP, ALIGNED, TILE>(d, blockIdx.x, gridDim.x);
+  __shared__ __align__(16) char lds[engine_lds_bytes<TH>()];
+  run_copy<TH, CP, ALIGNED, TILE>(d, blockIdx.x, gridDim.x, lds);
 }
 
 // One-to-one copies that move at least kStreamCopyBytes (read plus

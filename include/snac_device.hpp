@@ -13,13 +13,21 @@
 //                                              reduce of one slice
 //   snac::wait_geq / snac::notify              SNAC flag primitives (bounded
 //                                              acquire polls, release stores)
+//   snac::stage(staging, src, bytes)           copy a slice into a staging
+//                                              buffer with write-through
+//                                              stores (then notify())
 //   snac::group_barrier(ctx, blocks)           all `blocks` workgroups meet;
 //                                              stores before it are visible
 //                                              to every one of them after it
-//   snac::collective<T, N, TH>(desc, ctx, block, blocks, coll_blocks)
-//                                              any of the seven collectives
+//   snac::collective<T, N, TH>(args, ctx)      any of the seven collectives
 //                                              of a snac_coll_desc, run by
 //                                              the calling workgroups
+//                                              (snac_args: descriptor, LDS
+//                                              workspace, blocks,
+//                                              coll_blocks, block)
+//   snac::Atom<950>                            the launch contract: THREADS
+//                                              and the LDS bytes each call
+//                                              needs (PIPELINE_LDS_BYTES)
 //
 // The library's own collective kernels are thin wrappers over the same
 // tile engine (run_reduce / run_copy), so host and device calls move data
@@ -542,6 +550,64 @@ __device__ inline void notify(uint64_t* flag, uint64_t value) {
   }
 }
 
+// Stage (workgroup-level; every thread calls it): copy `bytes` from src (any
+// alignment) into a staging buffer for a consumer, as the producers of
+// snac_pipeline_scale_reduce do.  The 16-byte units of the staging side are
+// stored with sc0 sc1, writing through the L2, so that the release fence of
+// the notify() that follows finds little left to write back (on MI355X
+// write-through staging made the library's pipeline 10 % faster than
+// write-back stores); the source is read with streaming loads.  `staging`
+// should be 16-byte aligned: otherwise the slice is moved by copy(), which
+// is correct but leaves the write-back to the fence.  The last bytes % 16
+// bytes go one per lane.  Nothing is visible to other workgroups until
+// notify().
+template <int LCP = kCacheStreamLoads>
+__device__ void stage(void* staging, const void* src, uint64_t bytes) {
+  char* d = static_cast<char*>(staging);
+  const char* s = static_cast<const char*>(src);
+  if ((uintptr_t)d & 15u) {
+    copy<kCacheStream>(staging, src, bytes);
+    return;
+  }
+  const uint32_t nt = blockDim.x;
+  const uint64_t body = bytes & ~(uint64_t)15;
+  const uint32_t m = uniform((uint32_t)((uintptr_t)s & 3u));
+  constexpr int U = 4;
+  const uint64_t step = (uint64_t)nt * 16u * U;
+  for (uint64_t base = 0; base < body; base += step) {
+    const uint64_t left = body - base;
+    const uint32_t rem = left < step ? (uint32_t)left : (uint32_t)step;
+    u32x4 v[U];
+    uint32_t e[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      v[u] = u32x4{0u, 0u, 0u, 0u};
+      e[u] = 0u;
+    }
+    // one test per call (see ld20): the whole body under one load form
+    if (m == 0) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t o = (threadIdx.x + (uint32_t)u * nt) * 16u;
+        if (o < rem) v[u] = ld16_a4<LCP>(s + base + o);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t o = (threadIdx.x + (uint32_t)u * nt) * 16u;
+        if (o < rem) ld20<LCP>(s + base + o, m, v[u], e[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = shift16(v[u], e[u], m);
+    }
+    // units at or past rem fall outside the resource: the hardware drops them
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(d + base, rem);
+#pragma unroll
+    for (int u = 0; u < U; ++u) bst16<kWriteThrough>(r, (threadIdx.x + (uint32_t)u * nt) * 16u, v[u]);
+  }
+  for (uint64_t i = threadIdx.x; i < bytes - body; i += nt) d[body + i] = s[body + i];
+}
+
 // Consume (workgroup-level): the first wave waits for flags[i * stride] >=
 // target for i < n (one lane per flag, in groups of 64), then issues one
 // acquire fence; the workgroup meets at a barrier.  Returns false on
@@ -576,8 +642,10 @@ __device__ inline bool consume(const uint64_t* flags, int n, uint64_t stride, ui
 // store; the others wait for it and acquire.  So a workgroup pays two
 // agent-scope fences, which serialise GPU-wide, and the last one four; an
 // acquire-release add cost every workgroup two more.
-__device__ inline bool group_barrier(uint64_t* barrier, uint32_t blocks, const WaitCtl& w) {
-  __shared__ uint32_t s_ok;
+// `s_ok` is one LDS word of the workgroup that carries the verdict to
+// every wave; the overloads without it keep that word in static LDS.
+__device__ inline bool group_barrier(uint64_t* barrier, uint32_t blocks, const WaitCtl& w, uint32_t* s_ok_word) {
+  uint32_t& s_ok = *s_ok_word;
   wait_vm();
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -603,8 +671,17 @@ __device__ inline bool group_barrier(uint64_t* barrier, uint32_t blocks, const W
   return ok != 0;
 }
 
+__device__ inline bool group_barrier(uint64_t* barrier, uint32_t blocks, const WaitCtl& w) {
+  __shared__ uint32_t s_ok;
+  return group_barrier(barrier, blocks, w, &s_ok);
+}
+
 __device__ inline bool group_barrier(const snac_dev_ctx& c, uint32_t blocks) {
   return group_barrier(c.barrier, blocks, wait_ctl(c));
+}
+
+__device__ inline bool group_barrier(const snac_dev_ctx& c, uint32_t blocks, uint32_t* s_ok_word) {
+  return group_barrier(c.barrier, blocks, wait_ctl(c), s_ok_word);
 }
 
 // ======================================================== the tile engine
@@ -655,6 +732,27 @@ struct JobL {
   uint32_t head;
   uint32_t tile0;
   uint32_t lead;  // body bytes before the destination's tile grid (job_lead)
+};
+
+// LDS the tile engine needs in a workgroup of TH threads: the job table
+// (MAXJ entries), the tile-count scan (one word per thread) and one word for
+// the verdict of collective()'s closing barrier, rounded up to 128 bytes.
+// The engine keeps nothing else in LDS.
+template <int TH, int MAXJ = kMaxJobs>
+constexpr uint32_t engine_lds_bytes() {
+  return ((uint32_t)(MAXJ * sizeof(JobL) + (uint32_t)TH * 4u + 16u) + 127u) & ~127u;
+}
+
+// Where the engine's words sit in its workspace.
+template <int TH, int MAXJ>
+struct EngineLds {
+  JobL* jobs;
+  uint32_t* scan;
+  uint32_t* verdict;
+  __device__ __forceinline__ explicit EngineLds(void* lds)
+      : jobs(static_cast<JobL*>(lds)),
+        scan(reinterpret_cast<uint32_t*>(static_cast<char*>(lds) + MAXJ * sizeof(JobL))),
+        verdict(reinterpret_cast<uint32_t*>(static_cast<char*>(lds) + MAXJ * sizeof(JobL) + (uint32_t)TH * 4u)) {}
 };
 
 // Build the job table and its tile numbering in LDS.  Returns the total
@@ -1078,16 +1176,20 @@ __device__ __forceinline__ void reduce_tile_store(const CollDesc& d, const TileR
 // TILE = TH * 16 gives the small-tile form for messages too small to fill
 // the GPU.
 // Every thread of the workgroup calls them; they return once the share is
-// stored (not yet visible to other workgroups: see group_barrier).
+// stored (not yet visible to other workgroups: see group_barrier).  `lds`
+// is the workgroup's workspace for the job table and scan: at least
+// engine_lds_bytes<TH, kMaxRanks>() bytes for run_reduce and
+// engine_lds_bytes<TH>() for run_copy, 16-byte aligned; the engine declares
+// no LDS of its own.
 
 template <int N, typename T, int TH, int CP, bool ALIGNED, uint32_t TILE = kTileBytes>
-__device__ void run_reduce(const CollDesc& d, uint32_t block, uint32_t blocks) {
+__device__ void run_reduce(const CollDesc& d, uint32_t block, uint32_t blocks, void* lds) {
   constexpr int U = tile_units<TH, TILE>();
   // edge elements (head < 128 bytes, tail < 16) and jobs are looped over
-  __shared__ JobL jobs[kMaxRanks];
-  __shared__ uint32_t scan[TH];
+  const EngineLds<TH, kMaxRanks> w(lds);
+  JobL* const jobs = w.jobs;
   int nj;
-  const uint32_t total = build_table<TH, kMaxRanks, ALIGNED>(d, TILE, jobs, scan, nj);
+  const uint32_t total = build_table<TH, kMaxRanks, ALIGNED>(d, TILE, jobs, w.scan, nj);
   uint32_t tile = block;
   if (tile >= total) return;
   const uint32_t lane = threadIdx.x * 16u;
@@ -1117,12 +1219,12 @@ __device__ void run_reduce(const CollDesc& d, uint32_t block, uint32_t blocks) {
 }
 
 template <int TH, int CP, bool ALIGNED, uint32_t TILE = kTileBytes>
-__device__ void run_copy(const CollDesc& d, uint32_t block, uint32_t blocks) {
+__device__ void run_copy(const CollDesc& d, uint32_t block, uint32_t blocks, void* lds) {
   constexpr int U = tile_units<TH, TILE>();
-  __shared__ JobL jobs[kMaxJobs];
-  __shared__ uint32_t scan[TH];
+  const EngineLds<TH, kMaxJobs> w(lds);
+  JobL* const jobs = w.jobs;
   int nj;
-  const uint32_t total = build_table<TH, kMaxJobs, ALIGNED>(d, TILE, jobs, scan, nj);
+  const uint32_t total = build_table<TH, kMaxJobs, ALIGNED>(d, TILE, jobs, w.scan, nj);
   uint32_t tile = block;
   if (tile >= total) return;
   const uint32_t lane = threadIdx.x * 16u;
@@ -1155,19 +1257,41 @@ __device__ void run_copy(const CollDesc& d, uint32_t block, uint32_t blocks) {
 
 // ================================================ device-side collectives
 
-// Run the collective of `desc` (from snac_describe) inside the caller's
-// kernel.  Exactly `blocks` workgroups of TH threads call it, each with its
-// own `block` in [0, blocks); workgroups block < coll_blocks move the data
-// (tiles shared round-robin), the others only wait for it.  When it returns
-// true in a workgroup, the whole collective's output is stored and visible
-// to that workgroup.  It returns false (in every participant) on timeout or
-// abort, with the status word latched for snac_check().
+}  // namespace snac
+
+// Arguments of a device-side collective call, one per workgroup (Purlin
+// 0.6.5 "Samples": the kernel fills them in and passes them with the
+// host-created context).  The pages' per-rank dst, src and bytes describe
+// the calling rank's buffers in symmetric memory; with N logical ranks in
+// one GPU every rank's buffers, byte count and V counts travel together in
+// the descriptor that snac_describe() validated on the host, so `desc`
+// stands for them here.
+struct snac_args {
+  const snac_coll_desc* desc;  // the collective (snac_describe); usually the address of a kernel argument
+  void* workspace;             // this workgroup's LDS: at least snac::Atom<950>::PIPELINE_LDS_BYTES bytes
+                               // (for TH = THREADS; Atom<950>::collective_lds_bytes<TH>() otherwise),
+                               // 16-byte aligned -- the dynamic shared memory of the launch
+  uint32_t blocks;             // workgroups that enter the call: exactly this many must
+  uint32_t coll_blocks;        // the first coll_blocks of them (0 < coll_blocks <= blocks) move data
+  uint32_t block;              // this workgroup's index in [0, blocks)
+};
+
+namespace snac {
+
+// Run the collective of a.desc inside the caller's kernel.  Exactly
+// a.blocks workgroups of TH threads call it, each with its own a.block;
+// workgroups a.block < a.coll_blocks move the data (tiles shared
+// round-robin), the others only wait for it.  All LDS it uses is
+// a.workspace.  When it returns true in a workgroup, the whole collective's
+// output is stored and visible to that workgroup.  It returns false (in
+// every participant) on timeout or abort, with the status word latched for
+// snac_check().
 //
-// T and N must match desc.esize and desc.nsrc for reduce collectives
+// T and N must match desc->esize and desc->nsrc for reduce collectives
 // (AllReduce, ReduceScatter, ReduceScatterV); copy collectives ignore them.
-// On a mismatch nothing is moved and SNAC_E_ARG latches.  The `blocks`
-// workgroups must be co-resident; the context's barrier serves one group at
-// a time.
+// On a mismatch, a NULL desc or workspace, or a misaligned workspace,
+// nothing is moved and SNAC_E_ARG latches.  The a.blocks workgroups must be
+// co-resident; the context's barrier serves one group at a time.
 //
 // SYNC = false leaves out that closing grid barrier: the call returns as
 // soon as this workgroup's share is stored, and the output is complete and
@@ -1178,34 +1302,87 @@ __device__ void run_copy(const CollDesc& d, uint32_t block, uint32_t blocks) {
 // a 256 MiB-per-rank bf16 N=8 AllReduce (0.779 against 0.755 ms), most of it
 // the release fence of every workgroup (see group_barrier).
 template <typename T = F32, int N = 1, int TH = 256, int CP = kCacheStream, bool SYNC = true>
-__device__ bool collective(const CollDesc& desc, const snac_dev_ctx& ctx, uint32_t block, uint32_t blocks,
-                           uint32_t coll_blocks) {
-  const bool reduce = coll_is_reduce(desc.coll);
-  const bool aligned = desc_aligned(desc);
-  bool good = true;
-  if (reduce && (desc.nsrc != N || desc.esize != T::kSize)) good = false;
-  if (coll_blocks == 0 || coll_blocks > blocks) good = false;
+__device__ bool collective(const snac_args& a, const snac_dev_ctx& ctx) {
+  bool good = a.desc != nullptr && a.workspace != nullptr && ((uintptr_t)a.workspace & 15u) == 0;
+  if (a.coll_blocks == 0 || a.coll_blocks > a.blocks) good = false;
+  bool reduce = false;
+  if (good) {
+    const CollDesc& desc = *a.desc;
+    reduce = coll_is_reduce(desc.coll);
+    if (reduce && (desc.nsrc != N || desc.esize != T::kSize)) good = false;
+  }
   if (!good) {
-    if (block == 0 && threadIdx.x == 0) latch_status(ctx.status, SNAC_E_ARG);
-  } else if (block < coll_blocks) {
+    if (a.block == 0 && threadIdx.x == 0) latch_status(ctx.status, SNAC_E_ARG);
+  } else if (a.block < a.coll_blocks) {
+    const CollDesc& desc = *a.desc;
+    const bool aligned = desc_aligned(desc);
     if (reduce) {
       if (aligned)
-        run_reduce<N, T, TH, CP, true>(desc, block, coll_blocks);
+        run_reduce<N, T, TH, CP, true>(desc, a.block, a.coll_blocks, a.workspace);
       else
-        run_reduce<N, T, TH, CP, false>(desc, block, coll_blocks);
+        run_reduce<N, T, TH, CP, false>(desc, a.block, a.coll_blocks, a.workspace);
     } else {
       if (aligned)
-        run_copy<TH, CP, true>(desc, block, coll_blocks);
+        run_copy<TH, CP, true>(desc, a.block, a.coll_blocks, a.workspace);
       else
-        run_copy<TH, CP, false>(desc, block, coll_blocks);
+        run_copy<TH, CP, false>(desc, a.block, a.coll_blocks, a.workspace);
     }
   }
   if constexpr (!SYNC) {
     return good;
   } else {
-    const bool met = group_barrier(ctx, blocks);
+    // without a workspace there is no LDS word to meet in: return at once
+    // (the error is latched; a group that all passes the same arguments
+    // returns together)
+    if (a.blocks == 0 || a.workspace == nullptr || ((uintptr_t)a.workspace & 15u)) return false;
+    // the verdict word lies past the job table and scan
+    const bool met = group_barrier(ctx.barrier, a.blocks, wait_ctl(ctx), EngineLds<TH, kMaxJobs>(a.workspace).verdict);
     return good && met;
   }
 }
+
+// The Atoms of one target and their launch contract (Purlin 0.6.5
+// "Samples": a kernel using an Atom launches with its THREADS threads per
+// block and the dynamic shared memory it names; Purlin 0.6.4 "Atom
+// implementations": one Atom set per architecture).  This build has one
+// target, gfx950 (MI355X), so Atom<950> is the only one.
+template <int ARCH>
+struct Atom;
+
+template <>
+struct Atom<950> {
+  // workgroup size the collectives are tuned for (a wave on each of a CU's
+  // four SIMDs); copy() and reduce() take any multiple of 64 up to 1024
+  static constexpr int THREADS = 256;
+  // copy() and reduce() keep their pipeline in registers (four 16-byte
+  // units per lane in flight): they need no LDS, and ignore `workspace`
+  static constexpr uint32_t COPY_LDS_BYTES = 0;
+  static constexpr uint32_t REDUCE_LDS_BYTES = 0;
+  // LDS a collective() call needs in a workgroup of TH threads
+  template <int TH = THREADS>
+  static constexpr uint32_t collective_lds_bytes() {
+    return engine_lds_bytes<TH>();
+  }
+  static constexpr uint32_t COLLECTIVE_LDS_BYTES = engine_lds_bytes<THREADS>();
+  // the dynamic LDS a kernel of THREADS threads that calls any of them
+  // must be launched with (the largest of the three)
+  static constexpr uint32_t PIPELINE_LDS_BYTES = COLLECTIVE_LDS_BYTES;
+
+  template <int CP = kCacheStream>
+  __device__ static void copy(void* dst, const void* src, uint64_t bytes, void* workspace = nullptr) {
+    (void)workspace;
+    snac::copy<CP>(dst, src, bytes);
+  }
+  template <typename T, int N, int CP = kCacheStream>
+  __device__ static void reduce(void* const* dst, int ndst, const void* const* src, uint64_t count,
+                                void* workspace = nullptr) {
+    (void)workspace;
+    snac::reduce<T, N, CP>(dst, ndst, src, count);
+  }
+};
+
+static_assert(Atom<950>::PIPELINE_LDS_BYTES >= kMaxJobs * sizeof(JobL) + 256 * 4 + 4,
+              "the collective workspace holds the job table, the scan and the barrier word");
+static_assert(Atom<950>::PIPELINE_LDS_BYTES <= 64 * 1024, "fits the LDS one workgroup may allocate");
 
 }  // namespace snac

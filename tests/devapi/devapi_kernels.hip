@@ -12,13 +12,17 @@
 
 namespace {
 
-constexpr int TH = 256;
+using Atom = snac::Atom<950>;
+constexpr int TH = Atom::THREADS;
+// dynamic LDS of every kernel here that calls a collective: the workspace
+// the launch contract names
+constexpr uint32_t LDS = Atom::PIPELINE_LDS_BYTES;
 
-int fits(const void* fn, int grid) {
+int fits(const void* fn, int grid, uint32_t lds = LDS) {
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, TH, 0) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, TH, lds) != hipSuccess) return 0;
   return grid <= per_cu * cus;
 }
 
@@ -43,11 +47,16 @@ __global__ __launch_bounds__(TH) void reduce_slices_kernel(snac_coll_desc bufs, 
 
 // ---- a described collective run by workgroups [0, blocks) of a larger grid
 
+// The workspace is the launch's dynamic LDS, as in the pages' sample; with
+// no_workspace the call gets a NULL workspace and must latch SNAC_E_ARG.
 template <typename T, int N, bool SYNC = true>
 __global__ __launch_bounds__(TH) void collective_kernel(const snac_coll_desc desc, const snac_dev_ctx ctx,
-                                                        uint32_t blocks, uint32_t coll_blocks, uint32_t* ok_out) {
+                                                        uint32_t blocks, uint32_t coll_blocks, int no_workspace,
+                                                        uint32_t* ok_out) {
+  extern __shared__ __align__(128) char workspace[];
   if (blockIdx.x >= blocks) return;  // workgroups doing "other work"
-  const bool ok = snac::collective<T, N, TH, snac::kCacheStream, SYNC>(desc, ctx, blockIdx.x, blocks, coll_blocks);
+  const snac_args args{&desc, no_workspace ? nullptr : workspace, blocks, coll_blocks, blockIdx.x};
+  const bool ok = snac::collective<T, N, TH, snac::kCacheStream, SYNC>(args, ctx);
   if (threadIdx.x == 0) ok_out[blockIdx.x] = ok ? 1u : 0u;
 }
 
@@ -69,6 +78,7 @@ template <typename T, int N>
 __global__ __launch_bounds__(TH) void fused_kernel(const snac_coll_desc desc, const snac_dev_ctx ctx,
                                                    snac_coll_desc xs, uint64_t count, char* check,
                                                    uint32_t* ok_out) {
+  extern __shared__ __align__(128) char workspace[];
   const uint32_t blocks = gridDim.x;
   const uint64_t per = (count + blocks - 1) / blocks;
   const uint64_t first = (uint64_t)blockIdx.x * per;
@@ -76,8 +86,11 @@ __global__ __launch_bounds__(TH) void fused_kernel(const snac_coll_desc desc, co
   for (int r = 0; r < N; ++r)
     scale_slice<T>(static_cast<const char*>(xs.src[r]), static_cast<char*>(const_cast<void*>(desc.src[r])), first, n,
                    (float)r);
-  bool ok = snac::group_barrier(ctx, blocks);
-  if (ok) ok = snac::collective<T, N, TH>(desc, ctx, blockIdx.x, blocks, blocks);
+  // the workspace is free until the collective: its first word carries the
+  // barrier's verdict, so the kernel declares no LDS of its own
+  bool ok = snac::group_barrier(ctx, blocks, reinterpret_cast<uint32_t*>(workspace));
+  const snac_args args{&desc, workspace, blocks, blocks, blockIdx.x};
+  if (ok) ok = snac::collective<T, N, TH>(args, ctx);
   if (ok) {
     // read another workgroup's part of the result: slice (b + 1) mod blocks
     const uint32_t other = (blockIdx.x + 1) % blocks;
@@ -111,7 +124,7 @@ __global__ __launch_bounds__(TH) void flags_kernel(const snac_dev_ctx ctx, snac_
       if (!ok) break;
       float* dst = stage + ((uint64_t)p * S + slot) * B;
       const float* src = static_cast<const float*>(xs.src[p]) + (uint64_t)r * B;
-      for (uint32_t i = threadIdx.x; i < B; i += TH) dst[i] = src[i];
+      snac::stage(dst, src, (uint64_t)B * sizeof(float));
       snac::notify(ctx.flags + ((uint64_t)p * S + slot) * F, base + r + 1);
     }
   } else {
@@ -196,7 +209,7 @@ int devtest_reduce_slices(const snac_coll_desc* bufs, int nsrc, uint64_t count_p
 // caller, so a test can pass a mismatch.  ok_out[b] = 1 where it returned
 // true.
 int devtest_collective(const snac_coll_desc* desc, const snac_dev_ctx* ctx, int bf16, int nsrc, int blocks,
-                       int coll_blocks, int extra, uint32_t* ok_out, hipStream_t s) {
+                       int coll_blocks, int extra, int no_workspace, uint32_t* ok_out, hipStream_t s) {
   if (!desc || !ctx || blocks <= 0 || coll_blocks < 0 || extra < 0) return hipErrorInvalidValue;
   const int grid = blocks + extra;
   const void* fn = nullptr;
@@ -213,11 +226,11 @@ int devtest_collective(const snac_coll_desc* desc, const snac_dev_ctx* ctx, int 
 #define SNAC_CASE(NN)                                                                                      \
   case NN:                                                                                                 \
     if (bf16)                                                                                              \
-      hipLaunchKernelGGL((collective_kernel<snac::BF16, NN>), dim3(grid), dim3(TH), 0, s, *desc, *ctx,     \
-                         (uint32_t)blocks, (uint32_t)coll_blocks, ok_out);                                 \
+      hipLaunchKernelGGL((collective_kernel<snac::BF16, NN>), dim3(grid), dim3(TH), LDS, s, *desc, *ctx,   \
+                         (uint32_t)blocks, (uint32_t)coll_blocks, no_workspace, ok_out);                   \
     else                                                                                                   \
-      hipLaunchKernelGGL((collective_kernel<snac::F32, NN>), dim3(grid), dim3(TH), 0, s, *desc, *ctx,      \
-                         (uint32_t)blocks, (uint32_t)coll_blocks, ok_out);                                 \
+      hipLaunchKernelGGL((collective_kernel<snac::F32, NN>), dim3(grid), dim3(TH), LDS, s, *desc, *ctx,    \
+                         (uint32_t)blocks, (uint32_t)coll_blocks, no_workspace, ok_out);                   \
     break;
   switch (nsrc) {
     SNAC_DISPATCH_N(SNAC_CASE)
@@ -236,11 +249,11 @@ int devtest_collective_nosync(const snac_coll_desc* desc, const snac_dev_ctx* ct
 #define SNAC_CASE(NN)                                                                                       \
   case NN:                                                                                                  \
     if (bf16)                                                                                               \
-      hipLaunchKernelGGL((collective_kernel<snac::BF16, NN, false>), dim3(blocks), dim3(TH), 0, s, *desc,   \
-                         *ctx, (uint32_t)blocks, (uint32_t)blocks, ok_out);                                 \
+      hipLaunchKernelGGL((collective_kernel<snac::BF16, NN, false>), dim3(blocks), dim3(TH), LDS, s, *desc, \
+                         *ctx, (uint32_t)blocks, (uint32_t)blocks, 0, ok_out);                              \
     else                                                                                                    \
-      hipLaunchKernelGGL((collective_kernel<snac::F32, NN, false>), dim3(blocks), dim3(TH), 0, s, *desc,    \
-                         *ctx, (uint32_t)blocks, (uint32_t)blocks, ok_out);                                 \
+      hipLaunchKernelGGL((collective_kernel<snac::F32, NN, false>), dim3(blocks), dim3(TH), LDS, s, *desc,  \
+                         *ctx, (uint32_t)blocks, (uint32_t)blocks, 0, ok_out);                              \
     break;
   switch (nsrc) {
     SNAC_DISPATCH_N(SNAC_CASE)
@@ -270,11 +283,11 @@ int devtest_fused_scale_allreduce(const snac_coll_desc* desc, const snac_dev_ctx
 #define SNAC_CASE(NN)                                                                                          \
   case NN:                                                                                                     \
     if (bf16)                                                                                                  \
-      hipLaunchKernelGGL((fused_kernel<snac::BF16, NN>), dim3(blocks), dim3(TH), 0, s, *desc, *ctx, *xs, count, \
-                         static_cast<char*>(check), ok_out);                                                   \
+      hipLaunchKernelGGL((fused_kernel<snac::BF16, NN>), dim3(blocks), dim3(TH), LDS, s, *desc, *ctx, *xs,      \
+                         count, static_cast<char*>(check), ok_out);                                            \
     else                                                                                                       \
-      hipLaunchKernelGGL((fused_kernel<snac::F32, NN>), dim3(blocks), dim3(TH), 0, s, *desc, *ctx, *xs, count,  \
-                         static_cast<char*>(check), ok_out);                                                   \
+      hipLaunchKernelGGL((fused_kernel<snac::F32, NN>), dim3(blocks), dim3(TH), LDS, s, *desc, *ctx, *xs,      \
+                         count, static_cast<char*>(check), ok_out);                                            \
     break;
   switch (n) {
     SNAC_DISPATCH_N(SNAC_CASE)
@@ -291,7 +304,7 @@ int devtest_flags(const snac_dev_ctx* ctx, const snac_coll_desc* xs, float* stag
                   uint32_t R, uint32_t B, uint64_t base, uint32_t* ok_out, hipStream_t s) {
   if (!ctx || !xs || n < 1 || n > SNAC_MAX_RANKS || S < 1 || ((uint64_t)n + 1) * S > ctx->nflags)
     return hipErrorInvalidValue;
-  if (!fits((const void*)&flags_kernel, n + 1)) return -1;
+  if (!fits((const void*)&flags_kernel, n + 1, 0)) return -1;
   hipLaunchKernelGGL(flags_kernel, dim3(n + 1), dim3(TH), 0, s, *ctx, *xs, stage, out, n, S, R, B, base, ok_out);
   return hipGetLastError();
 }
@@ -299,9 +312,42 @@ int devtest_flags(const snac_dev_ctx* ctx, const snac_coll_desc* xs, float* stag
 int devtest_many_flags(const snac_dev_ctx* ctx, uint32_t* vals, int K, uint64_t target, uint64_t* sum_out,
                        uint32_t* ok_out, hipStream_t s) {
   if (!ctx || K < 1 || (uint64_t)K > ctx->nflags) return hipErrorInvalidValue;
-  if (!fits((const void*)&many_flags_kernel, K + 1)) return -1;
+  if (!fits((const void*)&many_flags_kernel, K + 1, 0)) return -1;
   hipLaunchKernelGGL(many_flags_kernel, dim3(K + 1), dim3(TH), 0, s, *ctx, vals, K, target, sum_out, ok_out);
   return hipGetLastError();
+}
+
+// The launch contract as the header publishes it: out[0] = THREADS,
+// out[1] = PIPELINE_LDS_BYTES, out[2] = COPY_LDS_BYTES, out[3] =
+// REDUCE_LDS_BYTES, out[4] = COLLECTIVE_LDS_BYTES.
+int devtest_atom_contract(uint32_t* out) {
+  if (!out) return hipErrorInvalidValue;
+  out[0] = (uint32_t)Atom::THREADS;
+  out[1] = Atom::PIPELINE_LDS_BYTES;
+  out[2] = Atom::COPY_LDS_BYTES;
+  out[3] = Atom::REDUCE_LDS_BYTES;
+  out[4] = Atom::COLLECTIVE_LDS_BYTES;
+  return hipSuccess;
+}
+
+// Static LDS (bytes the kernel declares itself, beyond the dynamic
+// workspace) of the collective test kernels: which 0 = collective_kernel
+// <BF16, 8>, 1 = collective_kernel<F32, 1>, 2 = fused_kernel<BF16, 8>,
+// 3 = copy_slices_kernel.
+int devtest_static_lds(int which, uint32_t* out) {
+  const void* fn = nullptr;
+  switch (which) {
+    case 0: fn = (const void*)&collective_kernel<snac::BF16, 8>; break;
+    case 1: fn = (const void*)&collective_kernel<snac::F32, 1>; break;
+    case 2: fn = (const void*)&fused_kernel<snac::BF16, 8>; break;
+    case 3: fn = (const void*)&copy_slices_kernel; break;
+    default: return hipErrorInvalidValue;
+  }
+  hipFuncAttributes attr;
+  const hipError_t e = hipFuncGetAttributes(&attr, fn);
+  if (e != hipSuccess) return e;
+  *out = (uint32_t)attr.sharedSizeBytes;
+  return hipSuccess;
 }
 
 }  // extern "C"

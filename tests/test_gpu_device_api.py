@@ -32,12 +32,14 @@ def dev():
     sigs = {
         "devtest_copy_slices": [_VP, _VP, _U64, _I, _VP],
         "devtest_reduce_slices": [_DP, _I, _U64, _I, _I, _VP],
-        "devtest_collective": [_DP, _CP, _I, _I, _I, _I, _I, _VP, _VP],
+        "devtest_collective": [_DP, _CP, _I, _I, _I, _I, _I, _I, _VP, _VP],
         "devtest_collective_nosync": [_DP, _CP, _I, _I, _I, _VP, _VP],
         "devtest_fused_scale_allreduce": [_DP, _CP, _DP, _U64, _VP, _I, _VP, _VP],
         "devtest_flags": [_CP, _DP, _VP, _VP, _I, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, _U64, _VP,
                           _VP],
         "devtest_many_flags": [_CP, _VP, _I, _U64, _VP, _VP, _VP],
+        "devtest_atom_contract": [_VP],
+        "devtest_static_lds": [_I, _VP],
     }
     for name, args in sigs.items():
         f = getattr(lib, name)
@@ -174,7 +176,7 @@ def test_device_collective(dev, ctx8, coll, dtype, misalign):
     blocks, coll_blocks, extra = 48, 32, 16
     ok = ok_buffer(blocks + extra)
     launch(dev.devtest_collective(ctypes.byref(desc), ctypes.byref(dctx), int(dtype == "bf16"), n, blocks,
-                                  coll_blocks, extra, ok.data_ptr(), None))
+                                  coll_blocks, extra, 0, ok.data_ptr(), None))
     sync()
     snac.snac_check(ctx8)
     assert ok[:blocks].cpu().numpy().tolist() == [1] * blocks
@@ -218,7 +220,7 @@ def test_device_collective_repeats_and_one_block(dev, ctx8):
         for b in db:
             b.t.fill_(0xA5)
         ok = ok_buffer(blocks)
-        launch(dev.devtest_collective(ctypes.byref(desc), ctypes.byref(dctx), 1, n, blocks, coll_blocks, 0,
+        launch(dev.devtest_collective(ctypes.byref(desc), ctypes.byref(dctx), 1, n, blocks, coll_blocks, 0, 0,
                                       ok.data_ptr(), None))
         sync()
         snac.snac_check(ctx8)
@@ -235,7 +237,7 @@ def test_device_collective_mismatch_latches_arg(dev, ctx8):
     dctx = snac.snac_get_device_context(ctx8)
     ok = ok_buffer(16)
     # the kernel is instantiated for N = 3 sources, the descriptor has 8
-    launch(dev.devtest_collective(ctypes.byref(desc), ctypes.byref(dctx), 0, 3, 16, 16, 0, ok.data_ptr(), None))
+    launch(dev.devtest_collective(ctypes.byref(desc), ctypes.byref(dctx), 0, 3, 16, 16, 0, 0, ok.data_ptr(), None))
     sync()
     assert int(ok.sum().item()) == 0
     for b in db:
@@ -245,11 +247,50 @@ def test_device_collective_mismatch_latches_arg(dev, ctx8):
     assert e.value.status == snac.SNAC_E_ARG
     # re-armed: the same descriptor with matching template arguments works
     ok = ok_buffer(16)
-    launch(dev.devtest_collective(ctypes.byref(desc), ctypes.byref(dctx), 0, 8, 16, 16, 0, ok.data_ptr(), None))
+    launch(dev.devtest_collective(ctypes.byref(desc), ctypes.byref(dctx), 0, 8, 16, 16, 0, 0, ok.data_ptr(), None))
     sync()
     snac.snac_check(ctx8)
     for r, (b, w) in enumerate(zip(db, want)):
         assert_same(b.download(np.float32), w, "f32", f"after re-arm dst[{r}]")
+
+
+def test_device_collective_null_workspace_latches_arg(dev, ctx8):
+    """A call without an LDS workspace moves nothing and latches SNAC_E_ARG;
+    every participant returns false without waiting."""
+    n, m = 8, 4096
+    srcs, sb, db, want, nbytes, _ = _case(snac.SNAC_COLL_ALL_REDUCE, n, "f32", m, False, seed=10)
+    desc = snac.snac_describe(ctx8, snac.SNAC_COLL_ALL_REDUCE, [b.ptr for b in sb], [b.ptr for b in db], nbytes,
+                              None, "f32")
+    dctx = snac.snac_get_device_context(ctx8)
+    ok = ok_buffer(16)
+    launch(dev.devtest_collective(ctypes.byref(desc), ctypes.byref(dctx), 0, 8, 16, 16, 0, 1, ok.data_ptr(), None))
+    sync()
+    assert int(ok.sum().item()) == 0
+    for b in db:
+        assert np.all(b.download() == 0xA5), "nothing may be written without a workspace"
+    with pytest.raises(snac.SnacError) as e:
+        snac.snac_check(ctx8)
+    assert e.value.status == snac.SNAC_E_ARG
+
+
+def test_atom_launch_contract(dev):
+    """The published launch contract: THREADS threads per workgroup, and the
+    dynamic LDS that holds everything collective() keeps in LDS (256 jobs of
+    the table, the scan, the barrier word) -- the test kernels that call it
+    declare no static LDS of their own, and copy() needs none."""
+    import ctypes as ct
+
+    out = (ct.c_uint32 * 5)()
+    launch(dev.devtest_atom_contract(out))
+    threads, pipeline, copy_lds, reduce_lds, coll = list(out)
+    assert threads == 256
+    assert copy_lds == 0 and reduce_lds == 0
+    assert pipeline == coll
+    assert 256 * 40 + 256 * 4 + 4 <= coll <= 64 * 1024 and coll % 128 == 0
+    for which in range(4):
+        v = ct.c_uint32(0xFFFFFFFF)
+        launch(dev.devtest_static_lds(which, ct.byref(v)))
+        assert v.value == 0, f"test kernel {which} declares {v.value} bytes of static LDS"
 
 
 # --------------------------------- compute + in-kernel AllReduce + compute
