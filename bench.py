@@ -5,33 +5,58 @@ inputs with binary32 accumulation and bf16 output, 256 MiB per rank, the
 result written to all 8 destination buffers.  A step is one AllReduce call
 (one kernel) over inputs already resident in HBM.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--jsonl PATH]
 
 Prints one JSON line.  ``value`` is the algorithmic HBM bandwidth of the
 AllReduce, 2 * N * B bytes per call (every source read once, every
-destination written once) over the measured time per call.  ``roofline``
-relates that to the 8 TB/s HBM peak; ``traffic`` is the HBM traffic per
-launch from rocprofv3 counters when the recorded counters match the current
-kernel sources (else null).  ``cpu_baseline`` times the CPU oracle on a
-bounded sample of the same workload.  ``extra`` holds the other configured
-collectives (ReduceScatter then AllGather, AllToAll / AllToAllV, AllGatherV,
-ReduceScatterV, the SNAC pipeline, and a plain copy) measured the same way.
+destination written once) over the mean time of exactly --steps calls
+timed with HIP events on the launch stream.  ``roofline`` relates that to
+the 8 TB/s HBM peak and to the 1:1 read/write (copy) ceiling measured in
+the same run; ``traffic`` is the HBM traffic per launch from rocprofv3
+counters when the recorded counters match the current kernel sources
+(else null).  ``cpu_baseline`` times the CPU oracle on a bounded sample of
+the same workload.  ``extra`` holds, each measured the same way and with
+the counter figures of its own summary when valid:
 
-Other modes:
-    --only NAME     run one workload (allreduce, allreduce_atomic, copy, rs_ag,
-                    a2a, a2av, agv, rsv, pipeline_bf16, pipeline_f32,
-                    pipeline_latency) --
-                    for profiler runs
-    --sweep         AllReduce bf16 N=8 over 1 KiB .. 1 GiB per rank (JSON
-                    lines to stdout; small sizes batched in a HIP graph)
+  * the other configured workloads (ReduceScatter then AllGather, AllToAll,
+    AllToAllV, AllGatherV, ReduceScatterV, the SNAC pipeline in bf16 and
+    f32 and its latency sizes, a 1 GiB copy, the atomic AllReduce mode);
+  * the HBM ceilings (read-only, write-only, 1:1 copy probes);
+  * the AllReduce sweep, 1 KiB .. 1 GiB per rank, and the AllGather sweep,
+    128 B .. 128 MiB in per rank, each size the median over 20 runs of a
+    HIP graph of 10 calls (1 call from 64 MiB per rank up).
+
+Per collective, in the argument form of the pages' benchmark binaries:
+
+    python bench.py --coll NAME [minBytes [maxBytes [graphLaunches [runs [warmup [seed]]]]]]
+                    [--dtype D] [--nranks N] [--jsonl PATH]
+
+NAME is allreduce, reduce_scatter, all_gather, all_to_all, all_gather_v,
+reduce_scatter_v or all_to_all_v (or AR, RS, AG, A2A, AGV, RSV, A2AV).
+Sizes take K, M and G (powers of 1024) and double from minBytes to
+maxBytes; a size is the per-rank input (for AllGather: per-rank input, for
+the V variants: the per-rank total of the counts).  Each size is a HIP
+graph of graphLaunches calls replayed `runs` times after `warmup` replays;
+the median per call is reported, one JSON line per size (also appended to
+--jsonl).  algbw uses the pages' totalBytes: the output size for
+AllGather(V), the per-rank input size otherwise.
+
+Single workloads for profiler runs:
+
+    python bench.py --only NAME [--steps K] [--warmup W]
+
+NAME: allreduce, allreduce_atomic, copy, rs, ag, ag_cold, rs_ag, a2a, a2av,
+agv, rsv, pipeline_bf16, pipeline_f32, pipeline_latency, ceilings,
+sweep_ar, sweep_ag.
 """
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
 import os
-import platform
+import re
 import sys
 import time
 
@@ -42,19 +67,30 @@ sys.path.insert(0, ROOT)
 
 METRIC = "HBM GB/s & % of peak, 8-logical-rank bf16 AllReduce reduceN, 256 MiB/rank"
 PEAK_GBPS = 8000.0
+KiB = 1 << 10
 MiB = 1 << 20
 GiB = 1 << 30
 N = 8
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "allreduce_bf16_n8_256mib_counters.md")
+INFINITY_CACHE = 256 * MiB
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-# sources of the collective kernel (the dominant kernel of the benchmark)
-KERNEL_SOURCES = ("include/snac_device.hpp", "include/snac_layout.hpp", "include/snac.h",
-                  "copy_reduce_snac_amd/csrc/collectives.hip", "copy_reduce_snac_amd/csrc/internal.hpp")
+# ------------------------------------------------------- kernel-source hashes
+# Counter summaries record the hash of the sources of the kernels they
+# measured; a summary whose hash differs from the current sources is stale
+# and its figures are not reported.
+_COMMON = ("include/snac_device.hpp", "include/snac_layout.hpp", "include/snac.h",
+           "copy_reduce_snac_amd/csrc/internal.hpp")
+KERNEL_SOURCES = _COMMON + ("copy_reduce_snac_amd/csrc/collectives.hip",)
+SOURCE_SETS = {
+    "collectives": KERNEL_SOURCES,
+    "pipeline": _COMMON + ("copy_reduce_snac_amd/csrc/pipeline.hip",),
+    "probes": _COMMON + ("copy_reduce_snac_amd/csrc/probes.hip",),
+}
 
 
 def code_only(src: str) -> str:
@@ -83,35 +119,65 @@ def code_only(src: str) -> str:
     return " ".join("".join(out).split())
 
 
-def kernel_source_hash() -> str:
+def source_hash(names=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in names:
         with open(os.path.join(ROOT, name), encoding="utf-8") as f:
             h.update(name.encode())
             h.update(code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
-def recorded_traffic() -> float | None:
-    """HBM bytes per AllReduce launch from the counter summary, if it was
-    taken with the current kernel sources."""
+def kernel_source_hash() -> str:
+    return source_hash(KERNEL_SOURCES)
+
+
+def read_counter_summaries() -> dict:
+    """Machine-readable lines ("- key: `value`") of every profiles/*_counters.md,
+    keyed by its `workload` value; only summaries whose kernel_source_hash
+    matches the current sources of their `sources` set."""
+    out = {}
+    for path in sorted(glob.glob(os.path.join(PROFILES, "*_counters.md"))):
+        vals = {}
+        for line in open(path, encoding="utf-8").read().splitlines():
+            m = re.match(r"\s*- ([a-z_0-9]+): `([^`]*)`", line)
+            if m:
+                vals[m.group(1)] = m.group(2)
+        key, srcs = vals.get("workload"), vals.get("sources", "collectives")
+        if not key or srcs not in SOURCE_SETS:
+            continue
+        if vals.get("kernel_source_hash") != source_hash(SOURCE_SETS[srcs]):
+            continue
+        vals["file"] = os.path.relpath(path, ROOT)
+        out[key] = vals
+    return out
+
+
+COUNTERS: dict = {}
+
+
+def attach_counters(row: dict, key: str) -> dict:
+    """Add the counter figures of summary `key` (traffic per launch, its
+    ratio to the algorithmic bytes, L2 hit rate) when it is valid."""
+    c = COUNTERS.get(key)
+    row["counters"] = key
+    if not c:
+        row["traffic_bytes"] = None
+        return row
     try:
-        txt = open(TRAFFIC_FILE).read()
-    except OSError:
-        return None
-    vals = {}
-    for line in txt.splitlines():
-        if ":" in line and line.strip().startswith("- "):
-            k, v = line.strip()[2:].split(":", 1)
-            vals[k.strip()] = v.strip().strip("`")
-    if vals.get("kernel_source_hash") != kernel_source_hash():
-        return None
-    try:
-        return float(vals["traffic_bytes_per_launch"])
+        tr = float(c["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
-        return None
+        tr = None
+    row["traffic_bytes"] = tr
+    if tr and row.get("algorithmic_bytes"):
+        row["traffic_over_algorithmic"] = round(tr / row["algorithmic_bytes"], 5)
+    if "l2_hit" in c:
+        row["l2_hit"] = float(c["l2_hit"])
+    row["counters_file"] = c["file"]
+    return row
 
 
+# ------------------------------------------------------------------ timing
 class Env:
     def __init__(self):
         import torch
@@ -131,10 +197,11 @@ class Env:
         return t.to(self.dev, non_blocking=False)
 
     def empty(self, nbytes: int):
-        return self.torch.empty(nbytes, dtype=self.torch.uint8, device=self.dev)
+        return self.torch.empty(max(1, nbytes), dtype=self.torch.uint8, device=self.dev)
 
     def time_calls(self, fn, steps: int, warmup: int) -> float:
-        """Seconds per call: events on the launch stream around `steps` calls."""
+        """Seconds per call: events on the launch stream around exactly
+        `steps` calls, after `warmup` untimed ones."""
         torch = self.torch
         for _ in range(warmup):
             fn()
@@ -147,7 +214,6 @@ class Env:
         end.record(self.stream)
         torch.cuda.synchronize()
         return start.elapsed_time(end) / 1e3 / steps
-
 
     def time_calls_cold(self, fn, steps: int, warmup: int) -> float:
         """Seconds per call with the inputs evicted from the caches first: a
@@ -171,11 +237,33 @@ class Env:
         del scratch
         return total / steps
 
-
-def gen_bf16(m: int, cfg: int, rank: int) -> np.ndarray:
-    from copy_reduce_snac_amd import workloads as wl
-
-    return wl.normal_bf16(m, cfg, rank)
+    def graph_median(self, call, batch: int = 10, runs: int = 20, warmup: int = 5) -> float:
+        """Median seconds per call: `batch` calls captured in one HIP graph
+        (call(stream) launches one), replayed `warmup` times untimed, then
+        `runs` times, each replay timed with events."""
+        torch = self.torch
+        s = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            call(torch.cuda.current_stream())  # first launch outside the capture
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=s):
+                for _ in range(batch):
+                    call(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        times = []
+        for _ in range(runs):
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / 1e3 / batch)
+        del g
+        return float(np.median(times))
 
 
 def result(name, t, alg_bytes, total_bytes, **kw):
@@ -192,16 +280,142 @@ def result(name, t, alg_bytes, total_bytes, **kw):
     return d
 
 
-# ------------------------------------------------------------------ workloads
-def run_allreduce(env: Env, steps: int, warmup: int, per_rank: int = 256 * MiB, cpu: bool = True):
+def gen_bf16(m: int, cfg: int, rank: int, seed: int = 0) -> np.ndarray:
+    from copy_reduce_snac_amd import workloads as wl
+
+    return wl.normal_bf16(m, cfg, rank, seed=seed)
+
+
+# -------------------------------------------------------- collective specs
+# For a per-rank size B (bytes) and N ranks: per-rank output bytes, the
+# algorithmic bytes of one call (every byte read once and written once, as
+# the layout moves them), and the pages' totalBytes.
+SPECS = {
+    "allreduce": dict(dtype="bf16", out=lambda B, n: B, alg=lambda B, n: 2 * n * B, total=lambda B, n: B),
+    "reduce_scatter": dict(dtype="bf16", out=lambda B, n: B // n, alg=lambda B, n: n * B + B, total=lambda B, n: B),
+    "all_gather": dict(dtype="bf16", out=lambda B, n: n * B, alg=lambda B, n: n * B + n * n * B,
+                       total=lambda B, n: n * B),
+    "all_to_all": dict(dtype="u32", out=lambda B, n: B, alg=lambda B, n: 2 * n * B, total=lambda B, n: B),
+    "all_gather_v": dict(dtype="u32", out=lambda B, n: B, alg=lambda B, n: B + n * B, total=lambda B, n: B),
+    "reduce_scatter_v": dict(dtype="f32", out=None, alg=lambda B, n: n * B + B, total=lambda B, n: B),
+    "all_to_all_v": dict(dtype="u32", out=None, alg=lambda B, n: 2 * n * B, total=lambda B, n: B),
+}
+ALIASES = {"AR": "allreduce", "RS": "reduce_scatter", "AG": "all_gather", "A2A": "all_to_all",
+           "AGV": "all_gather_v", "RSV": "reduce_scatter_v", "A2AV": "all_to_all_v", "all_reduce": "allreduce"}
+ESIZE = {"bf16": 2, "f32": 4, "u32": 4, "byte": 1}
+
+
+def parse_size(s: str) -> int:
+    m = re.fullmatch(r"\s*(\d+)\s*([KMG]?)i?B?\s*", s, flags=re.I)
+    if not m:
+        raise SystemExit(f"bad size {s!r}: use e.g. 1K, 128M, 1G or a byte count")
+    return int(m.group(1)) << {"": 0, "K": 10, "M": 20, "G": 30}[m.group(2).upper()]
+
+
+class Sweep:
+    """Inputs for one collective at sizes up to `top` bytes per rank, and a
+    call(size, stream) that runs the collective at any of them (prefixes of
+    the same seeded buffers; V counts drawn per size)."""
+
+    def __init__(self, env: Env, coll: str, top: int, dtype: str, n: int, seed: int):
+        from copy_reduce_snac_amd import workloads as wl
+
+        self.env, self.coll, self.n, self.dtype, self.seed = env, coll, n, dtype, seed
+        self.e = ESIZE[dtype]
+        snac = env.snac
+        self.snac = snac
+        self.ctx = env.ctx if n == N else snac.snac_init(n, 0, env.stream)
+        cfg = {"allreduce": wl.CFG_AR_BF16_N8, "reduce_scatter": wl.CFG_RS_AG_BF16_N8,
+               "all_gather": wl.CFG_RS_AG_BF16_N8}.get(coll, wl.CFG_A2A_N8)
+        elems = top // self.e
+        t0 = time.time()
+        if dtype == "bf16":
+            host = [wl.normal_bf16(elems, cfg, r, seed=seed) for r in range(n)]
+        elif dtype == "f32":
+            host = [wl.normal_f32(elems, cfg, r, seed=seed) for r in range(n)]
+        elif dtype == "u32":
+            host = [wl.raw_u32(elems, cfg, r, seed=seed) for r in range(n)]
+        else:
+            host = [wl.raw_bytes(elems, cfg, r, seed=seed) for r in range(n)]
+        self.src = [env.upload(h) for h in host]
+        del host
+        out = SPECS[coll]["out"]
+        self.dst = [env.empty(out(top, n) if out else top) for _ in range(n)]
+        self.cfg = cfg
+        log(f"{coll}: {n} x {top} B inputs ready in {time.time() - t0:.1f}s")
+
+    def close(self):
+        if self.ctx != self.env.ctx:
+            self.snac.snac_finalize(self.ctx, self.env.stream)
+        del self.src, self.dst
+
+    def call_for(self, B: int):
+        """A call(stream) running the collective at B bytes per rank."""
+        from copy_reduce_snac_amd import workloads as wl
+
+        snac, ctx, src, dst, dt, n = self.snac, self.ctx, self.src, self.dst, self.dtype, self.n
+        c = self.coll
+        if c == "allreduce":
+            return lambda st: snac.snac_all_reduce(ctx, src, dst, B, dt, st)
+        if c == "reduce_scatter":
+            return lambda st: snac.snac_reduce_scatter(ctx, src, dst, B, dt, st)
+        if c == "all_gather":
+            return lambda st: snac.snac_all_gather(ctx, src, dst, B, dt, st)
+        if c == "all_to_all":
+            return lambda st: snac.snac_all_to_all(ctx, src, dst, B, dt, st)
+        E = B // self.e
+        if c == "all_to_all_v":
+            counts = wl.v_counts(n, E, n, cfg=self.cfg, seed=self.seed).reshape(-1).tolist()
+            return lambda st: snac.snac_all_to_all_v(ctx, src, dst, counts, dt, st)
+        row = wl.v_counts(n, E, 1, cfg=self.cfg, seed=self.seed)[0].tolist()
+        if c == "all_gather_v":
+            return lambda st: snac.snac_all_gather_v(ctx, src, dst, row, dt, st)
+        return lambda st: snac.snac_reduce_scatter_v(ctx, src, dst, row, dt, st)
+
+
+def sweep_rows(env: Env, coll: str, lo: int, hi: int, graph_launches: int | None, runs: int, warmup: int, seed: int,
+               dtype: str | None = None, n: int = N, jsonl=None, emit=False):
+    """One row per size lo, 2 lo, ..., hi.  graph_launches None: 10 calls
+    per graph below 64 MiB per rank, 1 from there up."""
+    spec = SPECS[coll]
+    dtype = dtype or spec["dtype"]
+    sw = Sweep(env, coll, hi, dtype, n, seed)
+    rows = []
+    B = lo
+    try:
+        while B <= hi:
+            K = graph_launches if graph_launches else (10 if B < 64 * MiB else 1)
+            t = env.graph_median(sw.call_for(B), batch=K, runs=runs, warmup=warmup)
+            alg = spec["alg"](B, n)
+            r = result(f"{coll} {dtype} N={n} {B} B/rank", t, alg, spec["total"](B, n), collective=coll,
+                       dtype=dtype, nranks=n, bytes_per_rank=B,
+                       timing=f"median over {runs} runs of a HIP graph of {K} calls",
+                       cache_resident=bool(alg < INFINITY_CACHE), seed=seed)
+            rows.append(r)
+            if emit:
+                print(json.dumps(r), flush=True)
+            if jsonl:
+                jsonl.write(json.dumps(r) + "\n")
+                jsonl.flush()
+            B *= 2
+    finally:
+        sw.close()
+        env.torch.cuda.empty_cache()
+    return rows
+
+
+# ---------------------------------------------------------------- workloads
+def run_allreduce(env: Env, steps: int, warmup: int, per_rank: int = 256 * MiB, cpu: bool = True,
+                  top: int = 256 * MiB, graph: bool = True):
+    """The headline.  Inputs are the first `per_rank` bytes of seeded
+    buffers of `top` bytes per rank (the same values at any top)."""
     from copy_reduce_snac_amd import workloads as wl
 
     snac = env.snac
-    m = per_rank // 2
     t0 = time.time()
-    host = [gen_bf16(m, wl.CFG_AR_BF16_N8, r) for r in range(N)]
+    host = [gen_bf16(top // 2, wl.CFG_AR_BF16_N8, r) for r in range(N)]
     src = [env.upload(h) for h in host]
-    dst = [env.empty(per_rank) for _ in range(N)]
+    dst = [env.empty(top) for _ in range(N)]
     log(f"allreduce: inputs ready in {time.time() - t0:.1f}s")
 
     def call():
@@ -209,11 +423,20 @@ def run_allreduce(env: Env, steps: int, warmup: int, per_rank: int = 256 * MiB, 
 
     t = env.time_calls(call, steps, warmup)
     alg = 2 * N * per_rank
-    out = result(f"allreduce_sum bf16 N={N} {per_rank // MiB} MiB/rank", t, alg, per_rank)
+    out = result(f"allreduce_sum bf16 N={N} {per_rank // MiB} MiB/rank", t, alg, per_rank,
+                 timing=f"mean of {steps} calls after {warmup} warmup calls")
+    if graph:
+        # the same calls as the pages' benchmark times them: median over 20
+        # runs of a one-call HIP graph
+        out["graph_median_ms"] = round(env.graph_median(
+            lambda st: snac.snac_all_reduce(env.ctx, src, dst, per_rank, "bf16", st), batch=1, runs=20,
+            warmup=5) * 1e3, 5)
     cpu_res = None
     if cpu:
-        cpu_res = cpu_baseline_allreduce(host, dst, per_rank)
-    return out, cpu_res
+        cpu_res = cpu_baseline_allreduce([h[:per_rank // 2] for h in host], dst, per_rank)
+    del src, dst, host
+    env.torch.cuda.empty_cache()
+    return attach_counters(out, "allreduce"), cpu_res
 
 
 def run_allreduce_atomic(env: Env, steps: int, warmup: int, per_rank: int = 256 * MiB):
@@ -236,6 +459,27 @@ def run_allreduce_atomic(env: Env, steps: int, warmup: int, per_rank: int = 256 
                   2 * N * per_rank, per_rank)
 
 
+def host_info() -> dict:
+    """CPU model, host RAM and thread counts of the machine running this."""
+    model, mem = "unknown", None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        for line in open("/proc/meminfo"):
+            if line.startswith("MemTotal:"):
+                mem = round(int(line.split()[1]) / (1 << 20), 1)
+                break
+    except OSError:
+        pass
+    return {"host_cpu_model": model, "host_mem_GiB": mem, "nproc": os.cpu_count(),
+            "host_threads_available": len(os.sched_getaffinity(0))}
+
+
 def cpu_baseline_allreduce(host, dst, per_rank, budget_s: float = 10.0):
     """The oracle, as it stands, over consecutive 32 MiB-per-rank slices of
     the same inputs, cycling through the whole workload until about
@@ -248,7 +492,7 @@ def cpu_baseline_allreduce(host, dst, per_rank, budget_s: float = 10.0):
     done = 0  # elements reduced, over every pass
     spent = 0.0
     ok = True
-    got = dst[0].cpu().numpy().view(np.uint16)
+    got = dst[0][:per_rank].cpu().numpy().view(np.uint16)
     passes = 0
     while spent < budget_s:
         lo = done % m
@@ -263,17 +507,17 @@ def cpu_baseline_allreduce(host, dst, per_rank, budget_s: float = 10.0):
         if hi == m:
             passes += 1
     value = 2 * N * done * 2 / spent / 1e9
-    return {
+    res = {
         "value": round(value, 3),
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
         "sample": f"the whole 256 MiB-per-rank workload in 32 MiB slices, cycled {done / m:.1f} times "
                   f"(NumPy, single thread, {spent:.1f} s); GPU output equal on the first pass: {ok}",
-        "host_cpu": platform.processor() or platform.machine(),
-        "host_threads_available": len(os.sched_getaffinity(0)),
         "parallel": cpu_baseline_allreduce_threads(host, m),
     }
+    res.update(host_info())
+    return res
 
 
 def cpu_baseline_allreduce_threads(host, m: int, budget_s: float = 3.0):
@@ -313,10 +557,43 @@ def run_copy(env: Env, steps: int, warmup: int, nbytes: int = GiB):
     src = env.torch.randint(0, 255, (nbytes,), dtype=env.torch.uint8, device=env.dev)
     dst = env.empty(nbytes)
     t = env.time_calls(lambda: snac.snac_copy(dst, src, nbytes, env.stream), steps, warmup)
-    return result(f"copy {nbytes // MiB} MiB", t, 2 * nbytes, nbytes)
+    return attach_counters(result(f"copy {nbytes // MiB} MiB", t, 2 * nbytes, nbytes), "copy")
 
 
-def run_rs_ag(env: Env, steps: int, warmup: int):
+PROBE_SHAPES = [(64, 4096, 2), (64, 4096, 4), (64, 4096, 5), (64, 4096, 8), (256, 16384, 1), (256, 16384, 2),
+                (256, 16384, 4)]
+
+
+def run_ceilings(env: Env, steps: int, warmup: int, nbytes: int = GiB):
+    """HBM ceilings of this machine: read-only, write-only and 1:1 copy
+    streams (snac_hbm_probe) of `nbytes` each, at every launch shape of
+    PROBE_SHAPES; the best shape of each kind is the ceiling."""
+    snac = env.snac
+    torch = env.torch
+    src = torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device=env.dev)
+    dst = env.empty(nbytes)
+    rows, best = [], {}
+    for kind, moved in (("read", nbytes), ("write", nbytes), ("copy", 2 * nbytes)):
+        for th, tile, w in PROBE_SHAPES:
+            s = None if kind == "write" else src
+            t = env.time_calls(lambda: snac.snac_hbm_probe(kind, dst, s, nbytes, th, tile, w, 0x9E3779B9,
+                                                           env.stream), steps, warmup)
+            gbps = moved / t / 1e9
+            rows.append({"probe": kind, "threads": th, "tile_bytes": tile, "wgs_per_cu": w,
+                         "ms_per_call": round(t * 1e3, 5), "GBps": round(gbps, 1)})
+            if gbps > best.get(kind, (0,))[0]:
+                best[kind] = (gbps, th, tile, w)
+    del src, dst
+    torch.cuda.empty_cache()
+    out = {"workload": f"HBM ceilings, {nbytes // MiB} MiB streams (snac_hbm_probe)", "shapes": rows}
+    for kind, (gbps, th, tile, w) in best.items():
+        out[f"{kind}_GBps"] = round(gbps, 1)
+        out[f"{kind}_frac_of_peak"] = round(gbps / PEAK_GBPS, 4)
+        out[f"{kind}_shape"] = f"{th} threads, {tile} B tiles, {w} per CU"
+    return out
+
+
+def run_rs_ag(env: Env, steps: int, warmup: int, which=("rs", "ag", "ag_cold")):
     from copy_reduce_snac_amd import workloads as wl
 
     snac = env.snac
@@ -325,22 +602,33 @@ def run_rs_ag(env: Env, steps: int, warmup: int):
     src = [env.upload(gen_bf16(rows * cols, wl.CFG_RS_AG_BF16_N8, r)) for r in range(N)]
     rs_out = [env.empty(per_rank // N) for _ in range(N)]
     ag_out = [env.empty(per_rank) for _ in range(N)]
-    t_rs = env.time_calls(lambda: snac.snac_reduce_scatter(env.ctx, src, rs_out, per_rank, "bf16", env.stream),
-                          steps, warmup)
+    out = []
+    rs = lambda: snac.snac_reduce_scatter(env.ctx, src, rs_out, per_rank, "bf16", env.stream)
     ag = lambda: snac.snac_all_gather(env.ctx, rs_out, ag_out, per_rank // N, "bf16", env.stream)
-    t_ag = env.time_calls(ag, steps, warmup)
-    t_ag_cold = env.time_calls_cold(ag, steps, warmup)
-    ar_out = [env.empty(per_rank) for _ in range(N)]
-    snac.snac_all_reduce(env.ctx, src, ar_out, per_rank, "bf16", env.stream)
-    env.torch.cuda.synchronize()
-    same = all(bool(env.torch.equal(a, b)) for a, b in zip(ag_out, ar_out))
-    return [
-        result(f"reduce_scatter bf16 N={N} ({rows}x{cols})/rank", t_rs, N * per_rank + per_rank, per_rank),
-        result(f"all_gather bf16 N={N} ({rows // N}x{cols})/rank in", t_ag, per_rank + N * per_rank, per_rank,
-               ag_of_rs_equals_allreduce=same),
-        result(f"all_gather bf16 N={N} ({rows // N}x{cols})/rank in, inputs evicted from the caches before each call",
-               t_ag_cold, per_rank + N * per_rank, per_rank),
-    ]
+    rs()
+    if "rs" in which:
+        t_rs = env.time_calls(rs, steps, warmup)
+        out.append(attach_counters(result(f"reduce_scatter bf16 N={N} ({rows}x{cols})/rank", t_rs,
+                                          N * per_rank + per_rank, per_rank), "rs"))
+    if "ag" in which:
+        t_ag = env.time_calls(ag, steps, warmup)
+        ar_out = [env.empty(per_rank) for _ in range(N)]
+        snac.snac_all_reduce(env.ctx, src, ar_out, per_rank, "bf16", env.stream)
+        env.torch.cuda.synchronize()
+        same = all(bool(env.torch.equal(a, b)) for a, b in zip(ag_out, ar_out))
+        del ar_out
+        out.append(attach_counters(result(f"all_gather bf16 N={N} ({rows // N}x{cols})/rank in", t_ag,
+                                          per_rank + N * per_rank, per_rank,
+                                          ag_of_rs_equals_allreduce=same, inputs="reused across calls"), "ag"))
+    if "ag_cold" in which:
+        t_ag_cold = env.time_calls_cold(ag, steps, warmup)
+        out.append(attach_counters(
+            result(f"all_gather bf16 N={N} ({rows // N}x{cols})/rank in, inputs evicted from the caches before "
+                   "each call", t_ag_cold, per_rank + N * per_rank, per_rank, inputs="evicted before each call"),
+            "ag_cold"))
+    del src, rs_out, ag_out
+    env.torch.cuda.empty_cache()
+    return out
 
 
 def run_a2a(env: Env, steps: int, warmup: int, variant: str):
@@ -353,24 +641,28 @@ def run_a2a(env: Env, steps: int, warmup: int, variant: str):
     if variant == "a2a":
         dst = [env.empty(per_rank) for _ in range(N)]
         t = env.time_calls(lambda: snac.snac_all_to_all(env.ctx, src, dst, per_rank, "u32", env.stream), steps, warmup)
-        return result(f"all_to_all u32 N={N} 128 MiB/rank", t, 2 * N * per_rank, per_rank)
+        return attach_counters(result(f"all_to_all u32 N={N} 128 MiB/rank", t, 2 * N * per_rank, per_rank), "a2a")
     c = wl.v_counts(N, e, N, cfg=wl.CFG_A2A_N8)
     if variant == "a2av":
         cols = c.sum(axis=0)
         dst = [env.empty(int(cols[d]) * 4) for d in range(N)]
         flat = c.reshape(-1).tolist()
         t = env.time_calls(lambda: snac.snac_all_to_all_v(env.ctx, src, dst, flat, "u32", env.stream), steps, warmup)
-        return result(f"all_to_all_v u32 N={N} 128 MiB/rank, Dirichlet(0.5) counts", t, 2 * N * per_rank, per_rank,
-                      zero_chunks=int((c == 0).sum()), unaligned_chunks=int((c % 4 != 0).sum()))
+        return attach_counters(result(f"all_to_all_v u32 N={N} 128 MiB/rank, Dirichlet(0.5) counts", t,
+                                      2 * N * per_rank, per_rank, zero_chunks=int((c == 0).sum()),
+                                      unaligned_chunks=int((c % 4 != 0).sum())), "a2av")
     row = c[0].tolist()
     if variant == "agv":
         dst = [env.empty(per_rank) for _ in range(N)]
         t = env.time_calls(lambda: snac.snac_all_gather_v(env.ctx, src, dst, row, "u32", env.stream), steps, warmup)
-        return result(f"all_gather_v u32 N={N}, counts sum 128 MiB", t, per_rank + N * per_rank, per_rank)
+        return attach_counters(result(f"all_gather_v u32 N={N}, counts sum 128 MiB", t, per_rank + N * per_rank,
+                                      per_rank), "agv")
     dsrc = [env.upload(wl.normal_f32(e, wl.CFG_A2A_N8, r)) for r in range(N)]
+    del src
     dst = [env.empty(int(row[r]) * 4) for r in range(N)]
     t = env.time_calls(lambda: snac.snac_reduce_scatter_v(env.ctx, dsrc, dst, row, "f32", env.stream), steps, warmup)
-    return result(f"reduce_scatter_v f32 N={N}, 128 MiB/rank in", t, N * per_rank + per_rank, per_rank)
+    return attach_counters(result(f"reduce_scatter_v f32 N={N}, 128 MiB/rank in", t, N * per_rank + per_rank,
+                                  per_rank), "rsv")
 
 
 def run_pipeline(env: Env, steps: int, warmup: int, dtype: str):
@@ -394,35 +686,9 @@ def run_pipeline(env: Env, steps: int, warmup: int, dtype: str):
     finally:
         snac.snac_finalize(ctx, env.stream)
     per_rank = count * es
-    return result(f"snac_pipeline {dtype} N={N} ({rows}x{cols})/rank", t, 3 * N * per_rank + per_rank, per_rank,
-                  staging_bytes_per_rank=128 * MiB)
-
-
-def graph_time(env: Env, call, batch: int = 10, reps: int = 20) -> float:
-    """Median seconds per call: `batch` calls captured in one HIP graph,
-    replayed `reps` times, each replay timed with events."""
-    torch = env.torch
-    s = torch.cuda.Stream()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(s):
-        call(torch.cuda.current_stream())  # first launch outside the capture
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g, stream=s):
-            for _ in range(batch):
-                call(torch.cuda.current_stream())
-    torch.cuda.synchronize()
-    for _ in range(3):
-        g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    times = []
-    for _ in range(reps):
-        e0.record()
-        g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1) / 1e3 / batch)
-    return float(np.median(times))
+    return attach_counters(result(f"snac_pipeline {dtype} N={N} ({rows}x{cols})/rank", t,
+                                  3 * N * per_rank + per_rank, per_rank, staging_bytes_per_rank=128 * MiB),
+                           f"pipeline_{dtype}")
 
 
 def run_pipeline_latency(env: Env):
@@ -436,79 +702,255 @@ def run_pipeline_latency(env: Env):
     lat = {}
     for p in range(10, 21):
         b = 1 << p
-        t = graph_time(env, lambda st: snac.snac_pipeline_scale_reduce(env.ctx, xs, out, b // 2, "bf16", st))
+        t = env.graph_median(lambda st: snac.snac_pipeline_scale_reduce(env.ctx, xs, out, b // 2, "bf16", st))
         lat[str(b)] = round(t * 1e6, 2)
     snac.snac_check(env.ctx, env.stream)
-    return {"workload": f"snac_pipeline bf16 N={N} latency, bytes/rank -> us/call (HIP graph, 10 calls)",
-            "us_per_call": lat}
+    return {"workload": f"snac_pipeline bf16 N={N} latency, bytes/rank -> us/call "
+                        "(median over 20 runs of a HIP graph of 10 calls)", "us_per_call": lat}
 
 
-def run_sweep(env: Env):
-    """AllReduce bf16 N=8, per-rank 1 KiB .. 1 GiB; below 64 MiB the calls
-    are captured 10 at a time in a HIP graph and the graph is replayed."""
-    from copy_reduce_snac_amd import workloads as wl
+def run_sweep_ar(env: Env, runs: int = 20, warmup: int = 5):
+    return {"workload": f"allreduce bf16 N={N} sweep, 1 KiB .. 1 GiB per rank",
+            "rows": sweep_rows(env, "allreduce", KiB, GiB, None, runs, warmup, 0)}
 
-    snac = env.snac
-    top = GiB
-    src = [env.upload(gen_bf16(top // 2, wl.CFG_AR_BF16_N8, r)) for r in range(N)]
-    dst = [env.empty(top) for _ in range(N)]
-    p = 10
-    while (1 << p) <= top:
-        b = 1 << p
-        if b < 64 * MiB:
-            t = graph_time(env, lambda st: snac.snac_all_reduce(env.ctx, src, dst, b, "bf16", st))
-        else:
-            t = env.time_calls(lambda: snac.snac_all_reduce(env.ctx, src, dst, b, "bf16", env.stream), 10, 3)
-        r = result(f"allreduce_sum bf16 N={N} {b} B/rank", t, 2 * N * b, b,
-                   cache_resident=bool(2 * N * b < 256 * MiB))
-        print(json.dumps(r), flush=True)
-        p += 1
+
+def run_sweep_ag(env: Env, runs: int = 20, warmup: int = 5):
+    return {"workload": f"all_gather bf16 N={N} sweep, 128 B .. 128 MiB in per rank (1 KiB .. 1 GiB out)",
+            "rows": sweep_rows(env, "all_gather", 128, 128 * MiB, None, runs, warmup, 0)}
+
+
+ONLY = {
+    "allreduce": lambda env, a: run_allreduce(env, a.steps, a.warmup, cpu=False, graph=False)[0],
+    "allreduce_atomic": lambda env, a: run_allreduce_atomic(env, a.steps, a.warmup),
+    "copy": lambda env, a: run_copy(env, a.steps, a.warmup),
+    "ceilings": lambda env, a: run_ceilings(env, a.steps, a.warmup),
+    "rs": lambda env, a: run_rs_ag(env, a.steps, a.warmup, ("rs",)),
+    "ag": lambda env, a: run_rs_ag(env, a.steps, a.warmup, ("ag",)),
+    "ag_cold": lambda env, a: run_rs_ag(env, a.steps, a.warmup, ("ag_cold",)),
+    "rs_ag": lambda env, a: run_rs_ag(env, a.steps, a.warmup),
+    "a2a": lambda env, a: run_a2a(env, a.steps, a.warmup, "a2a"),
+    "a2av": lambda env, a: run_a2a(env, a.steps, a.warmup, "a2av"),
+    "agv": lambda env, a: run_a2a(env, a.steps, a.warmup, "agv"),
+    "rsv": lambda env, a: run_a2a(env, a.steps, a.warmup, "rsv"),
+    "pipeline_bf16": lambda env, a: run_pipeline(env, a.steps, a.warmup, "bf16"),
+    "pipeline_f32": lambda env, a: run_pipeline(env, a.steps, a.warmup, "f32"),
+    "pipeline_latency": lambda env, a: run_pipeline_latency(env),
+    "sweep_ar": lambda env, a: run_sweep_ar(env),
+    "sweep_ag": lambda env, a: run_sweep_ag(env),
+}
+
+
+# ------------------------------------------------- counter summaries
+# Each workload's dominant kernel (a regex on the kernel name rocprofv3
+# reports), its algorithmic bytes per launch, and the source set its
+# counters are tied to.
+PROFILED = {
+    "allreduce": (r"snac::reduce_kernel<8, snac::BF16", 2 * N * 256 * MiB, "collectives"),
+    "copy": (r"snac::copy_kernel", 2 * GiB, "collectives"),
+    "rs": (r"snac::reduce_kernel<8, snac::BF16", N * 128 * MiB + 128 * MiB, "collectives"),
+    "ag": (r"snac::copy_kernel", 128 * MiB + N * 128 * MiB, "collectives"),
+    "ag_cold": (r"snac::copy_kernel", 128 * MiB + N * 128 * MiB, "collectives"),
+    "a2a": (r"snac::copy_kernel", 2 * N * 128 * MiB, "collectives"),
+    "a2av": (r"snac::copy_kernel", 2 * N * 128 * MiB, "collectives"),
+    "agv": (r"snac::copy_kernel", 128 * MiB + N * 128 * MiB, "collectives"),
+    "rsv": (r"snac::reduce_kernel<8, snac::F32", N * 128 * MiB + 128 * MiB, "collectives"),
+    "pipeline_bf16": (r"snac::pipeline_kernel<snac::BF16, 8>", 3 * N * 64 * MiB + 64 * MiB, "pipeline"),
+    "pipeline_f32": (r"snac::pipeline_kernel<snac::F32, 8>", 3 * N * 128 * MiB + 128 * MiB, "pipeline"),
+}
+
+# counter passes (one rocprofv3 --pmc run each) and what each holds
+PMC_PASSES = {
+    "fetch": ["FETCH_SIZE"],
+    "write": ["WRITE_SIZE"],
+    "rdsize": ["TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum", "TCC_BUBBLE_sum"],
+    "l2wr": ["TCC_HIT_sum", "TCC_MISS_sum", "TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum"],
+    "stall": ["TCC_EA0_WRREQ_STALL_sum", "TCC_TAG_STALL_sum", "TCC_EA0_RDREQ_LEVEL_sum", "TCC_EA0_WRREQ_LEVEL_sum"],
+    "utcl1": ["TCP_UTCL1_TRANSLATION_MISS_sum", "TCP_UTCL1_REQUEST_sum", "TCP_PENDING_STALL_CYCLES_sum",
+              "TCP_TCC_READ_REQ_LATENCY_sum"],
+}
+
+
+def _csv_means(dirpath: str, kernel_re: str) -> dict:
+    """Mean value per counter over the dispatches of kernels matching
+    kernel_re in the rocprofv3 counter CSVs under dirpath; also the kernel
+    name and dispatch count."""
+    import csv
+
+    vals, name = {}, None
+    for path in glob.glob(os.path.join(dirpath, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            if not re.search(kernel_re, r["Kernel_Name"]):
+                continue
+            name = r["Kernel_Name"]
+            vals.setdefault(r["Counter_Name"], {})[r["Dispatch_Id"]] = float(r["Counter_Value"])
+    out = {k: sum(v.values()) / len(v) for k, v in vals.items()}
+    out["_dispatches"] = max((len(v) for v in vals.values()), default=0)
+    out["_kernel"] = name
+    return out
+
+
+def _trace_stats(dirpath: str, kernel_re: str):
+    """(name, calls, average ns) of the kernel matching kernel_re in a
+    rocprofv3 --stats kernel summary under dirpath."""
+    import csv
+
+    for path in glob.glob(os.path.join(dirpath, "**", "*kernel_stats.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            if re.search(kernel_re, r["Name"]):
+                return r["Name"], int(r["Calls"]), float(r["AverageNs"])
+    return None
+
+
+def summarize(workload: str, root: str, commands: list[str]) -> str:
+    """A profiles/ summary (markdown) of `workload` from the rocprofv3 output
+    under root/<pass>_<workload> (counter passes) and root/trace_<workload>
+    (kernel trace), with the copy passes under root/<pass>_copy as the
+    calibration of the FETCH_SIZE and WRITE_SIZE derived counters."""
+    kre, alg, srcs = PROFILED[workload]
+    m = {p: _csv_means(os.path.join(root, f"{p}_{workload}"), kre) for p in PMC_PASSES}
+    cal = {p: _csv_means(os.path.join(root, f"{p}_copy"), PROFILED["copy"][0]) for p in ("fetch", "write")}
+    kernel = next((v["_kernel"] for v in m.values() if v.get("_kernel")), kre)
+    rd, wr, l2 = m["rdsize"], m["write"], m["l2wr"]
+    read_bytes = 32 * rd["TCC_EA0_RDREQ_32B_sum"] + 64 * rd["TCC_EA0_RDREQ_64B_sum"] + 128 * rd["TCC_EA0_RDREQ_128B_sum"]
+    wreq, w64 = l2["TCC_EA0_WRREQ_sum"], l2["TCC_EA0_WRREQ_64B_sum"]
+    write_bytes = 32 * (wreq - w64) + 64 * w64
+    traffic = read_bytes + write_bytes
+    hit = l2["TCC_HIT_sum"] / max(1.0, l2["TCC_HIT_sum"] + l2["TCC_MISS_sum"])
+    fetch_kib, write_kib = m["fetch"]["FETCH_SIZE"], wr["WRITE_SIZE"]
+    cal_fetch = GiB / (1024 * cal["fetch"]["FETCH_SIZE"])
+    cal_write = GiB / (1024 * cal["write"]["WRITE_SIZE"])
+    tr = _trace_stats(os.path.join(root, f"trace_{workload}"), kre)
+    L = [f"# {workload}: HBM traffic and L2 behaviour of its dominant kernel from rocprofv3 counters", "",
+         f"Kernel: `{kernel}`.  Each figure is the mean over its {m['rdsize']['_dispatches']} profiled dispatches; "
+         "every counter pass is its own run of the same command on the same box.", ""]
+    if tr:
+        L += [f"Kernel trace (`--kernel-trace --stats`): {tr[1]} calls, average {tr[2] / 1e3:.1f} us "
+              f"= {alg / tr[2]:.0f} GB/s of algorithmic bytes.", ""]
+    L += ["Commands, from the repository root on the GPU box (`REPO=$PWD`; one run per pass):", ""]
+    L += [f"    {c}" for c in commands] + [""]
+    L += ["Bytes by request size (gfx950 has a counter per EA read size; the `FETCH_SIZE` expression counts "
+          "128-byte reads through `TCC_BUBBLE`, which reads zero here, so it counts each as 64 bytes):", "",
+          "| counter | per dispatch | bytes |", "|---|---|---|"]
+    for k, b in (("TCC_EA0_RDREQ_32B_sum", 32), ("TCC_EA0_RDREQ_64B_sum", 64), ("TCC_EA0_RDREQ_128B_sum", 128)):
+        L.append(f"| {k} | {rd[k]:.1f} | {rd[k] * b:.0f} |")
+    L += [f"| TCC_BUBBLE_sum | {rd['TCC_BUBBLE_sum']:.1f} | |",
+          f"| TCC_EA0_WRREQ_sum (64-byte: {w64:.1f}) | {wreq:.1f} | {write_bytes:.0f} |", "",
+          f"Read {read_bytes:.0f} B + written {write_bytes:.0f} B = **{traffic:.0f} B per launch**, "
+          f"**{traffic / alg:.5f} x** the algorithmic {alg} B.", "",
+          "Derived counters, and the calibration a plain 1 GiB copy gives them (`bench.py --only copy`):", "",
+          "| counter | KiB per dispatch | copy calibration (1 GiB / counter) | scaled bytes |", "|---|---|---|---|",
+          f"| FETCH_SIZE | {fetch_kib:.1f} | {cal_fetch:.4f} | {fetch_kib * 1024 * cal_fetch:.0f} |",
+          f"| WRITE_SIZE | {write_kib:.1f} | {cal_write:.4f} | {write_kib * 1024 * cal_write:.0f} |", "",
+          f"L2 (TCC): {l2['TCC_HIT_sum']:.0f} hits, {l2['TCC_MISS_sum']:.0f} misses per dispatch, hit rate "
+          f"**{hit:.3f}**.", ""]
+    if m["stall"].get("_dispatches"):
+        st = m["stall"]
+        L += ["Stall and latency counters (sums over TCC / TCP instances, per dispatch):", "",
+              "| counter | per dispatch |", "|---|---|"]
+        L += [f"| {k} | {v:.0f} |" for k, v in st.items() if not k.startswith("_")]
+        L += [f"| {k} | {v:.0f} |" for k, v in m["utcl1"].items() if not k.startswith("_")]
+        if rd.get("TCC_EA0_RDREQ_32B_sum") is not None and st.get("TCC_EA0_RDREQ_LEVEL_sum"):
+            nreq = rd["TCC_EA0_RDREQ_32B_sum"] + rd["TCC_EA0_RDREQ_64B_sum"] + rd["TCC_EA0_RDREQ_128B_sum"]
+            L.append(f"| mean EA read requests in flight x cycles / requests (read latency, cycles) | "
+                     f"{st['TCC_EA0_RDREQ_LEVEL_sum'] / max(1.0, nreq):.0f} |")
+            L.append(f"| mean write latency proxy: WRREQ_LEVEL / WRREQ (cycles) | "
+                     f"{st['TCC_EA0_WRREQ_LEVEL_sum'] / max(1.0, wreq):.0f} |")
+        L.append("")
+    L += ["Machine-readable (read by bench.py; the hash is of the kernel sources the counters were taken with):", "",
+          f"- workload: `{workload}`", f"- sources: `{srcs}`",
+          f"- kernel_source_hash: `{source_hash(SOURCE_SETS[srcs])}`",
+          f"- traffic_bytes_per_launch: `{traffic:.0f}`", f"- read_bytes_per_launch: `{read_bytes:.0f}`",
+          f"- write_bytes_per_launch: `{write_bytes:.0f}`", f"- algorithmic_bytes_per_launch: `{alg}`",
+          f"- l2_hit: `{hit:.4f}`", f"- fetch_size_copy_calibration: `{cal_fetch:.4f}`",
+          f"- write_size_copy_calibration: `{cal_write:.4f}`"]
+    if tr:
+        L.append(f"- kernel_average_ns: `{tr[2]:.0f}`")
+    return "\n".join(L) + "\n"
+
+
+def rows_of(item):
+    """The JSONL rows of one result (sweeps expand into their sizes)."""
+    if isinstance(item, list):
+        out = []
+        for x in item:
+            out.extend(rows_of(x))
+        return out
+    if isinstance(item, dict) and "rows" in item:
+        return list(item["rows"])
+    return [item]
 
 
 def main() -> int:
-    ap = argparse.ArgumentParser()
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default=None)
-    ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--only", default=None, choices=sorted(ONLY))
+    ap.add_argument("--coll", default=None, help="per-collective sweep: NAME then the pages' positional arguments")
+    ap.add_argument("pos", nargs="*", help="[minBytes [maxBytes [graphLaunches [runs [warmup [seed]]]]]] for --coll")
+    ap.add_argument("--dtype", default=None)
+    ap.add_argument("--nranks", type=int, default=N)
+    ap.add_argument("--jsonl", default=None, help="append one JSON line per measured row to this file")
+    ap.add_argument("--sweep", action="store_true", help="same as --coll allreduce 1K 1G")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--summarize", default=None, metavar="WORKLOAD",
+                    help="write profiles/WORKLOAD_counters.md from the rocprofv3 output under --prof-dir")
+    ap.add_argument("--prof-dir", default=os.path.join(ROOT, "gpurun_out", "prof"))
+    ap.add_argument("--commands", default=None, help="file listing the rocprofv3 commands that made --prof-dir")
     args = ap.parse_args()
+    if args.summarize:
+        cmds = open(args.commands).read().splitlines() if args.commands else []
+        text = summarize(args.summarize, args.prof_dir, [c for c in cmds if c.strip()])
+        dest = os.path.join(PROFILES, f"{args.summarize}_counters.md")
+        with open(dest, "w", encoding="utf-8") as f:
+            f.write(text)
+        print(dest)
+        return 0
     if args.gpus != 1:
         print(f"bench.py: the library runs its N logical ranks in one GPU's HBM; --gpus {args.gpus} "
-              "is not supported", file=sys.stderr)
+              "is not supported (nothing here uses a second GPU)", file=sys.stderr)
         return 2
+    if args.pos and not args.coll:
+        ap.error("positional size arguments go with --coll")
+    global COUNTERS
+    COUNTERS = read_counter_summaries()
+    jsonl = open(args.jsonl, "a") if args.jsonl else None
     env = Env()
-    if args.sweep:
-        run_sweep(env)
+    if args.sweep and not args.coll:
+        args.coll, args.pos = "allreduce", ["1K", "1G"]
+    if args.coll:
+        coll = ALIASES.get(args.coll, ALIASES.get(args.coll.upper(), args.coll))
+        if coll not in SPECS:
+            raise SystemExit(f"unknown collective {args.coll}: one of {', '.join(SPECS)}")
+        p = args.pos + [None] * (6 - len(args.pos))
+        lo = parse_size(p[0]) if p[0] else KiB
+        hi = parse_size(p[1]) if p[1] else lo
+        graph_launches = int(p[2]) if p[2] else 10
+        runs = int(p[3]) if p[3] else 20
+        warmup = int(p[4]) if p[4] else 5
+        seed = int(p[5]) if p[5] else 0
+        sweep_rows(env, coll, lo, hi, graph_launches, runs, warmup, seed, dtype=args.dtype, n=args.nranks,
+                   jsonl=jsonl, emit=True)
+        env.snac.snac_finalize(env.ctx, env.stream)
         return 0
     if args.only:
-        name = args.only
-        if name == "allreduce":
-            r, _ = run_allreduce(env, args.steps, args.warmup, cpu=False)
-        elif name == "allreduce_atomic":
-            r = run_allreduce_atomic(env, args.steps, args.warmup)
-        elif name == "copy":
-            r = run_copy(env, args.steps, args.warmup)
-        elif name == "rs_ag":
-            r = run_rs_ag(env, args.steps, args.warmup)
-        elif name in ("a2a", "a2av", "agv", "rsv"):
-            r = run_a2a(env, args.steps, args.warmup, name)
-        elif name == "pipeline_latency":
-            r = run_pipeline_latency(env)
-        elif name.startswith("pipeline_"):
-            r = run_pipeline(env, args.steps, args.warmup, name.split("_", 1)[1])
-        else:
-            raise SystemExit(f"unknown workload {name}")
+        r = ONLY[args.only](env, args)
         print(json.dumps(r), flush=True)
+        if jsonl:
+            for x in rows_of(r):
+                jsonl.write(json.dumps(x) + "\n")
+        env.snac.snac_finalize(env.ctx, env.stream)
         return 0
 
     head, cpu = run_allreduce(env, args.steps, args.warmup, cpu=not args.no_cpu)
     extra = []
+    ceilings = None
     if not args.no_extra:
         env.torch.cuda.empty_cache()
         extra.append(run_copy(env, args.steps, args.warmup))
+        ceilings = run_ceilings(env, args.steps, args.warmup)
+        extra.append(ceilings)
         extra.extend(run_rs_ag(env, args.steps, args.warmup))
         for v in ("a2a", "a2av", "agv", "rsv"):
             extra.append(run_a2a(env, args.steps, args.warmup, v))
@@ -518,9 +960,22 @@ def main() -> int:
         extra.append(run_pipeline_latency(env))
         env.torch.cuda.empty_cache()
         extra.append(run_allreduce_atomic(env, 3, 1))
-    t = head["ms_per_call"] / 1e3
+        env.torch.cuda.empty_cache()
+        extra.append(run_sweep_ar(env))
+        extra.append(run_sweep_ag(env))
     achieved = head["hbm_GBps"]
-    traffic = recorded_traffic()
+    roofline = {
+        "bound": "hbm",
+        "achieved": achieved,
+        "peak": PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": round(achieved / PEAK_GBPS, 4),
+        "traffic": head.get("traffic_bytes"),
+    }
+    if ceilings:
+        copy_ceiling = max(ceilings.get("copy_GBps", 0.0), extra[0]["hbm_GBps"])
+        roofline["copy_ceiling_GBps"] = round(copy_ceiling, 1)
+        roofline["frac_of_copy_ceiling"] = round(achieved / copy_ceiling, 4)
     line = {
         "metric": METRIC,
         "value": achieved,
@@ -541,19 +996,16 @@ def main() -> int:
             "parallelism": "one GPU, 8 logical ranks in its HBM",
         },
         "algbw_GBps": head["algbw_GBps"],
-        "roofline": {
-            "bound": "hbm",
-            "achieved": achieved,
-            "peak": PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": round(achieved / PEAK_GBPS, 4),
-            "traffic": traffic,
-        },
+        "graph_median_ms": head.get("graph_median_ms"),
+        "roofline": roofline,
         "cpu_baseline": cpu,
         "kernel_source_hash": kernel_source_hash(),
         "extra": extra,
     }
     print(json.dumps(line), flush=True)
+    if jsonl:
+        for x in [head] + rows_of(extra):
+            jsonl.write(json.dumps(x) + "\n")
     env.snac.snac_finalize(env.ctx, env.stream)
     return 0
 

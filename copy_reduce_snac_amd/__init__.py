@@ -127,6 +127,7 @@ _SIGS = {
     "snac_ctx_nranks": (_I, [_VP]),
     "snac_abort": (_I, [_VP]),
     "snac_copy": (_I, [_VP, _VP, _SZ, _VP]),
+    "snac_hbm_probe": (_I, [_I, _VP, _VP, _SZ, _I, _I, _I, ctypes.c_uint32, _VP]),
     "snac_reduce_n": (_I, [ctypes.POINTER(_VP), _I, ctypes.POINTER(_VP), _I, _SZ, _I, _VP]),
     "snac_all_reduce": (_I, [_VP, ctypes.POINTER(_VP), ctypes.POINTER(_VP), _SZ, _I, _VP]),
     "snac_all_reduce_ex": (_I, [_VP, ctypes.POINTER(_VP), ctypes.POINTER(_VP), _SZ, _I, _I, _VP]),
@@ -254,6 +255,18 @@ def snac_abort(ctx: int) -> None:
 # ----------------------------------------------------------------- Atoms
 def snac_copy(dst, src, nbytes: int, stream=None) -> None:
     _check(lib().snac_copy(_ptr(dst), _ptr(src), nbytes, _stream(stream)), "snac_copy")
+
+
+SNAC_PROBE_READ, SNAC_PROBE_WRITE, SNAC_PROBE_COPY = range(3)
+_PROBES = {"read": SNAC_PROBE_READ, "write": SNAC_PROBE_WRITE, "copy": SNAC_PROBE_COPY}
+
+
+def snac_hbm_probe(kind, dst, src, nbytes: int, threads: int = 64, tile_bytes: int = 4096, wgs_per_cu: int = 4,
+                   magic: int = 0x9E3779B9, stream=None) -> None:
+    """HBM ceiling probe (measurement helper): kind "read", "write" or "copy"."""
+    k = _PROBES[kind] if isinstance(kind, str) else int(kind)
+    _check(lib().snac_hbm_probe(k, _ptr(dst), _ptr(src) if src is not None else None, nbytes, threads, tile_bytes,
+                                wgs_per_cu, magic & 0xFFFFFFFF, _stream(stream)), "snac_hbm_probe")
 
 
 def snac_reduce_n(dsts: Sequence, srcs: Sequence, count: int, dtype, stream=None) -> None:

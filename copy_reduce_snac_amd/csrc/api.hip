@@ -375,12 +375,11 @@ snac_status describe_empty(int32_t coll, int n, int e) {
   return ok();
 }
 
-// fixed-size collectives share their checks
-snac_status fixed_collective(int32_t coll, snac_ctx* ctx, const void* const* src, void* const* dst, size_t bytes,
-                             snac_dtype dtype, snac_stream stream) {
-  snac_status st = check_ctx(ctx);
-  if (st != SNAC_OK) return st;
-  const int n = ctx->nranks;
+// fixed-size collectives share their checks (n ranks; the context's rank
+// count, or the caller's for the context-free entry point)
+snac_status fixed_collective_n(int32_t coll, int n, const void* const* src, void* const* dst, size_t bytes,
+                               snac_dtype dtype, snac_stream stream) {
+  snac_status st = SNAC_OK;
   const int e = esize_of(dtype);
   if (!e) return fail(SNAC_E_ARG, "unknown dtype %d", (int)dtype);
   const bool reduce = coll == kAllReduce || coll == kReduceScatter;
@@ -414,6 +413,13 @@ snac_status fixed_collective(int32_t coll, snac_ctx* ctx, const void* const* src
   if (coll == kAllReduce) p.d.split_multicast = needs_split(dst, n);
   if (coll == kAllGather) p.d.split_multicast = split_copy(dst, n);
   return run(p, (hipStream_t)stream);
+}
+
+snac_status fixed_collective(int32_t coll, snac_ctx* ctx, const void* const* src, void* const* dst, size_t bytes,
+                             snac_dtype dtype, snac_stream stream) {
+  const snac_status st = check_ctx(ctx);
+  if (st != SNAC_OK) return st;
+  return fixed_collective_n(coll, ctx->nranks, src, dst, bytes, dtype, stream);
 }
 
 snac_status v_collective(int32_t coll, snac_ctx* ctx, const void* const* src, void* const* dst, const size_t* counts,
@@ -628,6 +634,26 @@ snac_status snac_copy(void* dst, const void* src, size_t bytes, snac_stream stre
   p.d.src[0] = src;
   p.d.dst[0] = dst;
   return run(p, (hipStream_t)stream);
+}
+
+snac_status snac_hbm_probe(int kind, void* dst, const void* src, size_t bytes, int threads, int tile_bytes,
+                           int wgs_per_cu, uint32_t magic, snac_stream stream) {
+  if (kind < SNAC_PROBE_READ || kind > SNAC_PROBE_COPY) return fail(SNAC_E_ARG, "unknown probe kind %d", kind);
+  if (threads != 64 && threads != 256) return fail(SNAC_E_ARG, "threads must be 64 or 256");
+  if (tile_bytes != 4096 && tile_bytes != 16384) return fail(SNAC_E_ARG, "tile_bytes must be 4096 or 16384");
+  if (wgs_per_cu < 1 || wgs_per_cu > 32) return fail(SNAC_E_ARG, "wgs_per_cu outside 1..32");
+  if (bytes % 16) return fail(SNAC_E_ARG, "bytes must be a multiple of 16");
+  if (bytes == 0) return ok();
+  if (!dst) return fail(SNAC_E_ARG, "dst is NULL");
+  if (kind != SNAC_PROBE_WRITE && !src) return fail(SNAC_E_ARG, "src is NULL");
+  if (((uintptr_t)dst | (kind != SNAC_PROBE_WRITE ? (uintptr_t)src : 0)) & 15u)
+    return fail(SNAC_E_ARG, "dst and src must be 16-byte aligned");
+  if (kind == SNAC_PROBE_COPY &&
+      overlaps(Range{(uintptr_t)dst, (uintptr_t)dst + bytes}, Range{(uintptr_t)src, (uintptr_t)src + bytes}))
+    return fail(SNAC_E_ARG, "src and dst overlap");
+  const hipError_t e = launch_probe(kind, dst, src, bytes, threads, tile_bytes, wgs_per_cu, magic, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "probe launch");
+  return ok();
 }
 
 snac_status snac_reduce_n(void* const* dst, int ndst, const void* const* src, int nsrc, size_t count,

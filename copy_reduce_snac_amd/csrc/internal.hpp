@@ -109,4 +109,8 @@ hipError_t fill_u64(uint64_t* p, uint64_t n, uint64_t v, hipStream_t stream);
 
 int device_cu_count();
 
+// HBM ceiling probes (probes.hip): kind 0 read, 1 write, 2 copy.
+hipError_t launch_probe(int kind, void* dst, const void* src, uint64_t bytes, int threads, int tile_bytes,
+                        int wgs_per_cu, uint32_t magic, hipStream_t stream);
+
 }  // namespace snac

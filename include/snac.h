@@ -224,6 +224,34 @@ snac_status snac_copy(void* dst, const void* src, size_t bytes, snac_stream stre
 snac_status snac_reduce_n(void* const* dst, int ndst, const void* const* src, int nsrc, size_t count,
                           snac_dtype dtype, snac_stream stream);
 
+/* ---------------------------------------------------- measurement probes */
+
+typedef enum snac_probe_kind {
+  SNAC_PROBE_READ = 0,  /* read src[0, bytes) */
+  SNAC_PROBE_WRITE = 1, /* write dst[0, bytes) */
+  SNAC_PROBE_COPY = 2   /* dst[0, bytes) = src[0, bytes): one read and one write per byte */
+} snac_probe_kind;
+
+/*
+ * snac_hbm_probe -- a measurement helper, not one of the collectives and
+ * not from the pages: the plainest HBM stream of one kind, to measure on
+ * the machine at hand the ceilings the collective kernels are judged
+ * against (read-only, write-only and 1:1 read/write rates).  It uses the
+ * collectives' access primitives: 16-byte buffer loads and stores with the
+ * streaming hint over grid-stride tiles of `tile_bytes` per workgroup
+ * iteration, `wgs_per_cu` workgroups per CU of `threads` threads.
+ *   kind        SNAC_PROBE_READ, _WRITE or _COPY
+ *   dst         WRITE/COPY: output of `bytes`; READ: a 4-byte sink written
+ *               only if the XOR of every word read equals `magic`
+ *   src         READ/COPY: input of `bytes`; WRITE: unused (may be NULL)
+ *   bytes       multiple of 16; dst and src 16-byte aligned; 0 is a no-op
+ *   threads     64 or 256;  tile_bytes  4096 or 16384;  wgs_per_cu  1..32
+ *   magic       WRITE: the 32-bit word written; READ: see dst
+ * Asynchronous on `stream`; SNAC_E_ARG for anything else.  No context.
+ */
+snac_status snac_hbm_probe(int kind, void* dst, const void* src, size_t bytes, int threads, int tile_bytes,
+                           int wgs_per_cu, uint32_t magic, snac_stream stream);
+
 /* ----------------------------------------------------------- collectives
  *
  * Every collective takes ctx (which fixes N = snac_ctx_nranks(ctx)), an array

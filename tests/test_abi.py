@@ -78,6 +78,26 @@ def test_argument_errors_without_gpu():
     snac.snac_finalize(None)
 
 
+def test_probe_argument_errors_without_gpu():
+    E = snac.SNAC_E_ARG
+
+    def p(kind, dst, src, nbytes, threads=64, tile=4096, wgs=4):
+        return lambda: snac.snac_hbm_probe(kind, dst, src, nbytes, threads, tile, wgs)
+
+    _expect(E, p(7, 0x1000, 0x2000, 16))                 # unknown kind
+    _expect(E, p("copy", 0x1000, 0x2000, 16, threads=128))  # workgroup size
+    _expect(E, p("copy", 0x1000, 0x2000, 16, tile=8192))    # tile
+    _expect(E, p("copy", 0x1000, 0x2000, 16, wgs=0))
+    _expect(E, p("copy", 0x1000, 0x2000, 16, wgs=33))
+    _expect(E, p("copy", 0x1000, 0x2000, 17))            # not whole 16-byte units
+    _expect(E, p("copy", 0x1008, 0x2000, 16))            # misaligned dst
+    _expect(E, p("read", 0x1000, 0x2004, 16))            # misaligned src
+    _expect(E, p("copy", 0x1000, 0x1010, 64))            # overlap
+    _expect(E, p("write", 0, None, 16))                  # no dst
+    _expect(E, p("read", 0x1000, None, 16))              # no src
+    p("copy", 0, 0, 0)()                                 # nothing to do
+
+
 def test_tuning_roundtrip_and_ranges():
     t0 = snac.snac_get_tuning()
     try:
