@@ -131,6 +131,7 @@ _SIGS = {
     "snac_reduce_n": (_I, [ctypes.POINTER(_VP), _I, ctypes.POINTER(_VP), _I, _SZ, _I, _VP]),
     "snac_all_reduce": (_I, [_VP, ctypes.POINTER(_VP), ctypes.POINTER(_VP), _SZ, _I, _VP]),
     "snac_all_reduce_ex": (_I, [_VP, ctypes.POINTER(_VP), ctypes.POINTER(_VP), _SZ, _I, _I, _VP]),
+    "snac_all_reduce_atomic_static": (_I, [_I, ctypes.POINTER(_VP), ctypes.POINTER(_VP), _SZ, _I, _VP]),
     "snac_reduce_scatter": (_I, [_VP, ctypes.POINTER(_VP), ctypes.POINTER(_VP), _SZ, _I, _VP]),
     "snac_all_gather": (_I, [_VP, ctypes.POINTER(_VP), ctypes.POINTER(_VP), _SZ, _I, _VP]),
     "snac_all_to_all": (_I, [_VP, ctypes.POINTER(_VP), ctypes.POINTER(_VP), _SZ, _I, _VP]),
@@ -327,6 +328,16 @@ def snac_all_reduce_ex(ctx, srcs, dsts, nbytes, dtype, mode, stream=None):
                                     _rank_ptrs(ctx, dsts, "snac_all_reduce_ex dsts"), nbytes, _dtype(dtype), m,
                                     _stream(stream)),
            "snac_all_reduce_ex")
+
+
+def snac_all_reduce_atomic_static(srcs, dsts, nbytes, dtype, stream=None):
+    """The context-free, allocation-free atomic AllReduce over len(srcs) ranks."""
+    srcs, dsts = list(srcs), list(dsts)
+    if len(srcs) != len(dsts):
+        raise ValueError(f"snac_all_reduce_atomic_static: {len(srcs)} sources but {len(dsts)} destinations")
+    _check(lib().snac_all_reduce_atomic_static(len(srcs), _ptrs(srcs), _ptrs(dsts), nbytes, _dtype(dtype),
+                                               _stream(stream)),
+           "snac_all_reduce_atomic_static")
 
 
 def snac_reduce_scatter(ctx, srcs, dsts, nbytes, dtype, stream=None):

@@ -28,7 +28,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsnac.so")
-SOURCES = ["api.hip", "collectives.hip", "pipeline.hip", "probes.hip"]
+SOURCES = ["api.hip", "collectives.hip", "pipeline.hip", "probes.hip", "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 

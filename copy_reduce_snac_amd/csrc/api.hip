@@ -714,6 +714,36 @@ snac_status snac_all_reduce_ex(snac_ctx* ctx, const void* const* src, void* cons
   return ok();
 }
 
+snac_status snac_all_reduce_atomic_static(int nranks, const void* const* src, void* const* dst, size_t bytes,
+                                          snac_dtype dtype, snac_stream stream) {
+  if (nranks < 1 || nranks > SNAC_MAX_RANKS) return fail(SNAC_E_ARG, "nranks %d outside 1..%d", nranks, SNAC_MAX_RANKS);
+  if (!is_float(dtype)) return fail(SNAC_E_ARG, "reductions need SNAC_F32 or SNAC_BF16");
+  const uint64_t e = (uint64_t)esize_of(dtype);
+  const uint64_t max_elems = kStaticScratchBytes / sizeof(float);
+  if (bytes / e > max_elems)
+    return fail(SNAC_E_ARG,
+                "%zu bytes per rank need a %llu-element accumulator; the static scratch holds %llu elements "
+                "(%llu MiB)",
+                bytes, (unsigned long long)(bytes / e), (unsigned long long)max_elems,
+                (unsigned long long)(kStaticScratchBytes >> 20));
+  // validate exactly as the AllReduce does, without launching
+  snac_coll_desc d;
+  g_describe = &d;
+  snac_status st = fixed_collective_n(kAllReduce, nranks, src, dst, bytes, dtype, stream);
+  g_describe = nullptr;
+  if (st != SNAC_OK) return st;
+  if (bytes == 0) return ok();
+  float* acc = nullptr;
+  hipError_t he = static_scratch(&acc);
+  if (he != hipSuccess) return hip_fail(he, "static scratch address");
+  bool vec = true;
+  for (int i = 0; i < d.nsrc; ++i)
+    if (((uintptr_t)d.src[i] | (uintptr_t)d.dst[i]) & 15u) vec = false;
+  he = launch_atomic_allreduce(d, acc, 0, bytes / e, vec, (hipStream_t)stream);
+  if (he != hipSuccess) return hip_fail(he, "atomic all-reduce launch");
+  return ok();
+}
+
 snac_status snac_reduce_scatter(snac_ctx* ctx, const void* const* src, void* const* dst, size_t bytes,
                                 snac_dtype dtype, snac_stream stream) {
   return fixed_collective(kReduceScatter, ctx, src, dst, bytes, dtype, stream);

@@ -109,6 +109,12 @@ hipError_t fill_u64(uint64_t* p, uint64_t n, uint64_t v, hipStream_t stream);
 
 int device_cu_count();
 
+// The static device array of snac_all_reduce_atomic_static (noalloc.hip):
+// its size, and its address on the current device (looked up once per
+// device with hipGetSymbolAddress, then kept).
+constexpr uint64_t kStaticScratchBytes = 32ull << 20;
+hipError_t static_scratch(float** out);
+
 // HBM ceiling probes (probes.hip): kind 0 read, 1 write, 2 copy.
 hipError_t launch_probe(int kind, void* dst, const void* src, uint64_t bytes, int threads, int tile_bytes,
                         int wgs_per_cu, uint32_t magic, hipStream_t stream);

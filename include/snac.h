@@ -305,6 +305,27 @@ snac_status snac_all_reduce_ex(snac_ctx* ctx, const void* const* src, void* cons
                                snac_dtype dtype, snac_reduce_mode mode, snac_stream stream);
 
 /*
+ * snac_all_reduce_atomic_static -- for callers that cannot allocate (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): snac_all_reduce_ex(..., SNAC_REDUCE_ATOMIC, ...) without a
+ * context, allocating nothing.  Its binary32 accumulator is a static device
+ * array of 32 MiB inside the library, so a message may have at most 2^23
+ * elements per rank (16 MiB of bf16, 32 MiB of f32); a larger one is
+ * SNAC_E_ARG and nothing is enqueued.
+ *   nranks  1..SNAC_MAX_RANKS: the length of src[] and dst[]
+ *   src, dst, bytes, dtype, stream, in-place rule, result bounds:
+ *           as snac_all_reduce_ex in SNAC_REDUCE_ATOMIC mode
+ * Every call on one GPU uses that GPU's one array (each call clears the
+ * accumulator with a kernel before using it), so calls that overlap on the
+ * same GPU -- on different streams, or from different host threads -- race
+ * and their results are undefined; calls in stream order do not.  The first
+ * call on a device looks up the array's address there (hipGetSymbolAddress)
+ * and keeps it; no call allocates memory.
+ */
+snac_status snac_all_reduce_atomic_static(int nranks, const void* const* src, void* const* dst, size_t bytes,
+                                          snac_dtype dtype, snac_stream stream);
+
+/*
  * snac_reduce_scatter -- dst[r] (bytes/N) receives the reduction of chunk r
  * of every src, dim 0 split into N equal contiguous chunks (NKI
  * reduce_scatter_hbm_kernel).  `bytes` is the per-rank input size and must

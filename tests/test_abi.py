@@ -98,6 +98,22 @@ def test_probe_argument_errors_without_gpu():
     p("copy", 0, 0, 0)()                                 # nothing to do
 
 
+def test_static_atomic_allreduce_argument_errors_without_gpu():
+    """The allocation-free AllReduce checks its arguments, its size limit
+    included, before it touches the device."""
+    E = snac.SNAC_E_ARG
+    f = snac.snac_all_reduce_atomic_static
+    _expect(E, f, [0x1000] * 17, [0x100000 * (i + 1) for i in range(17)], 64, "f32")   # too many ranks
+    _expect(E, f, [0x1000, 0x2000], [0x3000, 0x4000], 64, "u32")                       # not a float type
+    msg = _expect(E, f, [0x1000, 0x2000], [0x3000, 0x4000], ((1 << 23) + 1) * 4, "f32")  # past the scratch
+    assert "static scratch" in msg
+    _expect(E, f, [0x1000, 0x2000], [0x3000, 0x4000], 6, "f32")                        # not whole elements
+    _expect(E, f, [0x1000, 0x1000], [0x3000, 0x3000], 64, "f32")                       # destinations overlap
+    with pytest.raises(ValueError):
+        f([0x1000], [0x3000, 0x4000], 64, "f32")
+    f([0, 0], [0, 0], 0, "bf16")  # nothing to do
+
+
 def test_tuning_roundtrip_and_ranges():
     t0 = snac.snac_get_tuning()
     try:
