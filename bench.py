@@ -745,17 +745,23 @@ ONLY = {
 # reports), its algorithmic bytes per launch, and the source set its
 # counters are tied to.
 PROFILED = {
-    "allreduce": (r"snac::reduce_kernel<8, snac::BF16", 2 * N * 256 * MiB, "collectives"),
-    "copy": (r"snac::copy_kernel", 2 * GiB, "collectives"),
-    "rs": (r"snac::reduce_kernel<8, snac::BF16", N * 128 * MiB + 128 * MiB, "collectives"),
-    "ag": (r"snac::copy_kernel", 128 * MiB + N * 128 * MiB, "collectives"),
-    "ag_cold": (r"snac::copy_kernel", 128 * MiB + N * 128 * MiB, "collectives"),
-    "a2a": (r"snac::copy_kernel", 2 * N * 128 * MiB, "collectives"),
-    "a2av": (r"snac::copy_kernel", 2 * N * 128 * MiB, "collectives"),
-    "agv": (r"snac::copy_kernel", 128 * MiB + N * 128 * MiB, "collectives"),
-    "rsv": (r"snac::reduce_kernel<8, snac::F32", N * 128 * MiB + 128 * MiB, "collectives"),
-    "pipeline_bf16": (r"snac::pipeline_kernel<snac::BF16, 8>", 3 * N * 64 * MiB + 64 * MiB, "pipeline"),
-    "pipeline_f32": (r"snac::pipeline_kernel<snac::F32, 8>", 3 * N * 128 * MiB + 128 * MiB, "pipeline"),
+    "allreduce": (r"snac::reduce_kernel<8, snac::BF16", 2 * N * 256 * MiB, "collectives",
+                  "allreduce_bf16_n8_256mib"),
+    "copy": (r"snac::copy_kernel", 2 * GiB, "collectives", "copy_1gib"),
+    "rs": (r"snac::reduce_kernel<8, snac::BF16", N * 128 * MiB + 128 * MiB, "collectives",
+           "reduce_scatter_bf16_n8_32768x2048"),
+    "ag": (r"snac::copy_kernel", 128 * MiB + N * 128 * MiB, "collectives", "all_gather_bf16_n8_4096x2048_in_reused"),
+    "ag_cold": (r"snac::copy_kernel", 128 * MiB + N * 128 * MiB, "collectives",
+                "all_gather_bf16_n8_4096x2048_in_evicted"),
+    "a2a": (r"snac::copy_kernel", 2 * N * 128 * MiB, "collectives", "all_to_all_u32_n8_128mib"),
+    "a2av": (r"snac::copy_kernel", 2 * N * 128 * MiB, "collectives", "all_to_all_v_u32_n8_128mib"),
+    "agv": (r"snac::copy_kernel", 128 * MiB + N * 128 * MiB, "collectives", "all_gather_v_u32_n8_128mib"),
+    "rsv": (r"snac::reduce_kernel<8, snac::F32", N * 128 * MiB + 128 * MiB, "collectives",
+            "reduce_scatter_v_f32_n8_128mib"),
+    "pipeline_bf16": (r"snac::pipeline_kernel<snac::BF16, 8>", 3 * N * 64 * MiB + 64 * MiB, "pipeline",
+                      "snac_pipeline_bf16_n8_4096x8192"),
+    "pipeline_f32": (r"snac::pipeline_kernel<snac::F32, 8>", 3 * N * 128 * MiB + 128 * MiB, "pipeline",
+                     "snac_pipeline_f32_n8_4096x8192"),
 }
 
 # counter passes (one rocprofv3 --pmc run each) and what each holds
@@ -789,16 +795,47 @@ def _csv_means(dirpath: str, kernel_re: str) -> dict:
     return out
 
 
+def _trace_rows(dirpath: str) -> list:
+    """The rows of a rocprofv3 --stats kernel summary under dirpath."""
+    import csv
+
+    rows = []
+    for path in glob.glob(os.path.join(dirpath, "**", "*kernel_stats.csv"), recursive=True):
+        rows.extend(csv.DictReader(open(path)))
+    return rows
+
+
 def _trace_stats(dirpath: str, kernel_re: str):
     """(name, calls, average ns) of the kernel matching kernel_re in a
     rocprofv3 --stats kernel summary under dirpath."""
-    import csv
-
-    for path in glob.glob(os.path.join(dirpath, "**", "*kernel_stats.csv"), recursive=True):
-        for r in csv.DictReader(open(path)):
-            if re.search(kernel_re, r["Name"]):
-                return r["Name"], int(r["Calls"]), float(r["AverageNs"])
+    for r in _trace_rows(dirpath):
+        if re.search(kernel_re, r["Name"]):
+            return r["Name"], int(r["Calls"]), float(r["AverageNs"])
     return None
+
+
+def _short(name: str) -> str:
+    """A kernel name without its return type, anonymous namespaces and
+    parameter list."""
+    name = name.replace("void ", "").replace("(anonymous namespace)::", "")
+    if name.endswith(")"):
+        depth = 0
+        for i in range(len(name) - 1, -1, -1):
+            depth += {")": 1, "(": -1}.get(name[i], 0)
+            if depth == 0:
+                name = name[:i]
+                break
+    return name if len(name) <= 72 else name[:69] + "..."
+
+
+def trace_table(dirpath: str, top: int = 6) -> list[str]:
+    rows = sorted(_trace_rows(dirpath), key=lambda r: -float(r["TotalDurationNs"]))[:top]
+    out = ["| kernel | calls | average (ns) | min (ns) | max (ns) | stddev (ns) | share |",
+           "|---|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | "
+                   f"{r['MaxNs']} | {float(r['StdDev']):.0f} | {float(r['Percentage']):.2f} % |")
+    return out
 
 
 def summarize(workload: str, root: str, commands: list[str]) -> str:
@@ -806,7 +843,7 @@ def summarize(workload: str, root: str, commands: list[str]) -> str:
     under root/<pass>_<workload> (counter passes) and root/trace_<workload>
     (kernel trace), with the copy passes under root/<pass>_copy as the
     calibration of the FETCH_SIZE and WRITE_SIZE derived counters."""
-    kre, alg, srcs = PROFILED[workload]
+    kre, alg, srcs, stem = PROFILED[workload]
     m = {p: _csv_means(os.path.join(root, f"{p}_{workload}"), kre) for p in PMC_PASSES}
     cal = {p: _csv_means(os.path.join(root, f"{p}_copy"), PROFILED["copy"][0]) for p in ("fetch", "write")}
     kernel = next((v["_kernel"] for v in m.values() if v.get("_kernel")), kre)
@@ -819,13 +856,28 @@ def summarize(workload: str, root: str, commands: list[str]) -> str:
     fetch_kib, write_kib = m["fetch"]["FETCH_SIZE"], wr["WRITE_SIZE"]
     cal_fetch = GiB / (1024 * cal["fetch"]["FETCH_SIZE"])
     cal_write = GiB / (1024 * cal["write"]["WRITE_SIZE"])
-    tr = _trace_stats(os.path.join(root, f"trace_{workload}"), kre)
-    L = [f"# {workload}: HBM traffic and L2 behaviour of its dominant kernel from rocprofv3 counters", "",
-         f"Kernel: `{kernel}`.  Each figure is the mean over its {m['rdsize']['_dispatches']} profiled dispatches; "
-         "every counter pass is its own run of the same command on the same box.", ""]
+    # the hash of the sources the run used, recorded on the GPU machine next to
+    # its output (else the current tree's)
+    hp = os.path.join(root, "source_hashes.json")
+    run_hash = json.load(open(hp))[srcs] if os.path.exists(hp) else source_hash(SOURCE_SETS[srcs])
+    tdir = os.path.join(root, f"trace_{workload}")
+    tr = _trace_stats(tdir, kre)
+    L = [f"# `bench.py --only {workload}` ({stem}): kernel trace, HBM traffic and L2 behaviour from rocprofv3", "",
+         f"Dominant kernel: `{_short(kernel or kre)}`, {alg} algorithmic bytes per launch.  Every run below is "
+         "its own process on the same box, in the same session.", ""]
     if tr:
-        L += [f"Kernel trace (`--kernel-trace --stats`): {tr[1]} calls, average {tr[2] / 1e3:.1f} us "
-              f"= {alg / tr[2]:.0f} GB/s of algorithmic bytes.", ""]
+        L += ["Kernel trace (`--kernel-trace --stats`, 20 timed calls after 5 warm-up calls):", ""]
+        L += trace_table(tdir) + [""]
+        L += [f"Average duration of the dominant kernel: {tr[2] / 1e3:.1f} us = **{alg / tr[2]:.0f} GB/s** of "
+              f"algorithmic bytes ({alg / tr[2] / PEAK_GBPS:.3f} of 8 TB/s).", ""]
+        tj = os.path.join(root, f"time_{workload}.json")
+        if os.path.exists(tj):
+            t = json.load(open(tj))
+            if isinstance(t, list):
+                t = t[0]
+            L += [f"Same box, same command without the profiler (HIP events on the launch stream, "
+                  f"`python3 bench.py --only {workload}`): {t['ms_per_call']} ms per call, {t['hbm_GBps']} GB/s; "
+                  f"the trace's average is {100 * (tr[2] / 1e6 / t['ms_per_call'] - 1):+.1f} % from it.", ""]
     L += ["Commands, from the repository root on the GPU box (`REPO=$PWD`; one run per pass):", ""]
     L += [f"    {c}" for c in commands] + [""]
     L += ["Bytes by request size (gfx950 has a counter per EA read size; the `FETCH_SIZE` expression counts "
@@ -834,7 +886,7 @@ def summarize(workload: str, root: str, commands: list[str]) -> str:
     for k, b in (("TCC_EA0_RDREQ_32B_sum", 32), ("TCC_EA0_RDREQ_64B_sum", 64), ("TCC_EA0_RDREQ_128B_sum", 128)):
         L.append(f"| {k} | {rd[k]:.1f} | {rd[k] * b:.0f} |")
     L += [f"| TCC_BUBBLE_sum | {rd['TCC_BUBBLE_sum']:.1f} | |",
-          f"| TCC_EA0_WRREQ_sum (64-byte: {w64:.1f}) | {wreq:.1f} | {write_bytes:.0f} |", "",
+          f"| TCC_EA0_WRREQ_sum ({w64:.1f} of them 64-byte) | {wreq:.1f} | {write_bytes:.0f} |", "",
           f"Read {read_bytes:.0f} B + written {write_bytes:.0f} B = **{traffic:.0f} B per launch**, "
           f"**{traffic / alg:.5f} x** the algorithmic {alg} B.", "",
           "Derived counters, and the calibration a plain 1 GiB copy gives them (`bench.py --only copy`):", "",
@@ -842,7 +894,7 @@ def summarize(workload: str, root: str, commands: list[str]) -> str:
           f"| FETCH_SIZE | {fetch_kib:.1f} | {cal_fetch:.4f} | {fetch_kib * 1024 * cal_fetch:.0f} |",
           f"| WRITE_SIZE | {write_kib:.1f} | {cal_write:.4f} | {write_kib * 1024 * cal_write:.0f} |", "",
           f"L2 (TCC): {l2['TCC_HIT_sum']:.0f} hits, {l2['TCC_MISS_sum']:.0f} misses per dispatch, hit rate "
-          f"**{hit:.3f}**.", ""]
+          f"**{hit:.3f}** (a streamed 128-byte line is one miss and one hit: two 64-byte requests).", ""]
     if m["stall"].get("_dispatches"):
         st = m["stall"]
         L += ["Stall and latency counters (sums over TCC / TCP instances, per dispatch):", "",
@@ -851,20 +903,78 @@ def summarize(workload: str, root: str, commands: list[str]) -> str:
         L += [f"| {k} | {v:.0f} |" for k, v in m["utcl1"].items() if not k.startswith("_")]
         if rd.get("TCC_EA0_RDREQ_32B_sum") is not None and st.get("TCC_EA0_RDREQ_LEVEL_sum"):
             nreq = rd["TCC_EA0_RDREQ_32B_sum"] + rd["TCC_EA0_RDREQ_64B_sum"] + rd["TCC_EA0_RDREQ_128B_sum"]
-            L.append(f"| mean EA read requests in flight x cycles / requests (read latency, cycles) | "
+            L.append(f"| mean EA read latency: RDREQ_LEVEL / read requests (cycles) | "
                      f"{st['TCC_EA0_RDREQ_LEVEL_sum'] / max(1.0, nreq):.0f} |")
-            L.append(f"| mean write latency proxy: WRREQ_LEVEL / WRREQ (cycles) | "
+            L.append(f"| mean EA write latency: WRREQ_LEVEL / write requests (cycles) | "
                      f"{st['TCC_EA0_WRREQ_LEVEL_sum'] / max(1.0, wreq):.0f} |")
         L.append("")
     L += ["Machine-readable (read by bench.py; the hash is of the kernel sources the counters were taken with):", "",
           f"- workload: `{workload}`", f"- sources: `{srcs}`",
-          f"- kernel_source_hash: `{source_hash(SOURCE_SETS[srcs])}`",
+          f"- kernel_source_hash: `{run_hash}`",
           f"- traffic_bytes_per_launch: `{traffic:.0f}`", f"- read_bytes_per_launch: `{read_bytes:.0f}`",
           f"- write_bytes_per_launch: `{write_bytes:.0f}`", f"- algorithmic_bytes_per_launch: `{alg}`",
           f"- l2_hit: `{hit:.4f}`", f"- fetch_size_copy_calibration: `{cal_fetch:.4f}`",
           f"- write_size_copy_calibration: `{cal_write:.4f}`"]
     if tr:
         L.append(f"- kernel_average_ns: `{tr[2]:.0f}`")
+    return "\n".join(L) + "\n"
+
+
+def summarize_headline(root: str, commands: list[str]) -> str:
+    """profiles/ summary of the headline command under the kernel trace
+    (root/trace_headline), set against the default run's line from the same
+    session (root/bench_line.json)."""
+    line = json.load(open(os.path.join(root, "bench_line.json")))
+    hp = os.path.join(root, "source_hashes.json")
+    run_hash = json.load(open(hp))["collectives"] if os.path.exists(hp) else kernel_source_hash()
+    tdir = os.path.join(root, "trace_headline")
+    _, calls, avg = _trace_stats(tdir, PROFILED["allreduce"][0])
+    alg = PROFILED["allreduce"][1]
+    r = line["roofline"]
+    L = ["# The headline command under rocprofv3: AllReduce bf16, N = 8, 256 MiB per rank", "",
+         "The benchmark's headline path as the default run executes it, without the other workloads "
+         "(`--no-extra`): 25 eager calls (5 warm-up, 20 timed with events), then 26 one-call HIP graph replays, "
+         "all at 256 MiB per rank.", "", "Command (from the repository root on the GPU box, `REPO=$PWD`):", ""]
+    L += [f"    {c}" for c in commands] + [""]
+    L += trace_table(tdir) + [""]
+    L += [f"Average duration of `reduce_kernel<8, snac::BF16, ...>`: {avg / 1e3:.1f} us over {calls} launches = "
+          f"**{alg / avg:.0f} GB/s** of algorithmic bytes (2 * 8 * 256 MiB per launch), "
+          f"{alg / avg / PEAK_GBPS:.3f} of 8 TB/s.", "",
+          f"Same box, same session, `python3 bench.py` (the default run, no profiler): `ms_per_step` "
+          f"{line['ms_per_step']} ms, `value` {line['value']} GB/s, `graph_median_ms` {line.get('graph_median_ms')} ms; "
+          f"the trace's average kernel duration is {100 * (avg / 1e6 / line['ms_per_step'] - 1):+.1f} % from "
+          "`ms_per_step`.", ""]
+    if "copy_ceiling_GBps" in r:
+        L += [f"Same-run ceiling (`roofline` of that line): copy {r['copy_ceiling_GBps']} GB/s; the AllReduce is at "
+              f"{r['frac_of_copy_ceiling']} of it and {r['frac']} of 8 TB/s.", ""]
+    L += [f"Kernel source hash (collectives): `{run_hash}`."]
+    return "\n".join(L) + "\n"
+
+
+def summarize_ceilings(root: str, commands: list[str]) -> str:
+    """profiles/ summary of `bench.py --only ceilings` (root/ceilings.json)
+    and its kernel trace (root/trace_ceilings)."""
+    c = json.load(open(os.path.join(root, "ceilings.json")))
+    hp = os.path.join(root, "source_hashes.json")
+    run_hash = json.load(open(hp))["probes"] if os.path.exists(hp) else source_hash(SOURCE_SETS["probes"])
+    L = ["# HBM ceilings of one MI355X: read-only, write-only and 1:1 copy streams of 1 GiB", "",
+         "`snac_hbm_probe` streams with the collectives' access primitives (16-byte buffer loads and stores with the "
+         "streaming hint, grid-stride tiles) at each launch shape; 20 timed calls after 5 warm-up calls, HIP events. "
+         "Bandwidth counts the bytes each stream must move (copy: read + written).", "",
+         "Commands (from the repository root on the GPU box, `REPO=$PWD`):", "",
+         "    python3 $REPO/bench.py --only ceilings"]
+    L += [f"    {x}" for x in commands] + ["",
+          "| probe | threads | tile (B) | WGs per CU | ms per call | GB/s |", "|---|---|---|---|---|---|"]
+    for r in c["shapes"]:
+        L.append(f"| {r['probe']} | {r['threads']} | {r['tile_bytes']} | {r['wgs_per_cu']} | {r['ms_per_call']} | "
+                 f"{r['GBps']} |")
+    L += ["", "Best shape of each kind (the ceiling on this box):", "", "| stream | GB/s | of 8 TB/s | shape |",
+          "|---|---|---|---|"]
+    for k in ("read", "write", "copy"):
+        L.append(f"| {k} | {c[k + '_GBps']} | {c[k + '_frac_of_peak']} | {c[k + '_shape']} |")
+    L += ["", "Kernel trace of the same command under the profiler (probe_kernel<kind, threads, tile>; "
+          "kind 0 read, 1 write, 2 copy):", ""]
+    L += trace_table(os.path.join(root, "trace_ceilings"), top=24) + ["", f"Kernel source hash (probes): `{run_hash}`."]
     return "\n".join(L) + "\n"
 
 
@@ -895,14 +1005,23 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--summarize", default=None, metavar="WORKLOAD",
-                    help="write profiles/WORKLOAD_counters.md from the rocprofv3 output under --prof-dir")
+                    help="write the profiles/ summary of WORKLOAD (a --only name, 'headline' or 'ceilings') from "
+                         "the rocprofv3 output under --prof-dir")
     ap.add_argument("--prof-dir", default=os.path.join(ROOT, "gpurun_out", "prof"))
     ap.add_argument("--commands", default=None, help="file listing the rocprofv3 commands that made --prof-dir")
     args = ap.parse_args()
     if args.summarize:
         cmds = open(args.commands).read().splitlines() if args.commands else []
-        text = summarize(args.summarize, args.prof_dir, [c for c in cmds if c.strip()])
-        dest = os.path.join(PROFILES, f"{args.summarize}_counters.md")
+        cmds = [c for c in cmds if c.strip()]
+        if args.summarize == "headline":
+            text = summarize_headline(args.prof_dir, cmds)
+            dest = os.path.join(PROFILES, "allreduce_bf16_n8_256mib_headline_kernel_trace.md")
+        elif args.summarize == "ceilings":
+            text = summarize_ceilings(args.prof_dir, cmds)
+            dest = os.path.join(PROFILES, "hbm_ceilings_1gib.md")
+        else:
+            text = summarize(args.summarize, args.prof_dir, cmds)
+            dest = os.path.join(PROFILES, f"{PROFILED[args.summarize][3]}_counters.md")
         with open(dest, "w", encoding="utf-8") as f:
             f.write(text)
         print(dest)

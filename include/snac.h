@@ -78,10 +78,11 @@ typedef struct snac_ctx snac_ctx;
 
 /*
  * snac_coll_desc -- one collective call, validated and laid out: what the
- * collective kernels take as their argument, and what a user kernel passes
- * to snac::collective() (include/snac_device.hpp) to run the same
- * collective inside its own grid.  Filled by snac_describe(); plain data, so
- * it can be copied into a kernel argument by value (2336 bytes).
+ * collective kernels take as their argument, and what a user kernel points
+ * to from the snac_args it passes to snac::collective()
+ * (include/snac_device.hpp) to run the same collective inside its own grid.
+ * Filled by snac_describe(); plain data, so it can be copied into a kernel
+ * argument by value (2336 bytes).
  */
 #define SNAC_MAX_COUNTS (SNAC_MAX_RANKS * SNAC_MAX_RANKS)
 #define SNAC_DESC_ALIGNED 1 /* flags: every job's addresses and length are 16-byte aligned */

@@ -1,12 +1,13 @@
 // snac_layout.hpp -- the layout engine: a collective -> a list of copy or
 // reduce jobs over byte ranges.
 //
-// "Layouts describe the collective: how inputs and outputs are distributed,
-// and whether to copy or reduce" (Purlin 0.6.4 project description, "Key
-// Idea").  The same functions run on the host (snac_plan, argument checks)
-// and in every workgroup of a collective kernel, which rebuilds the job table
-// in LDS from the compact descriptor (snac_coll_desc, include/snac.h) passed
-// as a kernel argument -- so no per-call host-to-device copy is needed.
+// In Purlin 0.6.4 (project description, "Key Idea") a layout is what defines
+// a collective: where its inputs and outputs sit across the ranks and which
+// of the two Atoms, copy or reduce, moves each part.  The same functions run
+// on the host (snac_plan, argument checks) and in every workgroup of a
+// collective kernel, which rebuilds the job table in LDS from the compact
+// descriptor (snac_coll_desc, include/snac.h) passed as a kernel argument --
+// so no per-call host-to-device copy is needed.
 //
 // Per-collective layouts (N ranks, B per-rank input bytes, e element size,
 // D(c) exclusive prefix sum of counts, every offset in bytes):
