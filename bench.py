@@ -24,7 +24,10 @@ the counter figures of its own summary when valid:
   * the HBM ceilings (read-only, write-only, 1:1 copy probes);
   * the AllReduce sweep, 1 KiB .. 1 GiB per rank, and the AllGather sweep,
     128 B .. 128 MiB in per rank, each size the median over 20 runs of a
-    HIP graph of 10 calls (1 call from 64 MiB per rank up).
+    HIP graph of 10 calls (1 call from 64 MiB per rank up).  A row is
+    cache_resident when its whole working set fits the 256 MB Infinity
+    Cache, inputs_cache_resident when its inputs do (so that replays read
+    them from there).
 
 Per collective, in the argument form of the pages' benchmark binaries:
 
@@ -387,10 +390,12 @@ def sweep_rows(env: Env, coll: str, lo: int, hi: int, graph_launches: int | None
             K = graph_launches if graph_launches else (10 if B < 64 * MiB else 1)
             t = env.graph_median(sw.call_for(B), batch=K, runs=runs, warmup=warmup)
             alg = spec["alg"](B, n)
+            inputs = n * (B if coll != "all_gather_v" else B // n)
             r = result(f"{coll} {dtype} N={n} {B} B/rank", t, alg, spec["total"](B, n), collective=coll,
                        dtype=dtype, nranks=n, bytes_per_rank=B,
                        timing=f"median over {runs} runs of a HIP graph of {K} calls",
-                       cache_resident=bool(alg < INFINITY_CACHE), seed=seed)
+                       cache_resident=bool(alg < INFINITY_CACHE),
+                       inputs_cache_resident=bool(inputs < INFINITY_CACHE), seed=seed)
             rows.append(r)
             if emit:
                 print(json.dumps(r), flush=True)
