@@ -285,7 +285,10 @@ template <typename T, int N>
 __global__ __launch_bounds__(kThreads) void pipeline_kernel(const PipeArgs a) {
   __shared__ uint32_t s_item;
   __shared__ uint32_t s_ok;
-  const uint64_t epoch = uniform64(ld_relaxed(&a.ctrl[kCtrlEpoch]));
+  // The epoch load is issued here and read only after the first ticket has
+  // come back, so the two round trips to memory overlap: at small messages
+  // every workgroup's start is on the call's critical path.
+  const uint64_t epoch_word = ld_relaxed(&a.ctrl[kCtrlEpoch]);
   const uint32_t Q = a.queues;
   const uint32_t S = a.qslots;
   const uint32_t q = uniform(blockIdx.x % Q);
@@ -294,18 +297,12 @@ __global__ __launch_bounds__(kThreads) void pipeline_kernel(const PipeArgs a) {
   const uint32_t L = uniform(a.lookahead < qtiles ? a.lookahead : qtiles);
   const uint32_t items = uniform((qtiles + L) * (uint32_t)(2 * N));
   uint64_t* ticket = &a.ctrl[kCtrlTicket + q * kFlagStride];
+  if (threadIdx.x == 0)
+    s_item = (uint32_t)__hip_atomic_fetch_add(ticket, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const uint64_t epoch = uniform64(epoch_word);
+  uint32_t item = uniform(s_item);
   for (;;) {
-    // The barrier at the top closes the previous item's single-lane flag
-    // store before the next single-lane ticket fetch; without it the
-    // compiler may thread the two lane-0 regions into one back edge that
-    // the other lanes skip, so that the lanes of a wave meet the barriers
-    // below on different iterations.  It also keeps s_item from being
-    // overwritten before every wave has read it.
-    __syncthreads();
-    if (threadIdx.x == 0)
-      s_item = (uint32_t)__hip_atomic_fetch_add(ticket, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    const uint32_t item = uniform(s_item);
     if (item >= items) break;
     const uint32_t g = uniform(item / (uint32_t)(2 * N));
     const uint32_t w = uniform(item - g * (uint32_t)(2 * N));
@@ -315,6 +312,17 @@ __global__ __launch_bounds__(kThreads) void pipeline_kernel(const PipeArgs a) {
       const uint32_t gc = g - L;
       consume_item<T, N>(a, gc * Q + q, uniform(q * S + gc % S), uniform(gc / S), w - (uint32_t)N, epoch, &s_ok);
     }
+    // The barrier before the next ticket closes the item's single-lane flag
+    // store before the next single-lane ticket fetch; without it the
+    // compiler may thread the two lane-0 regions into one back edge that
+    // the other lanes skip, so that the lanes of a wave meet the barriers
+    // on different iterations.  It also keeps s_item from being overwritten
+    // before every wave has read it.
+    __syncthreads();
+    if (threadIdx.x == 0)
+      s_item = (uint32_t)__hip_atomic_fetch_add(ticket, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    item = uniform(s_item);
   }
   // Completion, counted per queue first (each queue's workgroups hit their
   // own counter; a same-address atomic costs ~12 ns, so one global counter
@@ -332,11 +340,18 @@ __global__ __launch_bounds__(kThreads) void pipeline_kernel(const PipeArgs a) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       __hip_atomic_store(ticket, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(qdone, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const uint64_t old =
-          __hip_atomic_fetch_add(&a.ctrl[kCtrlDone], (uint64_t)1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-      if (old == (uint64_t)Q - 1) {
-        __hip_atomic_store(&a.ctrl[kCtrlDone], (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (Q == 1) {
+        // the only queue: its last workgroup is the grid's last, and the
+        // global count (one more round trip at the end of a small call)
+        // is not needed
         __hip_atomic_store(&a.ctrl[kCtrlEpoch], epoch + a.rounds, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        const uint64_t old =
+            __hip_atomic_fetch_add(&a.ctrl[kCtrlDone], (uint64_t)1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        if (old == (uint64_t)Q - 1) {
+          __hip_atomic_store(&a.ctrl[kCtrlDone], (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(&a.ctrl[kCtrlEpoch], epoch + a.rounds, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
     }
   }
