@@ -343,6 +343,27 @@ def test_pipeline_alternating_inputs():
         snac.snac_finalize(ctx)
 
 
+def test_pipeline_alternating_queue_counts():
+    """Calls of one tile (one queue, which finishes without the global done
+    count) alternating with calls over several queues, back to back on one
+    context: every output checked, so a done count or epoch left wrong by
+    either completion path would show as a timeout or stale data."""
+    n, dtype = 8, "bf16"
+    ctx = snac.snac_init(n, 8 * MiB)
+    try:
+        counts = [512, 2 * MiB + 7, 3, 4 * MiB // 2, 1024 + 1, 1 * MiB + 5] * 3
+        data = {c: gen(n, c, dtype, seed=c % 997) for c in set(counts)}
+        bufs = {c: [DevBuf(x.nbytes, data=x) for x in xs] for c, xs in data.items()}
+        outs = [DevBuf(data[c][0].nbytes) for c in counts]
+        for c, ob in zip(counts, outs):
+            snac.snac_pipeline_scale_reduce(ctx, [b.ptr for b in bufs[c]], ob.ptr, c, dtype)
+        snac.snac_check(ctx)
+        want = {c: oracle.pipeline_scale_reduce(xs, dtype) for c, xs in data.items()}
+        run_and_check(outs, [want[c] for c in counts], dtype, "pipeline alternating queue counts")
+    finally:
+        snac.snac_finalize(ctx)
+
+
 def test_pipeline_back_to_back():
     n, count, dtype = 8, 200_000, "bf16"
     ctx = snac.snac_init(n, 8 * 65536)
