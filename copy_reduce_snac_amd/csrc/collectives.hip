@@ -48,14 +48,17 @@ __global__ __launch_bounds__(TH) void copy_kernel(const CollDesc d) {
 }
 
 // One-to-one copies that move at least kStreamCopyBytes (read plus
-// written): single-wave workgroups on 4 KiB tiles, five per CU when every
-// job is 16-byte aligned, four otherwise.  Measured on three MI355X boxes
-// against 256-thread workgroups on 16 KiB tiles at two per CU: copy 1 GiB
+// written): single-wave workgroups on 4 KiB tiles, five per CU.  Measured
+// on three MI355X boxes against 256-thread workgroups on 16 KiB tiles at
+// two per CU: copy 1 GiB
 // 6.29-6.34 against 5.95-6.02 TB/s, AllToAll u32 N=8 128 MiB per rank
 // 5.96-5.97 against 5.58-5.69, AllToAllV with misaligned Dirichlet counts
 // 5.74 against 5.61-5.63.  Below about 512 MiB moved the 16 KiB tiles are
 // faster (copy 64 MiB: 6.05 against 5.75; AllToAll 16 MiB per rank: 5.85
-// against 5.64).  Copies whose source sits at a byte offset from the
+// against 5.64).  Five per CU also beat four for jobs off the 16-byte grid
+// (two boxes, three alternations each: AllToAllV u32 N=8 with Dirichlet
+// counts 0.362 against 0.373 ms, a 1 GiB copy from a source 4 bytes off
+// 0.354 against 0.362).  Copies whose source sits at a byte offset from the
 // destination's dword grid keep the 16 KiB tiles at every size: their full
 // tiles funnel through DPP lane shifts (funnel_next), which single-wave
 // 4 KiB tiles did not profit from.
@@ -197,10 +200,10 @@ static KernelFn small_kernel(const CollDesc& d, bool aligned) {
 // per rank) likewise run two per CU, one tile each: bf16 N=8 AllReduce at
 // 6 and 8 MiB per rank 18.7 and 21.9 us against 20.1 and 23.3 in graph
 // replays, ReduceScatter at 5-8 MiB per rank 4-7 % less.
-static int default_wgs_per_cu(const CollDesc& d, int shape, bool aligned, uint64_t tiles, int cus) {
+static int default_wgs_per_cu(const CollDesc& d, int shape, uint64_t tiles, int cus) {
   const bool reduce = coll_is_reduce(d.coll);
   if (shape == kShapeSmall) return reduce || is_multicast_copy(d) ? 4 : 2;
-  if (shape == kShapeStream) return aligned ? 5 : 4;
+  if (shape == kShapeStream) return 5;
   if (reduce) return d.nsrc >= 3 && tiles > 2u * (uint64_t)(cus > 0 ? cus : 1) ? 1 : 2;
   return !is_multicast_copy(d) && tiles <= 8u * (uint64_t)(cus > 0 ? cus : 1) ? 4 : 2;
 }
@@ -231,7 +234,7 @@ hipError_t launch_collective(const CollDesc& d, bool aligned, int shape, uint64_
   if (e != hipSuccess) return e;
   if (per_cu < 1) per_cu = 1;
   const int cus = device_cu_count();
-  const int want = cfg.wgs_per_cu > 0 ? cfg.wgs_per_cu : default_wgs_per_cu(d, shape, aligned, tiles, cus);
+  const int want = cfg.wgs_per_cu > 0 ? cfg.wgs_per_cu : default_wgs_per_cu(d, shape, tiles, cus);
   if (want < per_cu) per_cu = want;
   uint64_t grid = (uint64_t)(cus > 0 ? cus : 1) * (uint64_t)per_cu;
   if (grid > tiles) grid = tiles;

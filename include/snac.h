@@ -474,8 +474,8 @@ typedef struct snac_tuning {
                               >= 3 sources and more than 2 tiles per CU,
                               4 for one-to-one copies of at
                               most 8 tiles per CU, else 2; for one-to-one
-                              copies moving >= 1 GiB, 5 single-wave workgroups (4
-                              when a job is not 16-byte aligned); for smaller
+                              copies moving >= 1 GiB, 5 single-wave workgroups;
+                              for smaller
                               messages, 4 for reduces and AllGather(V), else
                               2; 1 for the pipeline) */
   int32_t cache_policy;    /* 0 library default (= 1), 1 streaming (non-temporal)
