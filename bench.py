@@ -861,7 +861,7 @@ def summarize(workload: str, root: str, commands: list[str]) -> str:
     fetch_kib, write_kib = m["fetch"]["FETCH_SIZE"], wr["WRITE_SIZE"]
     cal_fetch = GiB / (1024 * cal["fetch"]["FETCH_SIZE"])
     cal_write = GiB / (1024 * cal["write"]["WRITE_SIZE"])
-    # the hash of the sources the run used, recorded on the GPU box next to
+    # the hash of the sources the run used, recorded on the GPU machine next to
     # its output (else the current tree's)
     hp = os.path.join(root, "source_hashes.json")
     run_hash = json.load(open(hp))[srcs] if os.path.exists(hp) else source_hash(SOURCE_SETS[srcs])
@@ -869,7 +869,7 @@ def summarize(workload: str, root: str, commands: list[str]) -> str:
     tr = _trace_stats(tdir, kre)
     L = [f"# `bench.py --only {workload}` ({stem}): kernel trace, HBM traffic and L2 behaviour from rocprofv3", "",
          f"Dominant kernel: `{_short(kernel or kre)}`, {alg} algorithmic bytes per launch.  Every run below is "
-         "its own process on the same box, in the same session.", ""]
+         "its own process on the same machine, in the same session.", ""]
     if tr:
         L += ["Kernel trace (`--kernel-trace --stats`, 20 timed calls after 5 warm-up calls):", ""]
         L += trace_table(tdir) + [""]
@@ -880,10 +880,10 @@ def summarize(workload: str, root: str, commands: list[str]) -> str:
             t = json.load(open(tj))
             if isinstance(t, list):
                 t = t[0]
-            L += [f"Same box, same command without the profiler (HIP events on the launch stream, "
+            L += [f"Same machine, same command without the profiler (HIP events on the launch stream, "
                   f"`python3 bench.py --only {workload}`): {t['ms_per_call']} ms per call, {t['hbm_GBps']} GB/s; "
                   f"the trace's average is {100 * (tr[2] / 1e6 / t['ms_per_call'] - 1):+.1f} % from it.", ""]
-    L += ["Commands, from the repository root on the GPU box (`REPO=$PWD`; one run per pass):", ""]
+    L += ["Commands, from the repository root on the GPU machine (`REPO=$PWD`; one run per pass):", ""]
     L += [f"    {c}" for c in commands] + [""]
     L += ["Bytes by request size (gfx950 has a counter per EA read size; the `FETCH_SIZE` expression counts "
           "128-byte reads through `TCC_BUBBLE`, which reads zero here, so it counts each as 64 bytes):", "",
@@ -939,13 +939,13 @@ def summarize_headline(root: str, commands: list[str]) -> str:
     L = ["# The headline command under rocprofv3: AllReduce bf16, N = 8, 256 MiB per rank", "",
          "The benchmark's headline path as the default run executes it, without the other workloads "
          "(`--no-extra`): 25 eager calls (5 warm-up, 20 timed with events), then 26 one-call HIP graph replays, "
-         "all at 256 MiB per rank.", "", "Command (from the repository root on the GPU box, `REPO=$PWD`):", ""]
+         "all at 256 MiB per rank.", "", "Command (from the repository root on the GPU machine, `REPO=$PWD`):", ""]
     L += [f"    {c}" for c in commands] + [""]
     L += trace_table(tdir) + [""]
     L += [f"Average duration of `reduce_kernel<8, snac::BF16, ...>`: {avg / 1e3:.1f} us over {calls} launches = "
           f"**{alg / avg:.0f} GB/s** of algorithmic bytes (2 * 8 * 256 MiB per launch), "
           f"{alg / avg / PEAK_GBPS:.3f} of 8 TB/s.", "",
-          f"Same box, same session, `python3 bench.py` (the default run, no profiler): `ms_per_step` "
+          f"Same machine, same session, `python3 bench.py` (the default run, no profiler): `ms_per_step` "
           f"{line['ms_per_step']} ms, `value` {line['value']} GB/s, `graph_median_ms` {line.get('graph_median_ms')} ms; "
           f"the trace's average kernel duration is {100 * (avg / 1e6 / line['ms_per_step'] - 1):+.1f} % from "
           "`ms_per_step`.", ""]
@@ -966,14 +966,14 @@ def summarize_ceilings(root: str, commands: list[str]) -> str:
          "`snac_hbm_probe` streams with the collectives' access primitives (16-byte buffer loads and stores with the "
          "streaming hint, grid-stride tiles) at each launch shape; 20 timed calls after 5 warm-up calls, HIP events. "
          "Bandwidth counts the bytes each stream must move (copy: read + written).", "",
-         "Commands (from the repository root on the GPU box, `REPO=$PWD`):", "",
+         "Commands (from the repository root on the GPU machine, `REPO=$PWD`):", "",
          "    python3 $REPO/bench.py --only ceilings"]
     L += [f"    {x}" for x in commands] + ["",
           "| probe | threads | tile (B) | WGs per CU | ms per call | GB/s |", "|---|---|---|---|---|---|"]
     for r in c["shapes"]:
         L.append(f"| {r['probe']} | {r['threads']} | {r['tile_bytes']} | {r['wgs_per_cu']} | {r['ms_per_call']} | "
                  f"{r['GBps']} |")
-    L += ["", "Best shape of each kind (the ceiling on this box):", "", "| stream | GB/s | of 8 TB/s | shape |",
+    L += ["", "Best shape of each kind (the ceiling on this machine):", "", "| stream | GB/s | of 8 TB/s | shape |",
           "|---|---|---|---|"]
     for k in ("read", "write", "copy"):
         L.append(f"| {k} | {c[k + '_GBps']} | {c[k + '_frac_of_peak']} | {c[k + '_shape']} |")

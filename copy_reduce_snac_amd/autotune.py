@@ -14,7 +14,7 @@ measured size up to halfway to the next larger one.  The rules are printed
 as JSON, written to --out, and installed in this process; load them into
 another process with snac_set_tuning_rules(json.load(...)).
 
-Measurements on MI355X vary from box to box by up to 13 % in absolute HBM
+Measurements on MI355X vary from machine to machine by up to 13 % in absolute HBM
 bandwidth, so a table is best measured on the machine that will use it.
 """
 from __future__ import annotations

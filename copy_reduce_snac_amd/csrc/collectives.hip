@@ -49,14 +49,14 @@ __global__ __launch_bounds__(TH) void copy_kernel(const CollDesc d) {
 
 // One-to-one copies that move at least kStreamCopyBytes (read plus
 // written): single-wave workgroups on 4 KiB tiles, five per CU.  Measured
-// on three MI355X boxes against 256-thread workgroups on 16 KiB tiles at
+// on three MI355X machines against 256-thread workgroups on 16 KiB tiles at
 // two per CU: copy 1 GiB
 // 6.29-6.34 against 5.95-6.02 TB/s, AllToAll u32 N=8 128 MiB per rank
 // 5.96-5.97 against 5.58-5.69, AllToAllV with misaligned Dirichlet counts
 // 5.74 against 5.61-5.63.  Below about 512 MiB moved the 16 KiB tiles are
 // faster (copy 64 MiB: 6.05 against 5.75; AllToAll 16 MiB per rank: 5.85
 // against 5.64).  Five per CU also beat four for jobs off the 16-byte grid
-// (two boxes, three alternations each: AllToAllV u32 N=8 with Dirichlet
+// (two machines, three alternations each: AllToAllV u32 N=8 with Dirichlet
 // counts 0.362 against 0.373 ms, a 1 GiB copy from a source 4 bytes off
 // 0.354 against 0.362).  Copies whose source sits at a byte offset from the
 // destination's dword grid keep the 16 KiB tiles at every size: their full

@@ -1,7 +1,7 @@
 """bench.py's measurement plumbing on the CPU: size arguments in the pages'
 form, and the counter summaries -- bytes counted from EA requests by size,
 the copy calibration of the derived counters, L2 hit rate, the kernel trace
-and the same-box timing -- built from synthetic rocprofv3 output with known
+and the same-machine timing -- built from synthetic rocprofv3 output with known
 values, then read back by the benchmark as current or stale."""
 from __future__ import annotations
 
@@ -86,9 +86,9 @@ def test_summary_counts_bytes_by_request_size(tmp_path, monkeypatch):
     assert float(vals["l2_hit"]) == pytest.approx(0.25, abs=1e-4)
     assert float(vals["fetch_size_copy_calibration"]) == pytest.approx(2.0, abs=1e-4)
     assert float(vals["write_size_copy_calibration"]) == pytest.approx(1.0, abs=1e-4)
-    assert vals["kernel_source_hash"] == "feedfacecafebeef"  # recorded on the box, not this tree's
+    assert vals["kernel_source_hash"] == "feedfacecafebeef"  # recorded on the GPU machine, not this tree's
     assert int(vals["kernel_average_ns"]) == 760000
-    assert "+0.0 % from it" in text  # the trace's average against the same-box event timing
+    assert "+0.0 % from it" in text  # the trace's average against the same-machine event timing
     assert "other_kernel" not in text
 
     # read back by the benchmark: stale (hash of another tree), then current
