@@ -26,6 +26,7 @@ SNAC_BYTE, SNAC_U32, SNAC_F32, SNAC_BF16 = range(4)
 (SNAC_COLL_ALL_REDUCE, SNAC_COLL_REDUCE_SCATTER, SNAC_COLL_ALL_GATHER, SNAC_COLL_ALL_TO_ALL,
  SNAC_COLL_ALL_GATHER_V, SNAC_COLL_REDUCE_SCATTER_V, SNAC_COLL_ALL_TO_ALL_V) = range(7)
 SNAC_MAX_RANKS = 16
+SNAC_MAX_BYTES = 1 << 40  # largest buffer extent (bytes) or V count (elements) a call accepts
 
 _DTYPES = {"byte": SNAC_BYTE, "u8": SNAC_BYTE, "u32": SNAC_U32, "f32": SNAC_F32, "bf16": SNAC_BF16}
 ESIZE = {SNAC_BYTE: 1, SNAC_U32: 4, SNAC_F32: 4, SNAC_BF16: 2}

@@ -388,6 +388,7 @@ snac_status fixed_collective_n(int32_t coll, int n, const void* const* src, void
   if (!e) return fail(SNAC_E_ARG, "unknown dtype %d", (int)dtype);
   const bool reduce = coll == kAllReduce || coll == kReduceScatter;
   if (reduce && !is_float(dtype)) return fail(SNAC_E_ARG, "reductions need SNAC_F32 or SNAC_BF16");
+  if (bytes > SNAC_MAX_BYTES) return fail(SNAC_E_ARG, "bytes (%zu) above SNAC_MAX_BYTES", bytes);
   if (bytes % (size_t)e) return fail(SNAC_E_ARG, "bytes (%zu) is not a multiple of the element size %d", bytes, e);
   if ((coll == kReduceScatter || coll == kAllToAll) && bytes % ((size_t)n * e))
     return fail(SNAC_E_ARG, "bytes (%zu) is not a multiple of N * element size (%d)", bytes, n * e);
@@ -438,7 +439,7 @@ snac_status v_collective(int32_t coll, snac_ctx* ctx, const void* const* src, vo
   const int nc = coll == kAllToAllV ? n * n : n;
   uint64_t total = 0;
   for (int i = 0; i < nc; ++i) {
-    if (counts[i] > ((uint64_t)1 << 40)) return fail(SNAC_E_ARG, "counts[%d] is implausibly large", i);
+    if (counts[i] > SNAC_MAX_BYTES) return fail(SNAC_E_ARG, "counts[%d] above SNAC_MAX_BYTES", i);
     total += counts[i];
   }
   if (total == 0) return describe_empty(coll, n, e);
@@ -629,6 +630,7 @@ snac_status snac_finalize(snac_ctx* ctx, snac_stream stream) {
 
 snac_status snac_copy(void* dst, const void* src, size_t bytes, snac_stream stream) {
   if (bytes == 0) return ok();
+  if (bytes > SNAC_MAX_BYTES) return fail(SNAC_E_ARG, "bytes (%zu) above SNAC_MAX_BYTES", bytes);
   if (!dst || !src) return fail(SNAC_E_ARG, "NULL pointer");
   const Range a{(uintptr_t)dst, (uintptr_t)dst + bytes}, b{(uintptr_t)src, (uintptr_t)src + bytes};
   if (overlaps(a, b)) return fail(SNAC_E_ARG, "src and dst overlap");
@@ -647,6 +649,7 @@ snac_status snac_hbm_probe(int kind, void* dst, const void* src, size_t bytes, i
   if (tile_bytes != 4096 && tile_bytes != 16384) return fail(SNAC_E_ARG, "tile_bytes must be 4096 or 16384");
   if (wgs_per_cu < 1 || wgs_per_cu > 32) return fail(SNAC_E_ARG, "wgs_per_cu outside 1..32");
   if (bytes % 16) return fail(SNAC_E_ARG, "bytes must be a multiple of 16");
+  if (bytes > SNAC_MAX_BYTES) return fail(SNAC_E_ARG, "bytes (%zu) above SNAC_MAX_BYTES", bytes);
   if (bytes == 0) return ok();
   if (!dst) return fail(SNAC_E_ARG, "dst is NULL");
   if (kind != SNAC_PROBE_WRITE && !src) return fail(SNAC_E_ARG, "src is NULL");
@@ -667,6 +670,7 @@ snac_status snac_reduce_n(void* const* dst, int ndst, const void* const* src, in
   if (!is_float(dtype)) return fail(SNAC_E_ARG, "reduce needs SNAC_F32 or SNAC_BF16");
   if (count == 0) return ok();
   const int e = esize_of(dtype);
+  if (count > SNAC_MAX_BYTES / (uint64_t)e) return fail(SNAC_E_ARG, "count (%zu) above SNAC_MAX_BYTES bytes", count);
   const uint64_t bytes = (uint64_t)count * e;
   uint64_t in_b[kMaxRanks], out_b[kMaxRanks];
   for (int i = 0; i < kMaxRanks; ++i) in_b[i] = out_b[i] = bytes;
@@ -786,6 +790,7 @@ snac_status snac_pipeline_scale_reduce(snac_ctx* ctx, const void* const* x, void
   if (count == 0) return ok();
   const int n = ctx->nranks;
   const int e = esize_of(dtype);
+  if (count > SNAC_MAX_BYTES / (uint64_t)e) return fail(SNAC_E_ARG, "count (%zu) above SNAC_MAX_BYTES bytes", count);
   if (!x || !out) return fail(SNAC_E_ARG, "NULL pointer");
   for (int i = 0; i < n; ++i) {
     if (!x[i]) return fail(SNAC_E_ARG, "x[%d] is NULL", i);
@@ -963,8 +968,12 @@ snac_status snac_plan(snac_coll coll, int nranks, snac_dtype dtype, size_t bytes
   if (v) {
     if (!counts) return fail(SNAC_E_ARG, "counts is NULL");
     const int nc = coll == SNAC_COLL_ALL_TO_ALL_V ? nranks * nranks : nranks;
-    for (int i = 0; i < nc; ++i) p.d.counts[i] = counts[i];
+    for (int i = 0; i < nc; ++i) {
+      if (counts[i] > SNAC_MAX_BYTES) return fail(SNAC_E_ARG, "counts[%d] above SNAC_MAX_BYTES", i);
+      p.d.counts[i] = counts[i];
+    }
   } else {
+    if (bytes > SNAC_MAX_BYTES) return fail(SNAC_E_ARG, "bytes (%zu) above SNAC_MAX_BYTES", bytes);
     if (bytes % (size_t)e) return fail(SNAC_E_ARG, "bytes not a multiple of the element size");
     if ((coll == SNAC_COLL_REDUCE_SCATTER || coll == SNAC_COLL_ALL_TO_ALL) && bytes % ((size_t)nranks * e))
       return fail(SNAC_E_ARG, "bytes not a multiple of N * element size");

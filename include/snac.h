@@ -18,7 +18,9 @@
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null
  *     stream).  Buffers must stay alive until the stream has passed the call.
  *   - Argument errors are reported synchronously (SNAC_E_ARG) and nothing is
- *     enqueued.  Errors detected on the device (a consumer that waited too
+ *     enqueued.  A buffer extent or V count above SNAC_MAX_BYTES bytes (or
+ *     elements), far beyond any GPU's memory, is an argument error, so that
+ *     no extent or offset the checks compute can wrap.  Errors detected on the device (a consumer that waited too
  *     long, an abort) latch in the context's status word; snac_check() and
  *     snac_finalize() report them.
  *   - A context is used from one host thread and one stream at a time.
@@ -44,6 +46,8 @@ extern "C" {
 
 #define SNAC_ABI_VERSION 2
 #define SNAC_MAX_RANKS 16
+/* largest buffer extent (bytes) or V count (elements) a call accepts: 1 TiB */
+#define SNAC_MAX_BYTES (1ull << 40)
 
 typedef enum snac_status {
   SNAC_OK = 0,

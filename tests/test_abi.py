@@ -95,7 +95,25 @@ def test_probe_argument_errors_without_gpu():
     _expect(E, p("copy", 0x1000, 0x1010, 64))            # overlap
     _expect(E, p("write", 0, None, 16))                  # no dst
     _expect(E, p("read", 0x1000, None, 16))              # no src
+    _expect(E, p("copy", 0x1000, 1 << 44, snac.SNAC_MAX_BYTES + 16))  # past the size bound
     p("copy", 0, 0, 0)()                                 # nothing to do
+
+
+def test_size_bound_without_gpu():
+    """Extents and V counts above SNAC_MAX_BYTES are argument errors, so no
+    extent or offset the checks compute can wrap; the bound itself passes
+    the size check."""
+    E, M = snac.SNAC_E_ARG, snac.SNAC_MAX_BYTES
+    assert "SNAC_MAX_BYTES" in _expect(E, snac.snac_copy, 1 << 44, 0x1000, M + 1)
+    assert "SNAC_MAX_BYTES" in _expect(E, snac.snac_copy, 1 << 44, 0x1000, (1 << 64) - 1)
+    assert "SNAC_MAX_BYTES" in _expect(E, snac.snac_reduce_n, [1 << 44], [0x1000], M // 4 + 1, "f32")
+    assert "SNAC_MAX_BYTES" in _expect(E, snac.snac_plan, snac.SNAC_COLL_ALL_REDUCE, 2, "f32", M + 4)
+    assert "SNAC_MAX_BYTES" in _expect(E, snac.snac_plan, snac.SNAC_COLL_ALL_GATHER_V, 2, "byte", 0, [M + 1, 0])
+    assert "SNAC_MAX_BYTES" in _expect(E, snac.snac_plan, snac.SNAC_COLL_ALL_TO_ALL_V, 2, "u32", 0,
+                                       [1, 2, (1 << 64) - 1, 3])
+    # at the bound the plan is made
+    assert snac.snac_plan(snac.SNAC_COLL_ALL_REDUCE, 2, "bf16", M)[0][2] == M
+    assert snac.snac_plan(snac.SNAC_COLL_ALL_GATHER_V, 2, "byte", 0, [M, 0])[0][2] == M
 
 
 def test_static_atomic_allreduce_argument_errors_without_gpu():
