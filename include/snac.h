@@ -473,15 +473,14 @@ snac_status snac_plan(snac_coll coll, int nranks, snac_dtype dtype, size_t bytes
  */
 typedef struct snac_tuning {
   int32_t wgs_per_cu;      /* workgroups per compute unit in the persistent grid
-                              (0: the kernel default -- for messages of at
-                              least one 16 KiB tile per CU, 1 for reduces of
-                              >= 3 sources and more than 2 tiles per CU,
-                              4 for one-to-one copies of at
-                              most 8 tiles per CU, else 2; for one-to-one
-                              copies moving >= 1 GiB, 5 single-wave workgroups;
-                              for smaller
-                              messages, 4 for reduces and AllGather(V), else
-                              2; 1 for the pipeline) */
+                              (0: the kernel default.  Messages of at least
+                              one 16 KiB tile per CU: 1 for reduces of >= 3
+                              sources and more than 2 tiles per CU, 4 for
+                              one-to-one copies of at most 8 tiles per CU,
+                              5 single-wave workgroups for one-to-one copies
+                              moving >= 1 GiB, else 2.  Smaller messages: 4
+                              for reduces and AllGather(V), else 2.  The
+                              pipeline: 1) */
   int32_t cache_policy;    /* 0 library default (= 1), 1 streaming (non-temporal)
                               loads and stores, 2 streaming stores only,
                               3 streaming loads only, 4 cached loads and stores */
