@@ -58,6 +58,7 @@ class snac_tuning(ctypes.Structure):
         ("debug_drop_notify", ctypes.c_int32),
         ("copy_multicast", ctypes.c_int32),
         ("debug_producer_delay", ctypes.c_int32),
+        ("tile_schedule", ctypes.c_int32),
     ]
 
 

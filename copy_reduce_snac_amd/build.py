@@ -13,7 +13,9 @@ Each HIP source is compiled to an object in parallel, then linked into
 * ``-Xclang -target-feature -Xclang -packed-fp32-ops``
                                       keep the compiler from forming packed
                                       fp32 instructions;
-* no ``-ffast-math`` and no denormal flushing.
+* no ``-ffast-math`` and no denormal flushing;
+* ``collectives.hip`` also gets ``-mllvm -amdgpu-atomic-optimizer-strategy=None``
+  (see SOURCE_FLAGS).
 """
 from __future__ import annotations
 
@@ -78,6 +80,13 @@ def _link(objs, out):
     os.replace(tmp, out)
 
 
+# Per-source flags.  collectives.hip: the compiler's atomic optimizer off.
+# It turns an atomic on one address into a wave-wide reduction whose result
+# it waits for at once; the shared tile counter's fetch must instead stay in
+# flight while the current tile moves (TilePool in snac_device.hpp).
+SOURCE_FLAGS = {"collectives.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     t0 = time.time()
@@ -85,7 +94,7 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
         objs.append(obj)
-        jobs.append((src, [HIPCC, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]))
+        jobs.append((src, [HIPCC, *DEVICE_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]))
     dev_obj = os.path.join(BUILD, "devapi_kernels.o")
     jobs.append(("devapi_kernels.hip", [HIPCC, *DEVICE_FLAGS, "-c", DEVTEST_SRC, "-o", dev_obj]))
     _compile(jobs, verbose)

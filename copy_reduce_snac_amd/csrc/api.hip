@@ -34,6 +34,8 @@ struct snac_ctx {
   uint64_t* freed;
   uint64_t* ctrl;
   uint64_t* user_flags;  // kUserFlags flags for device-side users
+  uint64_t* pool;        // kPoolSlots tile-counter slots (kPoolSlotWords each)
+  uint32_t pool_seq;     // the next call's slot
   uint64_t signal_words;
   uint32_t* abort_host;  // host-mapped word (hipHostMalloc)
   uint32_t* abort_dev;   // its device-visible address
@@ -64,15 +66,16 @@ snac_status hip_fail(hipError_t e, const char* what) {
 
 // Process-wide tuning, initialised from the environment when the library
 // loads: SNAC_WGS_PER_CU, SNAC_CACHE_POLICY, SNAC_PIPELINE_TILE_BYTES,
-// SNAC_PIPELINE_LOOKAHEAD, SNAC_SPIN_LIMIT_LOG2, SNAC_COPY_MULTICAST (decimal
-// integers; a value snac_set_tuning would reject, or that does not parse,
-// is ignored).
+// SNAC_PIPELINE_LOOKAHEAD, SNAC_SPIN_LIMIT_LOG2, SNAC_COPY_MULTICAST,
+// SNAC_TILE_SCHEDULE (decimal integers; a value snac_set_tuning would
+// reject, or that does not parse, is ignored).
 bool tuning_valid(const snac_tuning& t) {
   return t.wgs_per_cu >= 0 && t.wgs_per_cu <= 32 && t.cache_policy >= 0 && t.cache_policy <= 4 &&
          t.pipeline_tile_bytes >= 0 && t.pipeline_tile_bytes % 4096 == 0 && t.pipeline_lookahead >= 0 &&
          t.spin_limit_log2 >= 0 && t.spin_limit_log2 <= 40 && t.debug_drop_notify >= 0 &&
          t.debug_drop_notify <= SNAC_MAX_RANKS && t.copy_multicast >= 0 && t.copy_multicast <= 2 &&
-         t.debug_producer_delay >= 0 && t.debug_producer_delay <= 100000;
+         t.debug_producer_delay >= 0 && t.debug_producer_delay <= 100000 && t.tile_schedule >= 0 &&
+         t.tile_schedule <= 2;
 }
 
 int env_int(const char* name, bool* ok) {
@@ -87,7 +90,7 @@ int env_int(const char* name, bool* ok) {
 }
 
 snac_tuning tuning_from_env() {
-  snac_tuning t{0, 0, 0, 0, 0, 0, 0, 0};
+  snac_tuning t{0, 0, 0, 0, 0, 0, 0, 0, 0};
   struct {
     const char* name;
     int32_t* field;
@@ -96,7 +99,8 @@ snac_tuning tuning_from_env() {
               {"SNAC_PIPELINE_TILE_BYTES", &t.pipeline_tile_bytes},
               {"SNAC_PIPELINE_LOOKAHEAD", &t.pipeline_lookahead},
               {"SNAC_SPIN_LIMIT_LOG2", &t.spin_limit_log2},
-              {"SNAC_COPY_MULTICAST", &t.copy_multicast}};
+              {"SNAC_COPY_MULTICAST", &t.copy_multicast},
+              {"SNAC_TILE_SCHEDULE", &t.tile_schedule}};
   for (auto& v : vars) {
     bool ok = false;
     const int x = env_int(v.name, &ok);
@@ -180,10 +184,10 @@ bool rule_matches(const snac_tuning_rule& r, int32_t coll, int nsrc, int esize, 
 // Launch parameters of a call: the first matching rule, then the explicit
 // process-wide values on top.  The caller holds g_tuning_mu.
 LaunchCfg launch_cfg_locked(int32_t coll, int nsrc, int esize, uint64_t bytes) {
-  LaunchCfg c{0, 0};
+  LaunchCfg c{0, 0, g_tuning.tile_schedule};
   for (const snac_tuning_rule& r : g_rules) {
     if (rule_matches(r, coll, nsrc, esize, bytes)) {
-      c = LaunchCfg{r.wgs_per_cu, r.cache_policy};
+      c = LaunchCfg{r.wgs_per_cu, r.cache_policy, g_tuning.tile_schedule};
       break;
     }
   }
@@ -227,6 +231,7 @@ bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 // Shared argument checks and planning for every collective.
 struct Plan {
   CollDesc d;
+  snac_ctx* ctx;  // the call's context (its tile counters), or nullptr
   bool aligned;
   int shape;   // kShape*: 16 KiB tiles, small tiles (message too small to fill the GPU
                // at 16 KiB tiles), or the 4 KiB streaming shape of big one-to-one copies
@@ -353,8 +358,13 @@ snac_status run(Plan& p, hipStream_t stream) {
     return ok();
   }
   if (p.tiles == 0) return ok();
+  unsigned long long* pool = nullptr;
+  if (p.ctx) {
+    pool = reinterpret_cast<unsigned long long*>(p.ctx->pool + (uint64_t)(p.ctx->pool_seq % kPoolSlots) * kPoolSlotWords);
+    ++p.ctx->pool_seq;
+  }
   hipError_t e = launch_collective(p.d, p.aligned, p.shape, p.tiles,
-                                   launch_cfg(p.d.coll, p.d.nsrc, p.d.esize, p.rule_bytes), stream);
+                                   launch_cfg(p.d.coll, p.d.nsrc, p.d.esize, p.rule_bytes), stream, pool);
   if (e != hipSuccess) return hip_fail(e, "collective launch");
   return ok();
 }
@@ -381,8 +391,8 @@ snac_status describe_empty(int32_t coll, int n, int e) {
 
 // fixed-size collectives share their checks (n ranks; the context's rank
 // count, or the caller's for the context-free entry point)
-snac_status fixed_collective_n(int32_t coll, int n, const void* const* src, void* const* dst, size_t bytes,
-                               snac_dtype dtype, snac_stream stream) {
+snac_status fixed_collective_n(int32_t coll, snac_ctx* ctx, int n, const void* const* src, void* const* dst,
+                               size_t bytes, snac_dtype dtype, snac_stream stream) {
   snac_status st = SNAC_OK;
   const int e = esize_of(dtype);
   if (!e) return fail(SNAC_E_ARG, "unknown dtype %d", (int)dtype);
@@ -409,6 +419,7 @@ snac_status fixed_collective_n(int32_t coll, int n, const void* const* src, void
   });
   if (st != SNAC_OK) return st;
   Plan p = base_plan(coll, n, n, e);
+  p.ctx = ctx;
   p.d.bytes = bytes;
   p.rule_bytes = bytes;
   for (int i = 0; i < n; ++i) {
@@ -424,7 +435,7 @@ snac_status fixed_collective(int32_t coll, snac_ctx* ctx, const void* const* src
                              snac_dtype dtype, snac_stream stream) {
   const snac_status st = check_ctx(ctx);
   if (st != SNAC_OK) return st;
-  return fixed_collective_n(coll, ctx->nranks, src, dst, bytes, dtype, stream);
+  return fixed_collective_n(coll, ctx, ctx->nranks, src, dst, bytes, dtype, stream);
 }
 
 snac_status v_collective(int32_t coll, snac_ctx* ctx, const void* const* src, void* const* dst, const size_t* counts,
@@ -465,6 +476,7 @@ snac_status v_collective(int32_t coll, snac_ctx* ctx, const void* const* src, vo
   st = check_overlap(src, in_b, n, dst, out_b, n, [](int, int) { return false; });
   if (st != SNAC_OK) return st;
   Plan p = base_plan(coll, n, n, e);
+  p.ctx = ctx;
   for (int i = 0; i < n; ++i) {
     p.d.src[i] = src[i];
     p.d.dst[i] = dst[i];
@@ -518,6 +530,7 @@ snac_status snac_set_tuning(const snac_tuning* in) {
   if (in->copy_multicast < 0 || in->copy_multicast > 2) return fail(SNAC_E_ARG, "copy_multicast out of range [0, 2]");
   if (in->debug_producer_delay < 0 || in->debug_producer_delay > 100000)
     return fail(SNAC_E_ARG, "debug_producer_delay out of range [0, 100000]");
+  if (in->tile_schedule < 0 || in->tile_schedule > 2) return fail(SNAC_E_ARG, "tile_schedule out of range [0, 2]");
   {
     std::unique_lock<std::shared_mutex> lk(g_tuning_mu);
     g_tuning = *in;
@@ -557,7 +570,8 @@ snac_status snac_init(int nranks, size_t staging_bytes_per_rank, snac_stream str
   c->flag_slots = (uint32_t)fslots;
   const uint64_t ready_words = (uint64_t)nranks * fslots * kFlagStride;
   const uint64_t free_words = (uint64_t)nranks * fslots * kFlagStride;
-  c->signal_words = ready_words + free_words + kCtrlWords + (uint64_t)kUserFlags * kFlagStride;
+  c->signal_words = ready_words + free_words + kCtrlWords + (uint64_t)kUserFlags * kFlagStride +
+                    (uint64_t)kPoolSlots * kPoolSlotWords;
   const size_t staging_total = (size_t)nranks * staging;
   const size_t bytes = staging_total + c->signal_words * sizeof(uint64_t);
   e = hipMalloc(reinterpret_cast<void**>(&c->workspace), bytes);
@@ -570,6 +584,8 @@ snac_status snac_init(int nranks, size_t staging_bytes_per_rank, snac_stream str
   c->freed = c->ready + ready_words;
   c->ctrl = c->freed + free_words;
   c->user_flags = c->ctrl + kCtrlWords;
+  c->pool = c->user_flags + (uint64_t)kUserFlags * kFlagStride;
+  c->pool_seq = 0;
   e = hipHostMalloc(reinterpret_cast<void**>(&c->abort_host), sizeof(uint32_t), hipHostMallocMapped | hipHostMallocCoherent);
   if (e != hipSuccess) {
     (void)hipFree(c->workspace);
@@ -737,7 +753,7 @@ snac_status snac_all_reduce_atomic_static(int nranks, const void* const* src, vo
   // validate exactly as the AllReduce does, without launching
   snac_coll_desc d;
   g_describe = &d;
-  snac_status st = fixed_collective_n(kAllReduce, nranks, src, dst, bytes, dtype, stream);
+  snac_status st = fixed_collective_n(kAllReduce, nullptr, nranks, src, dst, bytes, dtype, stream);
   g_describe = nullptr;
   if (st != SNAC_OK) return st;
   if (bytes == 0) return ok();

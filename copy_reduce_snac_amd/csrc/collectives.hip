@@ -28,11 +28,14 @@ constexpr int kSmallReduceThreads = 128;
 // the small-tile form (one 16-byte unit per lane, all sources in flight)
 // for messages with fewer 16 KiB tiles than the GPU has CUs.
 template <int N, typename T, int CP, bool ALIGNED, bool SMALL = false>
-__global__ __launch_bounds__(SMALL ? kSmallReduceThreads : kReduceThreads) void reduce_kernel(const CollDesc d) {
+__global__ __launch_bounds__(SMALL ? kSmallReduceThreads : kReduceThreads) void reduce_kernel(const CollDesc d,
+                                                                                            const PoolArg pa) {
   constexpr int TH = SMALL ? kSmallReduceThreads : kReduceThreads;
   constexpr uint32_t TILE = SMALL ? TH * 16u : kTileBytes;
   __shared__ __align__(16) char lds[engine_lds_bytes<TH, kMaxRanks>()];
-  run_reduce<N, T, TH, CP, ALIGNED, TILE>(d, blockIdx.x, gridDim.x, lds);
+  __shared__ unsigned long long xchg[2];
+  const TilePool pool{(global_u64*)pa.next, (global_u64*)(pa.next + kFlagStride), xchg, pa.rounds};
+  run_reduce<N, T, TH, CP, ALIGNED, TILE>(d, blockIdx.x, gridDim.x, lds, pool);
 }
 
 // Byte copy of the collective's jobs, the whole grid.  TH = 256 for
@@ -42,9 +45,11 @@ __global__ __launch_bounds__(SMALL ? kSmallReduceThreads : kReduceThreads) void 
 constexpr int kMulticastThreads = 64;
 
 template <int CP, bool ALIGNED, int TH, uint32_t TILE = kTileBytes>
-__global__ __launch_bounds__(TH) void copy_kernel(const CollDesc d) {
+__global__ __launch_bounds__(TH) void copy_kernel(const CollDesc d, const PoolArg pa) {
   __shared__ __align__(16) char lds[engine_lds_bytes<TH>()];
-  run_copy<TH, CP, ALIGNED, TILE>(d, blockIdx.x, gridDim.x, lds);
+  __shared__ unsigned long long xchg[2];
+  const TilePool pool{(global_u64*)pa.next, (global_u64*)(pa.next + kFlagStride), xchg, pa.rounds};
+  run_copy<TH, CP, ALIGNED, TILE>(d, blockIdx.x, gridDim.x, lds, pool);
 }
 
 // One-to-one copies that move at least kStreamCopyBytes (read plus
@@ -72,7 +77,7 @@ SNAC_HD bool is_multicast_copy(const CollDesc& d) {
 
 // ------------------------------------------------------------- launchers
 
-using KernelFn = void (*)(const CollDesc);
+using KernelFn = void (*)(const CollDesc, const PoolArg);
 
 template <int N, typename T, int CP, bool A, bool SMALL>
 KernelFn kernel_ptr() {
@@ -208,8 +213,29 @@ static int default_wgs_per_cu(const CollDesc& d, int shape, uint64_t tiles, int 
   return !is_multicast_copy(d) && tiles <= 8u * (uint64_t)(cus > 0 ? cus : 1) ? 4 : 2;
 }
 
+// The shared tile counter serves launches in the 16 KiB-tile shape with at
+// least kPoolMinRounds tiles per workgroup whose tiles each move at least
+// kPoolMinStreams 16 KiB streams (sources read plus destinations written).
+// The counter is one address, and on MI355X one address takes about 84 M
+// atomic adds per second; a one-to-one copy of 16 KiB tiles at 6 TB/s would
+// ask for 180 M (and AllToAll u32 N=8, 128 MiB per rank, with a fetch per
+// 4 KiB tile took 1.57 ms against 0.36).  The first kPoolGridRounds rounds
+// are grid-stride, since every workgroup starting on the counter at once
+// only queues on it.  AllReduce bf16 N=8 twin, 256 MiB per rank (64
+// rounds): 0.717 ms with 8 grid-stride rounds first, 0.718-0.721 with 16 or
+// none, against 0.751 with grid-stride tiles only.
+constexpr uint64_t kPoolMinRounds = 16;
+constexpr uint32_t kPoolGridRounds = 8;
+constexpr int kPoolMinStreams = 8;
+
+// 16 KiB streams one tile of this descriptor's kernel moves.
+static int tile_streams(const CollDesc& d) {
+  if (coll_is_reduce(d.coll)) return d.nsrc + (d.coll == kAllReduce && !d.split_multicast ? d.ndst : 1);
+  return is_multicast_copy(d) ? 1 + d.ndst : 2;
+}
+
 hipError_t launch_collective(const CollDesc& d, bool aligned, int shape, uint64_t tiles, const LaunchCfg& cfg,
-                             hipStream_t stream) {
+                             hipStream_t stream, unsigned long long* pool) {
   if (tiles == 0) return hipSuccess;
   KernelFn fn = nullptr;
   // tuning value 0 = library default (streaming loads and stores), 4 = cached
@@ -238,7 +264,15 @@ hipError_t launch_collective(const CollDesc& d, bool aligned, int shape, uint64_
   if (want < per_cu) per_cu = want;
   uint64_t grid = (uint64_t)(cus > 0 ? cus : 1) * (uint64_t)per_cu;
   if (grid > tiles) grid = tiles;
-  hipLaunchKernelGGL(fn, dim3((uint32_t)grid), dim3(threads), 0, stream, d);
+  PoolArg pa{nullptr, 0};
+  const uint64_t rounds = tiles / grid;
+  if (pool && shape == kShapeTile &&
+      (cfg.tile_schedule == 2 ||
+       (cfg.tile_schedule == 0 && rounds >= kPoolMinRounds && tile_streams(d) >= kPoolMinStreams))) {
+    pa.next = pool;
+    pa.rounds = rounds >= 2 * kPoolGridRounds ? kPoolGridRounds : (uint32_t)(rounds > 2 ? rounds / 2 : 1);
+  }
+  hipLaunchKernelGGL(fn, dim3((uint32_t)grid), dim3(threads), 0, stream, d, pa);
   return hipGetLastError();
 }
 

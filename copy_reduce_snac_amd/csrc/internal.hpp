@@ -11,8 +11,16 @@ namespace snac {
 constexpr int kThreads = 256;  // workgroup size of the pipeline and copy kernels
 
 struct LaunchCfg {
-  int wgs_per_cu;    // 0: as many as fit
-  int cache_policy;  // kCache*
+  int wgs_per_cu;     // 0: as many as fit
+  int cache_policy;   // kCache*
+  int tile_schedule;  // snac_tuning.tile_schedule: 0 default, 1 grid-stride only, 2 shared counter
+};
+
+// Shared tile counters of one launch (TilePool in snac_device.hpp): `next`,
+// and the done count kFlagStride words after it; nullptr: grid-stride.
+struct PoolArg {
+  unsigned long long* next;
+  uint32_t rounds;  // grid-stride rounds before the counter
 };
 
 // Tile shapes of the host-launched collective kernels:
@@ -36,9 +44,11 @@ int large_shape(const CollDesc& d, uint64_t job_bytes, bool byte_shift);
 
 // Launch the copy or reduce kernel for a collective descriptor.  `tiles` is
 // the total tile count of the layout at coll_tile_bytes(d, shape) (computed
-// on the host with the same layout functions the kernel uses).
+// on the host with the same layout functions the kernel uses).  `pool`: a
+// pair of zeroed counters (two words kFlagStride apart) this launch may
+// hand its tiles out from, or nullptr; a launch leaves them zeroed again.
 hipError_t launch_collective(const CollDesc& d, bool aligned, int shape, uint64_t tiles, const LaunchCfg& cfg,
-                             hipStream_t stream);
+                             hipStream_t stream, unsigned long long* pool = nullptr);
 
 // Non-deterministic AllReduce of elements [first, first + elems) of every
 // source: zero acc[0..elems), add every source into it with float atomics,
@@ -97,6 +107,10 @@ enum : uint32_t {
 };
 constexpr uint32_t kFlagStride = SNAC_FLAG_STRIDE;  // uint64 words between flags (128 B)
 constexpr uint32_t kUserFlags = 1024;               // flags handed to device-side users
+// Tile-counter slots per context: consecutive collective calls take
+// consecutive slots, so that calls in flight at once rarely share one.
+constexpr uint32_t kPoolSlots = 64;
+constexpr uint32_t kPoolSlotWords = 2 * kFlagStride;  // next, then done, one 128-byte line each
 
 // workgroups per CU of a pipeline launch under cfg
 int pipe_wgs_per_cu(const LaunchCfg& cfg);

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define SNAC_ABI_VERSION 2
+#define SNAC_ABI_VERSION 3
 #define SNAC_MAX_RANKS 16
 /* largest buffer extent (bytes) or V count (elements) a call accepts: 1 TiB */
 #define SNAC_MAX_BYTES (1ull << 40)
@@ -468,7 +468,7 @@ snac_status snac_plan(snac_coll coll, int nranks, snac_dtype dtype, size_t bytes
  * for peak performance).  Zero fields select the defaults.  When the library
  * loads, the fields start from the environment variables SNAC_WGS_PER_CU,
  * SNAC_CACHE_POLICY, SNAC_PIPELINE_TILE_BYTES, SNAC_PIPELINE_LOOKAHEAD,
- * SNAC_SPIN_LIMIT_LOG2 and SNAC_COPY_MULTICAST (decimal integers; values
+ * SNAC_SPIN_LIMIT_LOG2, SNAC_COPY_MULTICAST and SNAC_TILE_SCHEDULE (decimal integers; values
  * snac_set_tuning would reject are ignored).
  */
 typedef struct snac_tuning {
@@ -500,6 +500,13 @@ typedef struct snac_tuning {
                                     producer items (chosen by a hash of tile and
                                     rank) first sleep about this many microseconds,
                                     to skew producers against consumers */
+  int32_t tile_schedule;       /* how a collective call's workgroups share its
+                                  16 KiB tiles: 0 library default (grid-stride,
+                                  then a counter in the context handing out the
+                                  rest in order, for calls of at least 16 tiles
+                                  per workgroup whose tiles each read and write
+                                  at least 8 buffers), 1 grid-stride only, 2 the
+                                  counter for every call in that tile shape */
 } snac_tuning;
 
 snac_status snac_get_tuning(snac_tuning* out);

@@ -45,7 +45,7 @@ def test_nm_shows_c_linkage():
 
 
 def test_versions_and_status_strings():
-    assert snac.snac_abi_version() == 2
+    assert snac.snac_abi_version() == 3
     for s in range(8):
         assert snac.snac_status_str(s).startswith("SNAC_")
     assert "unknown" in snac.snac_status_str(99)
@@ -140,6 +140,9 @@ def test_tuning_roundtrip_and_ranges():
         assert t["wgs_per_cu"] == 3 and t["cache_policy"] == 1
         _expect(snac.SNAC_E_ARG, lambda: snac.snac_set_tuning(cache_policy=9))
         _expect(snac.SNAC_E_ARG, lambda: snac.snac_set_tuning(pipeline_tile_bytes=1000))
+        _expect(snac.SNAC_E_ARG, lambda: snac.snac_set_tuning(tile_schedule=3))
+        snac.snac_set_tuning(tile_schedule=2)
+        assert snac.snac_get_tuning()["tile_schedule"] == 2
     finally:
         snac.snac_set_tuning(**t0)
 
@@ -357,11 +360,14 @@ def test_tuning_from_environment():
 
     code = ("import sys; sys.path.insert(0, %r); import copy_reduce_snac_amd as s; t = s.snac_get_tuning(); "
             "print(t['wgs_per_cu'], t['cache_policy'], t['pipeline_tile_bytes'], t['spin_limit_log2'], "
-            "t['copy_multicast'])" % ROOT)
+            "t['copy_multicast'], t['tile_schedule'])" % ROOT)
     env = dict(os.environ, SNAC_WGS_PER_CU="3", SNAC_CACHE_POLICY="4", SNAC_PIPELINE_TILE_BYTES="8192",
-               SNAC_SPIN_LIMIT_LOG2="99", SNAC_COPY_MULTICAST="x1")
+               SNAC_SPIN_LIMIT_LOG2="99", SNAC_COPY_MULTICAST="x1", SNAC_TILE_SCHEDULE="1")
     out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, check=True).stdout
-    assert out.split() == ["3", "4", "8192", "0", "0"]
+    assert out.split() == ["3", "4", "8192", "0", "0", "1"]
+    env["SNAC_TILE_SCHEDULE"] = "5"
+    out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, check=True).stdout
+    assert out.split()[-1] == "0"
 
 
 def test_binding_refuses_rank_lists_of_the_wrong_length(monkeypatch):

@@ -16,6 +16,11 @@
   every unit in turn, one load group in flight per wave.
 * Full byte-misaligned tiles of the 256-thread copy kernels take the next
   lane's bytes through DPP whole-wave shifts (wave_shl:1).
+* The shared tile counter's fetch in the 16 KiB-tile kernels is a plain
+  global atomic that stays in flight: no wave-wide reduction around it
+  (v_mbcnt) and no wait for every memory operation right after it (the
+  build turns the compiler's atomic optimizer off for this), and nothing
+  spills to scratch.
 """
 from __future__ import annotations
 
@@ -43,15 +48,15 @@ SOURCES = {
 @pytest.fixture(scope="module")
 def asm(tmp_path_factory) -> dict[str, str]:
     """gfx950 assembly of every source, the compiles run side by side."""
-    from copy_reduce_snac_amd.build import DEVICE_FLAGS
+    from copy_reduce_snac_amd.build import DEVICE_FLAGS, SOURCE_FLAGS
 
     d = tmp_path_factory.mktemp("asm")
     flags = [f for f in DEVICE_FLAGS if f not in ("-fPIC",)]
     procs = {}
     for name, path in SOURCES.items():
         out = d / (name + ".s")
-        procs[name] = (out, subprocess.Popen([hipcc, *flags, "--cuda-device-only", "-S", path, "-o", str(out)],
-                                             stdout=subprocess.PIPE, stderr=subprocess.PIPE))
+        cmd = [hipcc, *flags, *SOURCE_FLAGS.get(name, []), "--cuda-device-only", "-S", path, "-o", str(out)]
+        procs[name] = (out, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE))
     res = {}
     for name, (out, p) in procs.items():
         _, err = p.communicate()
@@ -157,3 +162,20 @@ def test_misaligned_256_thread_copy_uses_dpp_shifts(asm):
     assert ks
     for name, lines in ks.items():
         assert any("wave_shl:1" in l for l in lines), f"{name}: no DPP lane shift"
+
+
+def test_tile_counter_fetch_stays_in_flight(asm):
+    ks = {k: v for k, v in _kernels(asm["collectives.hip"]).items()
+          if (k.startswith("_ZN4snac13reduce_kernelI") and re.search(r"ELb[01]ELb0EEEv", k))
+          or (k.startswith("_ZN4snac11copy_kernelI") and "Lj16384E" in k)}
+    assert len(ks) >= 96
+    for name, lines in ks.items():
+        text = "\n".join(lines)
+        assert "flat_atomic" not in text and "scratch_" not in text, name
+        code = [l.strip() for l in lines if l.strip() and not l.strip().startswith(";")]
+        fetch = [i for i, l in enumerate(code) if l.startswith("global_atomic_add_x2") and " sc0" in l]
+        assert fetch, f"{name}: no counter fetch"
+        i = fetch[0]
+        assert not any(l.startswith("v_mbcnt") for l in code[max(0, i - 8):i]), f"{name}: fetch folded wave-wide"
+        assert not any(re.match(r"s_waitcnt\s+vmcnt\(0\)", l) for l in code[i + 1:i + 4]), \
+            f"{name}: waits for the tile fetch at once"
