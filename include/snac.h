@@ -24,7 +24,11 @@
  *     long, an abort) latch in the context's status word; snac_check() and
  *     snac_finalize() report them.
  *   - A context is used from one host thread and one stream at a time.
- *     Different contexts may be used from different threads at once.  The
+ *     Different contexts may be used from different threads at once.
+ *     (Long collective calls hand out their tiles from counters in the
+ *     context; consecutive calls take different counters, 64 in turn, so
+ *     calls of one context must not run 64 or more at a time, nor two
+ *     replays of one captured graph at once.)  The
  *     process-wide tuning (snac_set_tuning, the rule table) may be changed
  *     from any thread; every call uses one consistent copy of it.
  *   - Reductions accumulate in binary32 in rank order 0..N-1 starting from
@@ -167,8 +171,8 @@ const char* snac_last_error(void);
  *   out                     receives the context; on error *out is NULL.
  *
  * The context owns its workspace: staging[nranks][slots][tile] and the
- * signal area (one 128-byte line per ready flag, per free flag and per
- * control word).  Errors: SNAC_E_ARG (bad nranks/size/out), SNAC_E_NOMEM,
+ * signal area (one 128-byte line per ready flag, per free flag, per control
+ * word and per tile counter of the collectives' shared tile schedule).  Errors: SNAC_E_ARG (bad nranks/size/out), SNAC_E_NOMEM,
  * SNAC_E_HIP.
  */
 snac_status snac_init(int nranks, size_t staging_bytes_per_rank, snac_stream stream, snac_ctx** out);
