@@ -28,9 +28,9 @@
  *     (Long collective calls hand out their tiles from counters in the
  *     context; consecutive calls take different counters, 64 in turn, so
  *     calls of one context must not run 64 or more at a time, nor two
- *     replays of one captured graph at once.)  The
- *     process-wide tuning (snac_set_tuning, the rule table) may be changed
- *     from any thread; every call uses one consistent copy of it.
+ *     replays of one captured graph at once.)  The process-wide tuning
+ *     (snac_set_tuning, the rule table) may be changed from any thread;
+ *     every call uses one consistent copy of it.
  *   - Reductions accumulate in binary32 in rank order 0..N-1 starting from
  *     the rank-0 value and round once to the output type (bf16:
  *     round-to-nearest-even).  Results are therefore bitwise repeatable, the
