@@ -565,8 +565,10 @@ def run_copy(env: Env, steps: int, warmup: int, nbytes: int = GiB):
     return attach_counters(result(f"copy {nbytes // MiB} MiB", t, 2 * nbytes, nbytes), "copy")
 
 
-PROBE_SHAPES = [(64, 4096, 2), (64, 4096, 4), (64, 4096, 5), (64, 4096, 8), (256, 16384, 1), (256, 16384, 2),
-                (256, 16384, 4)]
+# (threads, tile bytes, workgroups per CU, tiles in order from counters)
+PROBE_SHAPES = [(64, 4096, 2, False), (64, 4096, 4, False), (64, 4096, 5, False), (64, 4096, 8, False),
+                (256, 16384, 1, False), (256, 16384, 2, False), (256, 16384, 4, False),
+                (64, 16384, 2, True), (256, 16384, 1, True), (256, 16384, 2, True)]
 
 
 def run_ceilings(env: Env, steps: int, warmup: int, nbytes: int = GiB):
@@ -579,22 +581,25 @@ def run_ceilings(env: Env, steps: int, warmup: int, nbytes: int = GiB):
     dst = env.empty(nbytes)
     rows, best = [], {}
     for kind, moved in (("read", nbytes), ("write", nbytes), ("copy", 2 * nbytes)):
-        for th, tile, w in PROBE_SHAPES:
+        for th, tile, w, ordered in PROBE_SHAPES:
             s = None if kind == "write" else src
-            t = env.time_calls(lambda: snac.snac_hbm_probe(kind, dst, s, nbytes, th, tile, w, 0x9E3779B9,
+            k = kind + ("_ordered" if ordered else "")
+            t = env.time_calls(lambda: snac.snac_hbm_probe(k, dst, s, nbytes, th, tile, w, 0x9E3779B9,
                                                            env.stream), steps, warmup)
             gbps = moved / t / 1e9
             rows.append({"probe": kind, "threads": th, "tile_bytes": tile, "wgs_per_cu": w,
+                         "tiles": "in order from counters" if ordered else "grid-stride",
                          "ms_per_call": round(t * 1e3, 5), "GBps": round(gbps, 1)})
             if gbps > best.get(kind, (0,))[0]:
-                best[kind] = (gbps, th, tile, w)
+                best[kind] = (gbps, th, tile, w, ordered)
     del src, dst
     torch.cuda.empty_cache()
     out = {"workload": f"HBM ceilings, {nbytes // MiB} MiB streams (snac_hbm_probe)", "shapes": rows}
-    for kind, (gbps, th, tile, w) in best.items():
+    for kind, (gbps, th, tile, w, ordered) in best.items():
         out[f"{kind}_GBps"] = round(gbps, 1)
         out[f"{kind}_frac_of_peak"] = round(gbps / PEAK_GBPS, 4)
-        out[f"{kind}_shape"] = f"{th} threads, {tile} B tiles, {w} per CU"
+        out[f"{kind}_shape"] = (f"{th} threads, {tile} B tiles, {w} per CU, "
+                                + ("tiles in order from counters" if ordered else "grid-stride tiles"))
     return out
 
 
@@ -964,15 +969,16 @@ def summarize_ceilings(root: str, commands: list[str]) -> str:
     run_hash = json.load(open(hp))["probes"] if os.path.exists(hp) else source_hash(SOURCE_SETS["probes"])
     L = ["# HBM ceilings of one MI355X: read-only, write-only and 1:1 copy streams of 1 GiB", "",
          "`snac_hbm_probe` streams with the collectives' access primitives (16-byte buffer loads and stores with the "
-         "streaming hint, grid-stride tiles) at each launch shape; 20 timed calls after 5 warm-up calls, HIP events. "
+         "streaming hint) at each launch shape, the tiles grid-stride or, after 8 grid-stride rounds, in order from "
+         "counters as the collectives' long launches take them; 20 timed calls after 5 warm-up calls, HIP events. "
          "Bandwidth counts the bytes each stream must move (copy: read + written).", "",
          "Commands (from the repository root on the GPU machine, `REPO=$PWD`):", "",
          "    python3 $REPO/bench.py --only ceilings"]
     L += [f"    {x}" for x in commands] + ["",
-          "| probe | threads | tile (B) | WGs per CU | ms per call | GB/s |", "|---|---|---|---|---|---|"]
+          "| probe | threads | tile (B) | WGs per CU | tiles | ms per call | GB/s |", "|---|---|---|---|---|---|---|"]
     for r in c["shapes"]:
-        L.append(f"| {r['probe']} | {r['threads']} | {r['tile_bytes']} | {r['wgs_per_cu']} | {r['ms_per_call']} | "
-                 f"{r['GBps']} |")
+        L.append(f"| {r['probe']} | {r['threads']} | {r['tile_bytes']} | {r['wgs_per_cu']} | "
+                 f"{r.get('tiles', 'grid-stride')} | {r['ms_per_call']} | {r['GBps']} |")
     L += ["", "Best shape of each kind (the ceiling on this machine):", "", "| stream | GB/s | of 8 TB/s | shape |",
           "|---|---|---|---|"]
     for k in ("read", "write", "copy"):

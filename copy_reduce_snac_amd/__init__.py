@@ -261,12 +261,15 @@ def snac_copy(dst, src, nbytes: int, stream=None) -> None:
 
 
 SNAC_PROBE_READ, SNAC_PROBE_WRITE, SNAC_PROBE_COPY = range(3)
+SNAC_PROBE_ORDERED = 8
 _PROBES = {"read": SNAC_PROBE_READ, "write": SNAC_PROBE_WRITE, "copy": SNAC_PROBE_COPY}
+_PROBES.update({k + "_ordered": v | SNAC_PROBE_ORDERED for k, v in list(_PROBES.items())})
 
 
 def snac_hbm_probe(kind, dst, src, nbytes: int, threads: int = 64, tile_bytes: int = 4096, wgs_per_cu: int = 4,
                    magic: int = 0x9E3779B9, stream=None) -> None:
-    """HBM ceiling probe (measurement helper): kind "read", "write" or "copy"."""
+    """HBM ceiling probe (measurement helper): kind "read", "write" or "copy", or the same with "_ordered"
+    (tiles handed out in order from counters after 8 grid-stride rounds)."""
     k = _PROBES[kind] if isinstance(kind, str) else int(kind)
     _check(lib().snac_hbm_probe(k, _ptr(dst), _ptr(src) if src is not None else None, nbytes, threads, tile_bytes,
                                 wgs_per_cu, magic & 0xFFFFFFFF, _stream(stream)), "snac_hbm_probe")

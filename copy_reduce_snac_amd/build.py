@@ -14,8 +14,8 @@ Each HIP source is compiled to an object in parallel, then linked into
                                       keep the compiler from forming packed
                                       fp32 instructions;
 * no ``-ffast-math`` and no denormal flushing;
-* ``collectives.hip`` also gets ``-mllvm -amdgpu-atomic-optimizer-strategy=None``
-  (see SOURCE_FLAGS).
+* ``collectives.hip`` and ``probes.hip`` also get
+  ``-mllvm -amdgpu-atomic-optimizer-strategy=None`` (see SOURCE_FLAGS).
 """
 from __future__ import annotations
 
@@ -80,11 +80,13 @@ def _link(objs, out):
     os.replace(tmp, out)
 
 
-# Per-source flags.  collectives.hip: the compiler's atomic optimizer off.
+# Per-source flags.  collectives.hip and probes.hip: the compiler's atomic
+# optimizer off.
 # It turns an atomic on one address into a wave-wide reduction whose result
 # it waits for at once; the shared tile counter's fetch must instead stay in
 # flight while the current tile moves (TilePool in snac_device.hpp).
-SOURCE_FLAGS = {"collectives.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
+_NO_ATOMIC_OPT = ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
+SOURCE_FLAGS = {"collectives.hip": _NO_ATOMIC_OPT, "probes.hip": _NO_ATOMIC_OPT}
 
 
 def build(verbose: bool = False) -> str:

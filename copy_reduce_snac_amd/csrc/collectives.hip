@@ -34,7 +34,8 @@ __global__ __launch_bounds__(SMALL ? kSmallReduceThreads : kReduceThreads) void 
   constexpr uint32_t TILE = SMALL ? TH * 16u : kTileBytes;
   __shared__ __align__(16) char lds[engine_lds_bytes<TH, kMaxRanks>()];
   __shared__ unsigned long long xchg[2];
-  const TilePool pool{(global_u64*)pa.next, (global_u64*)(pa.next + kFlagStride), xchg, pa.rounds};
+  const TilePool pool{(global_u64*)pa.next, (global_u64*)(pa.next + (uint64_t)pa.counters * kFlagStride), xchg,
+                      pa.rounds, pa.counters};
   run_reduce<N, T, TH, CP, ALIGNED, TILE>(d, blockIdx.x, gridDim.x, lds, pool);
 }
 
@@ -48,7 +49,8 @@ template <int CP, bool ALIGNED, int TH, uint32_t TILE = kTileBytes>
 __global__ __launch_bounds__(TH) void copy_kernel(const CollDesc d, const PoolArg pa) {
   __shared__ __align__(16) char lds[engine_lds_bytes<TH>()];
   __shared__ unsigned long long xchg[2];
-  const TilePool pool{(global_u64*)pa.next, (global_u64*)(pa.next + kFlagStride), xchg, pa.rounds};
+  const TilePool pool{(global_u64*)pa.next, (global_u64*)(pa.next + (uint64_t)pa.counters * kFlagStride), xchg,
+                      pa.rounds, pa.counters};
   run_copy<TH, CP, ALIGNED, TILE>(d, blockIdx.x, gridDim.x, lds, pool);
 }
 
@@ -213,20 +215,25 @@ static int default_wgs_per_cu(const CollDesc& d, int shape, uint64_t tiles, int 
   return !is_multicast_copy(d) && tiles <= 8u * (uint64_t)(cus > 0 ? cus : 1) ? 4 : 2;
 }
 
-// The shared tile counter serves launches in the 16 KiB-tile shape with at
-// least kPoolMinRounds tiles per workgroup whose tiles each move at least
-// kPoolMinStreams 16 KiB streams (sources read plus destinations written).
-// The counter is one address, and on MI355X one address takes about 84 M
-// atomic adds per second; a one-to-one copy of 16 KiB tiles at 6 TB/s would
-// ask for 180 M (and AllToAll u32 N=8, 128 MiB per rank, with a fetch per
-// 4 KiB tile took 1.57 ms against 0.36).  The first kPoolGridRounds rounds
-// are grid-stride, since every workgroup starting on the counter at once
-// only queues on it.  AllReduce bf16 N=8 twin, 256 MiB per rank (64
-// rounds): 0.717 ms with 8 grid-stride rounds first, 0.718-0.721 with 16 or
-// none, against 0.751 with grid-stride tiles only.
+// Tile counters serve launches in the 16 KiB-tile shape with at least
+// kPoolMinRounds tiles per workgroup.  The first kPoolGridRounds rounds are
+// grid-stride, since every workgroup starting on the counters at once only
+// queues on them; the rest of the tiles are handed out in order.  One
+// address takes about 84 M atomic adds per second on MI355X, and a counter
+// serves fastest at about a quarter of that, so a launch takes one counter
+// per 16 streams of 16 KiB its tiles move (sources read plus destinations
+// written), at most kPoolMaxUse.  Measured, one box, two alternations, ms:
+//   AllReduce bf16 N=8 256 MiB (16 streams): 1 counter 0.718, 2 0.719,
+//     4 0.721, grid-stride 0.758-0.763;
+//   ReduceScatter bf16 N=8 (9 streams): 1 0.181, 2 0.180, 4 0.181, 8 0.183,
+//     grid-stride 0.194-0.195;  AllGather bf16 N=8 (9): 1 0.169, 2 0.167,
+//     4 0.167-0.168, grid-stride 0.174;
+//   AllToAll u32 N=8 128 MiB (2 streams, on 16 KiB tiles): 1 0.786, 2 0.426,
+//     4 0.332, 8 0.335, against 0.360 for grid-stride 4 KiB tiles.
 constexpr uint64_t kPoolMinRounds = 16;
 constexpr uint32_t kPoolGridRounds = 8;
-constexpr int kPoolMinStreams = 8;
+constexpr uint32_t kPoolMaxUse = 4;
+static_assert(kPoolMaxUse <= kPoolMaxCounters, "a slot holds the counters a launch uses");
 
 // 16 KiB streams one tile of this descriptor's kernel moves.
 static int tile_streams(const CollDesc& d) {
@@ -264,13 +271,17 @@ hipError_t launch_collective(const CollDesc& d, bool aligned, int shape, uint64_
   if (want < per_cu) per_cu = want;
   uint64_t grid = (uint64_t)(cus > 0 ? cus : 1) * (uint64_t)per_cu;
   if (grid > tiles) grid = tiles;
-  PoolArg pa{nullptr, 0};
+  PoolArg pa{nullptr, 0, 1};
   const uint64_t rounds = tiles / grid;
-  if (pool && shape == kShapeTile &&
-      (cfg.tile_schedule == 2 ||
-       (cfg.tile_schedule == 0 && rounds >= kPoolMinRounds && tile_streams(d) >= kPoolMinStreams))) {
+  if (pool && shape == kShapeTile && (cfg.tile_schedule == 2 || (cfg.tile_schedule == 0 && rounds >= kPoolMinRounds))) {
     pa.next = pool;
     pa.rounds = rounds >= 2 * kPoolGridRounds ? kPoolGridRounds : (uint32_t)(rounds > 2 ? rounds / 2 : 1);
+    const int streams = tile_streams(d);
+    uint32_t cnt = (uint32_t)((16 + streams - 1) / streams);
+    if (cnt > kPoolMaxUse) cnt = kPoolMaxUse;
+    const uint64_t groups = (grid + 7) / 8;  // every counter needs a workgroup: (block / 8) % counters
+    if (cnt > groups) cnt = (uint32_t)groups;
+    pa.counters = cnt;
   }
   hipLaunchKernelGGL(fn, dim3((uint32_t)grid), dim3(threads), 0, stream, d, pa);
   return hipGetLastError();

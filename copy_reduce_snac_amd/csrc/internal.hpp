@@ -19,8 +19,9 @@ struct LaunchCfg {
 // Shared tile counters of one launch (TilePool in snac_device.hpp): `next`,
 // and the done count kFlagStride words after it; nullptr: grid-stride.
 struct PoolArg {
-  unsigned long long* next;
-  uint32_t rounds;  // grid-stride rounds before the counter
+  unsigned long long* next;  // counter 0; counter c kFlagStride * c words on, then the done count
+  uint32_t rounds;           // grid-stride rounds before the counters
+  uint32_t counters;         // counters of the launch
 };
 
 // Tile shapes of the host-launched collective kernels:
@@ -110,7 +111,8 @@ constexpr uint32_t kUserFlags = 1024;               // flags handed to device-si
 // Tile-counter slots per context: consecutive collective calls take
 // consecutive slots, so that calls in flight at once rarely share one.
 constexpr uint32_t kPoolSlots = 64;
-constexpr uint32_t kPoolSlotWords = 2 * kFlagStride;  // next, then done, one 128-byte line each
+constexpr uint32_t kPoolMaxCounters = 8;
+constexpr uint32_t kPoolSlotWords = (kPoolMaxCounters + 1) * kFlagStride;  // counters, then done, a line each
 
 // workgroups per CU of a pipeline launch under cfg
 int pipe_wgs_per_cu(const LaunchCfg& cfg);

@@ -236,9 +236,11 @@ snac_status snac_reduce_n(void* const* dst, int ndst, const void* const* src, in
 /* ---------------------------------------------------- measurement probes */
 
 typedef enum snac_probe_kind {
-  SNAC_PROBE_READ = 0,  /* read src[0, bytes) */
-  SNAC_PROBE_WRITE = 1, /* write dst[0, bytes) */
-  SNAC_PROBE_COPY = 2   /* dst[0, bytes) = src[0, bytes): one read and one write per byte */
+  SNAC_PROBE_READ = 0,    /* read src[0, bytes) */
+  SNAC_PROBE_WRITE = 1,   /* write dst[0, bytes) */
+  SNAC_PROBE_COPY = 2,    /* dst[0, bytes) = src[0, bytes): one read and one write per byte */
+  SNAC_PROBE_ORDERED = 8  /* or'ed into a kind: after 8 grid-stride rounds the tiles are handed out in
+                             order from 4 counters, as the collectives' long launches take them */
 } snac_probe_kind;
 
 /*
@@ -249,7 +251,9 @@ typedef enum snac_probe_kind {
  * collectives' access primitives: 16-byte buffer loads and stores with the
  * streaming hint over grid-stride tiles of `tile_bytes` per workgroup
  * iteration, `wgs_per_cu` workgroups per CU of `threads` threads.
- *   kind        SNAC_PROBE_READ, _WRITE or _COPY
+ *   kind        SNAC_PROBE_READ, _WRITE or _COPY, optionally | SNAC_PROBE_ORDERED
+ *               (its counters are a static device array of the library:
+ *               ordered probes must not run at the same time on one GPU)
  *   dst         WRITE/COPY: output of `bytes`; READ: a 4-byte sink written
  *               only if the XOR of every word read equals `magic`
  *   src         READ/COPY: input of `bytes`; WRITE: unused (may be NULL)

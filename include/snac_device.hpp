@@ -1196,10 +1196,13 @@ __device__ __forceinline__ void reduce_tile_store(const CollDesc& d, const TileR
 typedef __attribute__((address_space(1))) unsigned long long global_u64;
 
 struct TilePool {
-  global_u64* next;          // agent-scope tile counter, zero between launches; nullptr: grid-stride only
+  global_u64* next;          // the first of `counters` agent-scope tile counters, SNAC_FLAG_STRIDE words
+                             // apart, zero between launches; nullptr: grid-stride only
   global_u64* done;          // workgroups finished; zero between launches
   unsigned long long* xchg;  // two LDS words that pass thread 0's fetch to the workgroup
   uint32_t rounds;           // grid-stride rounds first (0 counts as 1)
+  uint32_t counters;         // counter c serves the pooled tiles first + c + counters * k to the workgroups with
+                             // (block / 8) % counters == c; every c must have one (0 counts as 1)
 };
 
 // Calls step(tile) for every tile of this workgroup's share, in ascending
@@ -1215,17 +1218,21 @@ __device__ __forceinline__ void for_each_tile(uint32_t block, uint32_t blocks, u
   // one call site of step, so that the tile code is emitted once
   const bool pooled = pool.next != nullptr;
   const uint32_t rounds = pooled ? (pool.rounds ? pool.rounds : 1u) : 0u;
-  const uint64_t first = (uint64_t)rounds * blocks;  // the first pooled tile
-  uint32_t left = rounds;                            // grid-stride rounds still to run
+  const uint32_t ncount = pooled && pool.counters ? pool.counters : 1u;
+  // workgroups are dealt to the XCDs in turn (block % 8), so each counter's
+  // group of workgroups holds every XCD alike
+  const uint32_t c = (block / 8u) % ncount;
+  global_u64* const mine = pooled ? pool.next + (uint64_t)c * SNAC_FLAG_STRIDE : nullptr;
+  const uint64_t first = (uint64_t)rounds * blocks + c;  // this group's first pooled tile
+  uint32_t left = rounds;                                // grid-stride rounds still to run
   uint64_t t = block;
   int p = 0;
   while (t < total) {
     // from the last grid-stride round on, each tile's successor comes from
-    // the counter, fetched while the tile moves
+    // the group's counter, fetched while the tile moves
     const bool fetch = pooled && left <= 1;
     unsigned long long nxt = 0;
-    if (fetch && threadIdx.x == 0)
-      nxt = __hip_atomic_fetch_add(pool.next, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (fetch && threadIdx.x == 0) nxt = __hip_atomic_fetch_add(mine, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     step((uint32_t)t);
     if (!fetch) {
       t += blocks;
@@ -1235,15 +1242,17 @@ __device__ __forceinline__ void for_each_tile(uint32_t block, uint32_t blocks, u
     // xchg[p] was last read before the previous barrier, so it is free
     if (threadIdx.x == 0) pool.xchg[p] = nxt;
     __syncthreads();
-    t = first + uniform64(pool.xchg[p]);
+    t = first + (uint64_t)ncount * uniform64(pool.xchg[p]);
     p ^= 1;
   }
   if (pooled && threadIdx.x == 0) {
     // every workgroup took its last tile index before counting itself done,
-    // so the last one to count may clear both counters
+    // so the last one to count may clear every counter
     const unsigned long long d = __hip_atomic_fetch_add(pool.done, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (d == (unsigned long long)blocks - 1) {
-      __hip_atomic_exchange(pool.next, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (uint32_t i = 0; i < ncount; ++i)
+        __hip_atomic_exchange(pool.next + (uint64_t)i * SNAC_FLAG_STRIDE, 0ull, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_exchange(pool.done, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }

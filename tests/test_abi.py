@@ -85,6 +85,8 @@ def test_probe_argument_errors_without_gpu():
         return lambda: snac.snac_hbm_probe(kind, dst, src, nbytes, threads, tile, wgs)
 
     _expect(E, p(7, 0x1000, 0x2000, 16))                 # unknown kind
+    _expect(E, p(8 | 3, 0x1000, 0x2000, 16))             # unknown kind, ordered
+    _expect(E, p("copy_ordered", 0x1008, 0x2000, 16))    # misaligned dst, ordered
     _expect(E, p("copy", 0x1000, 0x2000, 16, threads=128))  # workgroup size
     _expect(E, p("copy", 0x1000, 0x2000, 16, tile=8192))    # tile
     _expect(E, p("copy", 0x1000, 0x2000, 16, wgs=0))

@@ -42,6 +42,7 @@ PACKED = ["v_pk_" + op + "_f32" for op in ("add", "mul", "fma")]
 
 SOURCES = {
     "collectives.hip": os.path.join(CSRC, "collectives.hip"),
+    "probes.hip": os.path.join(CSRC, "probes.hip"),
     "pipeline.hip": os.path.join(CSRC, "pipeline.hip"),
     "devapi_kernels.hip": os.path.join(ROOT, "tests", "devapi", "devapi_kernels.hip"),
 }
@@ -169,6 +170,9 @@ def test_tile_counter_fetch_stays_in_flight(asm):
           if (k.startswith("_ZN4snac13reduce_kernelI") and re.search(r"ELb[01]ELb0EEEv", k))
           or (k.startswith("_ZN4snac11copy_kernelI") and "Lj16384E" in k)}
     assert len(ks) >= 96
+    probes = {k: v for k, v in _kernels(asm["probes.hip"]).items() if "probe_kernel" in k}
+    assert len(probes) == 12
+    ks.update(probes)
     for name, lines in ks.items():
         text = "\n".join(lines)
         assert "flat_atomic" not in text and "scratch_" not in text, name

@@ -66,3 +66,29 @@ def test_probe_copy_write_read(threads, tile, wgs, nbytes):
     sync()
     assert sink.guards_ok()
     assert int(sink.download(np.uint32)[0]) == fold, "lane 0 of workgroup 0 did not read exactly its words"
+
+
+@pytest.mark.parametrize("threads,tile,wgs", [(256, 16384, 1), (64, 16384, 2), (256, 16384, 2)])
+@pytest.mark.parametrize("nbytes", [16384 * 300, (1 << 22) + 16 * 5, 16384 * 4096 + 48])
+def test_ordered_probes_copy_and_write(threads, tile, wgs, nbytes):
+    """With tiles handed out in order from the probes' counters, the copy
+    probe still copies every byte once and the write probe writes its word
+    everywhere, twice in a row (the counters are left at zero for the next
+    launch)."""
+    data = wl.raw_bytes(nbytes, wl.CFG_TEST, 5, seed=nbytes % 997)
+    src = DevBuf(nbytes, data=data)
+    for rep in range(2):
+        dst = DevBuf(nbytes)
+        snac.snac_hbm_probe("copy_ordered", dst.ptr, src.ptr, nbytes, threads, tile, wgs)
+        sync()
+        assert dst.guards_ok(), f"ordered copy probe wrote outside its range (call {rep})"
+        assert np.array_equal(dst.download(), data), f"ordered copy probe output differs (call {rep})"
+        magic = 0x3C3CC3C3 + rep
+        snac.snac_hbm_probe("write_ordered", dst.ptr, None, nbytes, threads, tile, wgs, magic)
+        sync()
+        assert dst.guards_ok()
+        assert np.all(dst.download(np.uint32) == magic), f"ordered write probe missed words (call {rep})"
+    sink = DevBuf(4)
+    snac.snac_hbm_probe("read_ordered", sink.ptr, src.ptr, nbytes, threads, tile, wgs, 0)
+    sync()
+    assert sink.guards_ok()

@@ -1,14 +1,16 @@
 """Whole-output parity of the copy kernels in their big-message shapes.
 
 One-to-one copies that move at least 1 GiB (bytes read plus bytes written)
-run single-wave workgroups on 4 KiB tiles, five per CU when every job is
-16-byte aligned and four otherwise; those whose source sits at a byte
-offset from the destination's dword grid keep 256-thread workgroups on
-16 KiB tiles, whose full tiles take the next lane's bytes through DPP
-shifts.  Sampled checks at the benchmark sizes could miss a single lost
-tile, so here every output byte is compared with the oracle, aligned and
-misaligned, with ragged tails, and the canary bytes around every
-destination must be untouched."""
+run single-wave workgroups on grid-stride 4 KiB tiles, five per CU, when
+the call has no context (snac_copy) or its tile schedule is grid-stride
+only; a collective call with a context instead hands 16 KiB tiles out in
+order from its tile counters.  Copies whose source sits at a byte offset
+from the destination's dword grid keep 256-thread workgroups on 16 KiB
+tiles, whose full tiles take the next lane's bytes through DPP shifts.
+Sampled checks at the benchmark sizes could miss a single lost tile, so
+here every output byte is compared with the oracle, aligned and
+misaligned, with ragged tails, under both schedules, and the canary bytes
+around every destination must be untouched."""
 from __future__ import annotations
 
 import numpy as np
@@ -53,12 +55,20 @@ def test_copy_moving_a_gib_or_more(src_off, dst_off, nbytes):
     assert db.guards_ok()
 
 
+@pytest.fixture(params=[0, 1], ids=["counters", "grid-stride"])
+def schedule(request):
+    t0 = snac.snac_get_tuning()
+    snac.snac_set_tuning(tile_schedule=request.param)
+    yield request.param
+    snac.snac_set_tuning(**t0)
+
+
 @pytest.mark.parametrize("n,chunk_bytes,offset", [
     (4, 64 * MiB + 4096, 0),  # every chunk 16-byte aligned
     (4, 64 * MiB + 12, 0),    # chunk starts 4-byte aligned only
     (2, 256 * MiB + 8, 4),    # two ranks, buffers 4 bytes off
 ])
-def test_all_to_all_moving_a_gib_or_more(n, chunk_bytes, offset):
+def test_all_to_all_moving_a_gib_or_more(schedule, n, chunk_bytes, offset):
     per_rank = n * chunk_bytes
     assert 2 * n * per_rank >= 1 << 30
     e = per_rank // 4
@@ -81,7 +91,7 @@ def test_all_to_all_moving_a_gib_or_more(n, chunk_bytes, offset):
         assert db[d].guards_ok()
 
 
-def test_byte_all_to_all_moving_a_gib_or_more():
+def test_byte_all_to_all_moving_a_gib_or_more(schedule):
     # chunks of 64 MiB + 3 bytes: every job but the first reads at a byte
     # offset from its destination's dword grid (16 KiB tiles, DPP shifts)
     n, chunk_bytes = 4, 64 * MiB + 3
