@@ -509,12 +509,13 @@ typedef struct snac_tuning {
                                     rank) first sleep about this many microseconds,
                                     to skew producers against consumers */
   int32_t tile_schedule;       /* how a collective call's workgroups share its
-                                  16 KiB tiles: 0 library default (grid-stride,
-                                  then a counter in the context handing out the
-                                  rest in order, for calls of at least 16 tiles
-                                  per workgroup whose tiles each read and write
-                                  at least 8 buffers), 1 grid-stride only, 2 the
-                                  counter for every call in that tile shape */
+                                  16 KiB tiles: 0 library default (for calls of
+                                  at least 16 tiles per workgroup, grid-stride
+                                  rounds and then the rest in order from 1-4
+                                  counters in the context; one-to-one copies
+                                  moving >= 1 GiB then also take 16 KiB tiles),
+                                  1 grid-stride only, 2 the counters for every
+                                  call in the 16 KiB-tile shape */
 } snac_tuning;
 
 snac_status snac_get_tuning(snac_tuning* out);
