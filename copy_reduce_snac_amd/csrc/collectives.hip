@@ -26,8 +26,10 @@ constexpr int kSmallReduceThreads = 128;
 
 // N-to-1 reduce of element type T over N sources, the whole grid.  SMALL:
 // the small-tile form (one 16-byte unit per lane, all sources in flight)
-// for messages with fewer 16 KiB tiles than the GPU has CUs.
-template <int N, typename T, int CP, bool ALIGNED, bool SMALL = false>
+// for messages with fewer 16 KiB tiles than the GPU has CUs.  ROLL: tiles
+// on the dword grid take the rolling load pipeline (the bf16 AllReduce of
+// 8 ranks only).
+template <int N, typename T, int CP, bool ALIGNED, bool SMALL = false, bool ROLL = false>
 __global__ __launch_bounds__(SMALL ? kSmallReduceThreads : kReduceThreads) void reduce_kernel(const CollDesc d,
                                                                                             const PoolArg pa) {
   constexpr int TH = SMALL ? kSmallReduceThreads : kReduceThreads;
@@ -36,7 +38,7 @@ __global__ __launch_bounds__(SMALL ? kSmallReduceThreads : kReduceThreads) void 
   __shared__ unsigned long long xchg[2];
   const TilePool pool{(global_u64*)pa.next, (global_u64*)(pa.next + (uint64_t)pa.counters * kFlagStride), xchg,
                       pa.rounds, pa.counters};
-  run_reduce<N, T, TH, CP, ALIGNED, TILE>(d, blockIdx.x, gridDim.x, lds, pool);
+  run_reduce<N, T, TH, CP, ALIGNED, TILE, ROLL>(d, blockIdx.x, gridDim.x, lds, pool);
 }
 
 // Byte copy of the collective's jobs, the whole grid.  TH = 256 for
@@ -106,6 +108,19 @@ KernelFn reduce_kernel_n(int n) {
     case 15: return kernel_ptr<15, T, CP, A, SMALL>();
     case 16: return kernel_ptr<16, T, CP, A, SMALL>();
     default: return nullptr;
+  }
+}
+
+// The bf16 AllReduce of 8 ranks, every destination written by each tile.
+static KernelFn rolling_reduce_kernel_cp(int cp, bool aligned) {
+  if (!aligned)
+    return cp == kCached ? &reduce_kernel<8, BF16, kCached, false, false, true>
+                         : &reduce_kernel<8, BF16, kCacheStream, false, false, true>;
+  switch (cp) {
+    case kCacheStream: return &reduce_kernel<8, BF16, kCacheStream, true, false, true>;
+    case kCacheStreamStores: return &reduce_kernel<8, BF16, kCacheStreamStores, true, false, true>;
+    case kCacheStreamLoads: return &reduce_kernel<8, BF16, kCacheStreamLoads, true, false, true>;
+    default: return &reduce_kernel<8, BF16, kCached, true, false, true>;
   }
 }
 
@@ -253,7 +268,10 @@ hipError_t launch_collective(const CollDesc& d, bool aligned, int shape, uint64_
     fn = small_kernel(d, aligned);
   } else if (reduce) {
     if (shape != kShapeTile) return hipErrorInvalidValue;
-    fn = d.esize == 4 ? reduce_kernel_cp<F32>(d.nsrc, cp, aligned) : reduce_kernel_cp<BF16>(d.nsrc, cp, aligned);
+    if (d.esize == 2 && d.nsrc == 8 && d.coll == kAllReduce && !d.split_multicast && d.ndst == 8)
+      fn = rolling_reduce_kernel_cp(cp, aligned);
+    else
+      fn = d.esize == 4 ? reduce_kernel_cp<F32>(d.nsrc, cp, aligned) : reduce_kernel_cp<BF16>(d.nsrc, cp, aligned);
   } else if (shape == kShapeStream) {
     if (is_multicast_copy(d)) return hipErrorInvalidValue;
     fn = copy_kernel_cp<kStreamThreads, kStreamTile>(cp, aligned);

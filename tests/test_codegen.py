@@ -145,16 +145,39 @@ def test_misaligned_copy_tile_issues_every_load_first(asm, shape):
         assert _longest_unwaited_run(lines, "global_load_dword") >= 4, f"{name}: misaligned loads serialised"
 
 
+# reduce_kernel<N, T, CP, ALIGNED, SMALL, ROLL>
+REDUCE_NAME = re.compile(r"_ZN4snac13reduce_kernelILi(\d+)ENS_\d+(\w+?)ELi(\d)ELb([01])ELb([01])ELb([01])EEEv")
+
+
+def _reduce_kernels(asm: str) -> dict[tuple, list[str]]:
+    out = {}
+    for k, v in _kernels(asm).items():
+        m = REDUCE_NAME.match(k)
+        if m:
+            n, t, cp, a, small, roll = m.groups()
+            out[(int(n), t, int(cp), a == "1", small == "1", roll == "1")] = v
+    return out
+
+
+def test_reduce_kernel_set(asm):
+    ks = _reduce_kernels(asm["collectives.hip"])
+    # N = 1..16, two types: four cache policies aligned and two generic at
+    # 16 KiB tiles, aligned and generic small tiles; the rolling form for
+    # bf16 N=8 at 16 KiB tiles only
+    assert len([k for k in ks if not k[5]]) == 16 * 2 * 8
+    assert sorted(k for k in ks if k[5]) == sorted(
+        [(8, "BF16", cp, True, False, True) for cp in range(4)] + [(8, "BF16", cp, False, False, True) for cp in (0, 1)])
+
+
 def test_misaligned_reduce_tile_issues_every_load_first(asm):
     # generic reduce kernels: the 16 KiB-tile form keeps a source's 4 units
     # per lane in flight, the small-tile form every source's unit
-    ks = {k: v for k, v in _kernels(asm["collectives.hip"]).items()
-          if k.startswith("_ZN4snac13reduce_kernelI") and re.search(r"Lb0ELb[01]E", k)}
-    assert len(ks) == 96
-    for name, lines in ks.items():
-        n = int(re.match(r"_ZN4snac13reduce_kernelILi(\d+)E", name).group(1))
-        want = n if "Lb0ELb1E" in name else 4
-        assert _longest_unwaited_run(lines, "global_load_dword") >= want, f"{name}: misaligned loads serialised"
+    ks = {k: v for k, v in _reduce_kernels(asm["collectives.hip"]).items() if not k[3]}
+    assert len(ks) == 98
+    for (n, t, cp, a, small, roll), lines in ks.items():
+        want = n if small else 4
+        assert _longest_unwaited_run(lines, "global_load_dword") >= want, \
+            f"reduce N={n} {t} cp={cp} small={small} roll={roll}: misaligned loads serialised"
 
 
 def test_misaligned_256_thread_copy_uses_dpp_shifts(asm):
@@ -167,9 +190,9 @@ def test_misaligned_256_thread_copy_uses_dpp_shifts(asm):
 
 def test_tile_counter_fetch_stays_in_flight(asm):
     ks = {k: v for k, v in _kernels(asm["collectives.hip"]).items()
-          if (k.startswith("_ZN4snac13reduce_kernelI") and re.search(r"ELb[01]ELb0EEEv", k))
+          if (REDUCE_NAME.match(k) and REDUCE_NAME.match(k).group(5) == "0")
           or (k.startswith("_ZN4snac11copy_kernelI") and "Lj16384E" in k)}
-    assert len(ks) >= 96
+    assert len(ks) >= 6 + 16 * 2 * 6
     probes = {k: v for k, v in _kernels(asm["probes.hip"]).items() if "probe_kernel" in k}
     assert len(probes) == 12
     ks.update(probes)
