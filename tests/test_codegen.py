@@ -169,6 +169,23 @@ def test_reduce_kernel_set(asm):
         [(8, "BF16", cp, True, False, True) for cp in range(4)] + [(8, "BF16", cp, False, False, True) for cp in (0, 1)])
 
 
+def test_rolling_allreduce_tile_keeps_four_loads_in_flight(asm):
+    # the bf16 AllReduce of 8 ranks, aligned, every cache policy: the tile's
+    # 32 loads per lane go out at most 4 without a wait, and each wait leaves
+    # 2-3 in flight (the two-buffer form waits 8 times, leaving 4-7)
+    ks = {k: v for k, v in _reduce_kernels(asm["collectives.hip"]).items() if k[5] and k[3]}
+    assert len(ks) == 4
+    for key, lines in ks.items():
+        code = [l.strip() for l in lines if l.strip() and not l.strip().startswith(";")]
+        loads = [i for i, l in enumerate(code) if l.startswith("buffer_load_dwordx4")]
+        assert len(loads) == 32, f"{key}: {len(loads)} tile loads"
+        region = code[loads[0]:loads[-1] + 1]
+        waits = [int(m.group(1)) for m in (re.search(r"vmcnt\((\d+)\)", l) for l in region
+                                           if l.startswith("s_waitcnt")) if m]
+        assert len(waits) >= 24 and set(waits) <= {2, 3}, f"{key}: waits {waits}"
+        assert _longest_unwaited_run(region, "buffer_load_dwordx4") <= 4, f"{key}: loads hoisted"
+
+
 def test_misaligned_reduce_tile_issues_every_load_first(asm):
     # generic reduce kernels: the 16 KiB-tile form keeps a source's 4 units
     # per lane in flight, the small-tile form every source's unit

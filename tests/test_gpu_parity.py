@@ -414,6 +414,22 @@ def test_large_tiles_misaligned_allreduce_and_rs(ctxs, dtype):
     run_and_check(rb, oracle.reduce_scatter(srcs, dtype), dtype, f"RS large misaligned {dtype}")
 
 
+@pytest.mark.parametrize("aligned", [True, False], ids=["aligned", "dword-offsets"])
+def test_large_tiles_allreduce_bf16_n8_rolling(ctxs, aligned):
+    """The bf16 AllReduce of 8 ranks has its own kernel (a rolling load
+    pipeline over the tile): buffers on the 16-byte grid, and sources 4, 8
+    and 12 bytes off it (dword-aligned, so the rolling form still runs, with
+    unaligned 16-byte loads), each with a ragged last tile."""
+    n = 8
+    m = 8 * (700_000 + 16) if aligned else 8 * (700_000 + 13)
+    srcs = gen(n, m, "bf16", seed=47)
+    nb = srcs[0].nbytes
+    sb = [DevBuf(nb, offset=0 if aligned else 4 * (k % 4), data=s) for k, s in enumerate(srcs)]
+    db = [DevBuf(nb, offset=0 if aligned else 8) for _ in srcs]
+    snac.snac_all_reduce(ctxs(n), [b.ptr for b in sb], [b.ptr for b in db], nb, "bf16")
+    run_and_check(db, oracle.all_reduce(srcs, "bf16"), "bf16", f"AR bf16 N=8 rolling aligned={aligned}")
+
+
 @pytest.mark.parametrize("dtype", ["u32", "byte"])
 def test_large_tiles_v_collectives(ctxs, dtype):
     n = 8
