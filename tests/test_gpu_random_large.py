@@ -42,34 +42,50 @@ def gen(n, m, dtype, seed):
     return [wl.raw_bytes(m, wl.CFG_TEST, r, seed=seed) for r in range(n)]
 
 
-def case(i: int):
-    """Case i: collective, rank count, data type, sizes and buffer offsets."""
-    rng = np.random.default_rng([20261202, i])
-    coll = COLLS[i % len(COLLS)]
+GRID_COLLS = ["all_reduce", "reduce_scatter", "all_gather", "all_to_all"]
+
+
+def case(i: int, grid: bool = False):
+    """Case i: collective, rank count, data type, sizes and buffer offsets.
+    grid: every buffer and size on the 16-byte grid (the aligned kernels),
+    sizes still ragged against the 16 KiB tile; every other AllReduce case
+    is bf16 over 8 ranks, which has a kernel of its own."""
+    rng = np.random.default_rng([20261202, 1, i] if grid else [20261202, i])
+    colls = GRID_COLLS if grid else COLLS
+    coll = colls[i % len(colls)]
     n = int(rng.choice([2, 3, 5, 8, 16]))
     dtype = str(rng.choice(["bf16", "f32"] if coll in REDUCES else ["bf16", "u32", "byte"]))
+    if grid and coll == "all_reduce" and (i // len(colls)) % 2 == 0:
+        n, dtype = 8, "bf16"
     e = ESIZE[dtype]
+    unit = 16 // e if grid else 1
 
     def elems(lo_bytes, hi_bytes, multiple=1):
+        multiple = int(np.lcm(multiple, unit))
         m = int(rng.integers(lo_bytes // e, hi_bytes // e))
         m -= m % multiple
         return max(m, multiple)
 
     if coll in ("all_reduce", "reduce_scatter"):
         m = elems(5 * MiB, 12 * MiB, n if coll == "reduce_scatter" else 1)
+        if grid and coll == "reduce_scatter":
+            m = elems(5 * MiB, 12 * MiB, n * unit)  # each rank's chunk on the grid too
     elif coll == "all_gather":
         # N jobs of m elements; the output holds N * N * m
         m = elems(max(5 * MiB // n, 64 << 10), max(256 * MiB // (n * n), 6 * MiB // n))
     elif coll == "all_to_all":
-        m = elems(max(5 * MiB // n, 64 << 10), 12 * MiB, n)
+        m = elems(max(5 * MiB // n, 64 << 10), 12 * MiB, n * unit if grid else n)
     else:
         m = elems(5 * MiB, 16 * MiB)  # per-rank total of the V counts
-    offs = rng.integers(0, 16, size=2 * n) * e
+    offs = rng.integers(0, 16, size=2 * n) * (16 if grid else e)
     return coll, n, dtype, m, [int(o) for o in offs[:n]], [int(o) for o in offs[n:]], i
 
 
-# SNAC_RANDOM_LARGE_CASES widens the sweep (the default covers each collective four times)
+# SNAC_RANDOM_LARGE_CASES widens the sweep (the default covers each collective four times);
+# SNAC_RANDOM_GRID_CASES the one on the 16-byte grid (default: each of its collectives three times)
 CASES = [case(i) for i in range(int(os.environ.get("SNAC_RANDOM_LARGE_CASES", "28")))]
+CASES += [case(i, grid=True)[:-1] + (1000 + i,)
+          for i in range(int(os.environ.get("SNAC_RANDOM_GRID_CASES", "12")))]
 
 
 @pytest.fixture(scope="module")
