@@ -1033,10 +1033,11 @@ __device__ __forceinline__ bool tile_needs_shift(const CollDesc& d, const TileRe
 // U in flight took 0.694-0.698 ms, against 0.697 with U + 1, 0.710 with
 // U + 2, 0.715-0.716 with 2U or 3U, 0.720 with U - 1, and 0.712-0.714 for
 // two sources loaded as blocks in turn (reduce_tile below).  In the library
-// (one box, two alternations) it ran that AllReduce 2.2-3.1% faster from
-// 128 MiB per rank up, bf16 N=6 and f32 N=8 even, but bf16 N=4 up to 1.3%
-// and ReduceScatter of 8 ranks (one destination: more reads in flight pay)
-// 14% slower; at 16 sources its unrolled schedule spills scalar registers.
+// (one box, two alternations) it ran that AllReduce 1% faster in calls back
+// to back and 2.3-4.3% faster in graph replays from 128 MiB per rank up;
+// bf16 N=6 and f32 N=8 even, but bf16 N=4 up to 1.3% and ReduceScatter of
+// 8 ranks (one destination: more reads in flight pay) 14% slower; at 16
+// sources its unrolled schedule spills scalar registers.
 // Hence only the bf16 AllReduce of 8 ranks takes it.  Left to itself the
 // compiler issues every load of the tile first, so each load's offset
 // takes a zero it cannot see, made from the sum just added (an empty
@@ -1082,8 +1083,9 @@ __device__ __forceinline__ void reduce_tile_rolling(const CollDesc& d, const Til
 
 // The reduced units of one tile, sources added in rank order, for every
 // tile not given the rolling pipeline.  Two register buffers alternate:
-// while source k is added from one, source k + 1 loads into the other.  The source loop is deliberately not unrolled: unrolled,
-// the compiler issues every source's loads before the first add.
+// while source k is added from one, source k + 1 loads into the other.
+// The source loop is deliberately not unrolled: unrolled, the compiler
+// issues every source's loads before the first add.
 template <int N, typename T, int TH, int U, int CP, bool ALIGNED, bool FULL, bool SHIFT = false>
 __device__ __forceinline__ void reduce_tile(const CollDesc& d, const TileRef& t, u32x4 (&r)[U]) {
   u32x4 a[U], b[U];
