@@ -1018,7 +1018,7 @@ def main() -> int:
     ap.add_argument("--summarize", default=None, metavar="WORKLOAD",
                     help="write the profiles/ summary of WORKLOAD (a --only name, 'headline' or 'ceilings') from "
                          "the rocprofv3 output under --prof-dir")
-    ap.add_argument("--prof-dir", default=os.path.join(ROOT, "gpurun_out", "prof"))
+    ap.add_argument("--prof-dir", default=os.path.join(ROOT, "rocprof_out"))
     ap.add_argument("--commands", default=None, help="file listing the rocprofv3 commands that made --prof-dir")
     args = ap.parse_args()
     if args.summarize:

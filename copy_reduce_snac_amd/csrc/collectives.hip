@@ -237,7 +237,7 @@ static int default_wgs_per_cu(const CollDesc& d, int shape, uint64_t tiles, int 
 // address takes about 84 M atomic adds per second on MI355X, and a counter
 // serves fastest at about a quarter of that, so a launch takes one counter
 // per 16 streams of 16 KiB its tiles move (sources read plus destinations
-// written), at most kPoolMaxUse.  Measured, one box, two alternations, ms:
+// written), at most kPoolMaxUse.  Measured, one machine, two alternations, ms:
 //   AllReduce bf16 N=8 256 MiB (16 streams): 1 counter 0.718, 2 0.719,
 //     4 0.721, grid-stride 0.758-0.763;
 //   ReduceScatter bf16 N=8 (9 streams): 1 0.181, 2 0.180, 4 0.181, 8 0.183,

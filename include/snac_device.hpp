@@ -1033,7 +1033,7 @@ __device__ __forceinline__ bool tile_needs_shift(const CollDesc& d, const TileRe
 // U in flight took 0.694-0.698 ms, against 0.697 with U + 1, 0.710 with
 // U + 2, 0.715-0.716 with 2U or 3U, 0.720 with U - 1, and 0.712-0.714 for
 // two sources loaded as blocks in turn (reduce_tile below).  In the library
-// (one box, two alternations) it ran that AllReduce 1% faster in calls back
+// (one machine, two alternations) it ran that AllReduce 1% faster in calls back
 // to back and 2.3-4.3% faster in graph replays from 128 MiB per rank up;
 // bf16 N=6 and f32 N=8 even, but bf16 N=4 up to 1.3% and ReduceScatter of
 // 8 ranks (one destination: more reads in flight pay) 14% slower; at 16
@@ -1480,7 +1480,7 @@ __device__ bool collective(const snac_args& a, const snac_dev_ctx& ctx) {
 // The Atoms of one target and their launch contract (Purlin 0.6.5
 // "Samples": a kernel using an Atom launches with its THREADS threads per
 // block and the dynamic shared memory it names; Purlin 0.6.4 "Atom
-// implementations": one Atom set per architecture).  This build has one
+// implementations": one Atom set per architecture).  This library has one
 // target, gfx950 (MI355X), so Atom<950> is the only one.
 template <int ARCH>
 struct Atom;
